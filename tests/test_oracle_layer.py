@@ -1,0 +1,310 @@
+"""Pins for the oracle's calibrate / plan / forward against closed forms,
+identities, brute force and exact rational arithmetic.
+
+Equation numbers refer to "W4A4 Quantization for Inference on Wan2.2-I2V-A14B"
+(arXiv 2606.29337).
+"""
+import itertools
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import layer, mxfp4
+
+E2M1 = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3),
+        Fraction(4), Fraction(6)]
+
+
+def _bf16(x):
+    return layer.bf16_rne(np.asarray(x, np.float32))
+
+
+def _small_layer(M, K, N, seed, outl=3, mult=25.0):
+    g = np.random.default_rng(seed)
+    X = (g.standard_normal((M, K)) * 0.25).astype(np.float32)
+    ch = g.choice(K, size=outl, replace=False)
+    X[:, ch] *= mult
+    W = np.clip(g.standard_normal((N, K)) * 0.05, -0.6, 0.6).astype(np.float32)
+    return X, W, ch
+
+
+# ----------------------------------------------------------------------------- calibration
+
+def test_act_max_bruteforce_and_invariances():
+    X, W, _ = _small_layer(37, 64, 8, 1)
+    a = layer.act_max(X)
+    want = [max(abs(float(X[t, j])) for t in range(X.shape[0])) for j in range(X.shape[1])]
+    assert a.tolist() == want
+    perm = np.random.default_rng(2).permutation(X.shape[0])
+    assert np.array_equal(layer.act_max(X[perm]), a)
+    run = layer.act_max(X[:10])
+    run = layer.act_max(X[10:11], run)
+    run = layer.act_max(X[11:], run)
+    assert np.array_equal(run, a)
+    Xb = _bf16(X)
+    assert np.array_equal(layer.act_max(Xb), np.abs(layer.as_f32(Xb)).max(axis=0))
+
+
+def test_weight_range_bruteforce():
+    _, W, _ = _small_layer(4, 64, 9, 3)
+    w = layer.weight_range(W)
+    assert w.tolist() == [max(abs(float(W[n, j])) for n in range(W.shape[0])) for j in range(64)]
+
+
+# ----------------------------------------------------------------------------- Eq. (2)
+
+@pytest.mark.parametrize("alpha", [0.3, 0.5, 0.6, 0.7])
+def test_smooth_scale_closed_form(alpha):
+    X, W, _ = _small_layer(64, 128, 16, 4)
+    a, w = layer.act_max(X), layer.weight_range(W)
+    s, rcp = layer.smooth_scales(a, w, alpha)
+    for j in range(0, 128, 7):
+        want = math.exp(alpha * math.log(float(a[j])) - (1 - alpha) * math.log(float(w[j])))
+        assert abs(float(s[j]) - want) <= 2 ** -23 * want        # within one f32 rounding
+        # (a/s) and (w s) are the two geometric forms of the fold
+        assert math.isclose(float(a[j]) / float(s[j]), (float(a[j]) * float(w[j])) ** (1 - alpha),
+                            rel_tol=1e-6)
+        assert math.isclose(float(w[j]) * float(s[j]), (float(a[j]) * float(w[j])) ** alpha,
+                            rel_tol=1e-6)
+        assert float(rcp[j]) == float(np.float32(1.0) / s[j])
+    # larger alpha pushes more of the channel-to-channel dynamic range into W:
+    # the spread of the folded weight maxima (a w)^alpha grows, that of the
+    # smoothed activation maxima (a w)^(1-alpha) shrinks
+    s2, _ = layer.smooth_scales(a, w, min(alpha + 0.1, 0.9))
+    spread = lambda v: float(v.max() / v.min())
+    assert spread(w * s2) > spread(w * s) and spread(a / s2) < spread(a / s)
+
+
+def test_smooth_off_is_identity():
+    a = np.array([3.0, 0.5], np.float32)
+    s, rcp = layer.smooth_scales(a, a, 0.5, smooth=False)
+    assert s.tolist() == [1.0, 1.0] and rcp.tolist() == [1.0, 1.0]
+
+
+def test_alpha_half_balances_maxima():
+    """At alpha = 0.5 the activation and weight maxima of each channel are equal
+    after the fold (up to f32 rounding), and the smoothed activation maximum is
+    exactly RN(a_j / s_j) because rounding is monotone."""
+    X, W, _ = _small_layer(128, 64, 32, 5)
+    a, w = layer.act_max(X), layer.weight_range(W)
+    s, _ = layer.smooth_scales(a, w, 0.5)
+    q = X / s[None, :]
+    qmax = np.abs(q).max(axis=0)
+    assert np.array_equal(qmax, (a / s).astype(np.float32))
+    wmax = np.abs(W * s[None, :]).max(axis=0)
+    assert np.allclose(qmax, wmax, rtol=4 * 2 ** -23, atol=0)
+
+
+# ----------------------------------------------------------------------------- Eq. (1)
+
+def test_fold_identity_f64():
+    X, W, _ = _small_layer(16, 64, 24, 6)
+    a, w = layer.act_max(X), layer.weight_range(W)
+    s, _ = layer.smooth_scales(a, w, 0.6)
+    s64 = s.astype(np.float64)
+    Y0 = X.astype(np.float64) @ W.astype(np.float64).T
+    Y1 = (X.astype(np.float64) / s64) @ (W.astype(np.float64) * s64).T
+    assert np.abs(Y1 - Y0).max() <= 1e-13 * np.abs(Y0).max()
+
+
+# ----------------------------------------------------------------------------- Eq. (4)
+
+def test_topk_bruteforce_with_ties():
+    a = np.array([3, 1, 3, 2, 5, 1, 3, 0, 2, 5], np.float32)
+    K = a.size
+    for k in range(K + 1):
+        O, pos = layer.outlier_set(a, k)
+        winners = []
+        for sub in itertools.combinations(range(K), k):
+            rest = [j for j in range(K) if j not in sub]
+            # every member outranks every non-member under (score desc, index asc)
+            if all((a[i] > a[r]) or (a[i] == a[r] and i < r) for i in sub for r in rest):
+                winners.append(sub)
+        assert len(winners) == 1
+        assert O.tolist() == list(winners[0])
+        assert all(pos[O[i]] == i for i in range(k))
+        assert np.sum(pos >= 0) == k
+
+
+# ----------------------------------------------------------------------------- forward pieces
+
+def test_quantize_divides_exactly():
+    """q = x / s rounded once to f32 (checked against exact rationals)."""
+    g = np.random.default_rng(8)
+    x = (g.standard_normal(64) * 3).astype(np.float32)
+    s = (np.abs(g.standard_normal(64)) * 5 + 0.1).astype(np.float32)
+    q = (x / s).astype(np.float32)
+    for xi, si, qi in zip(x, s, q):
+        exact = Fraction(float(xi)) / Fraction(float(si))
+        lo = np.nextafter(qi, np.float32(-np.inf))
+        hi = np.nextafter(qi, np.float32(np.inf))
+        d = abs(Fraction(float(qi)) - exact)
+        assert d <= abs(Fraction(float(lo)) - exact) and d <= abs(Fraction(float(hi)) - exact)
+
+
+def test_outlier_columns_leave_block_scales():
+    """Routing: an O column is gathered to XO and zeroed in the bulk, so its
+    magnitude cannot set the bulk block scale (the point of the split)."""
+    X = np.full((2, 64), 0.1, np.float32)
+    X[:, 5] = 1000.0
+    s = np.ones(64, np.float32)
+    O = np.array([5], np.int32)
+    r = layer.quantize_act(X, s, O)
+    assert np.all(r["As"] == mxfp4.e8m0_from_amax(np.float32(0.1)))
+    assert np.all(mxfp4.unpack_nibbles(r["Aq"])[:, 5] == 0)
+    assert np.all(layer.as_f32(r["XO"])[:, 0] == 1000.0)
+    r0 = layer.quantize_act(X, s, np.zeros(0, np.int32))
+    assert r0["As"][0, 0] == mxfp4.e8m0_from_amax(np.float32(1000.0))
+
+
+def _decode_fraction(packed_row, scale_row, K):
+    out = []
+    for j in range(K):
+        byte = int(packed_row[j // 2])
+        nib = byte & 0xF if j % 2 == 0 else byte >> 4
+        v = E2M1[nib & 7] * Fraction(2) ** (int(scale_row[j // 32]) - 127)
+        out.append(-v if nib & 8 else v)
+    return out
+
+
+def _bf16_fraction(bits):
+    return Fraction(float(layer.as_f32(np.asarray([bits], np.uint16))[0]))
+
+
+@pytest.mark.parametrize("k", [0, 2, 64])
+def test_tiny_gemm_exact_rational(k):
+    M, K, N = 3, 64, 5
+    X, W, _ = _small_layer(M, K, N, 9, outl=4)
+    a, w = layer.act_max(X), layer.weight_range(W)
+    p = layer.plan(a, w, W, 0.5, k)
+    qa = layer.quantize_act(X, p["s"], p["O"])
+    Y = layer.dual_gemm_f64(qa["Aq"], qa["As"], p["Wq"], p["Ws"], qa["XO"], p["WO"])
+    assert Y.shape == (M, N)
+    for m in range(M):
+        xa = _decode_fraction(qa["Aq"][m], qa["As"][m], K)
+        for n in range(N):
+            wb = _decode_fraction(p["Wq"][n], p["Ws"][n], K)
+            acc = sum(xi * wi for xi, wi in zip(xa, wb))
+            for i in range(k):
+                acc += _bf16_fraction(qa["XO"][m, i]) * _bf16_fraction(p["WO"][n, i])
+            assert abs(Fraction(float(Y[m, n])) - acc) <= Fraction(1, 10 ** 12) * (1 + abs(acc))
+
+
+def test_k_equals_K_is_bf16_gemm():
+    """k = K routes every channel to the high-precision branch: the bulk is all
+    zero codes and Y is the f64 product of bf16(X/s) and bf16(s*W); with
+    smoothing off that is the plain bf16 GEMM of X and W."""
+    M, K, N = 24, 64, 40
+    X, W, _ = _small_layer(M, K, N, 10)
+    Xb, Wb = _bf16(X), _bf16(W)
+    a, w = layer.act_max(Xb), layer.weight_range(Wb)
+    p = layer.plan(a, w, Wb, 0.5, K, smooth=False)
+    qa = layer.quantize_act(Xb, p["s"], p["O"])
+    assert np.all(qa["Aq"] == 0) and np.all(p["Wq"] == 0)
+    Y = layer.dual_gemm_f64(qa["Aq"], qa["As"], p["Wq"], p["Ws"], qa["XO"], p["WO"])
+    ref = layer.as_f32(Xb).astype(np.float64) @ layer.as_f32(Wb).astype(np.float64).T
+    assert np.abs(Y - ref).max() <= 1e-14 * np.abs(ref).max()
+    # smoothing on: the fold keeps the product within two bf16 roundings
+    p = layer.plan(a, w, Wb, 0.6, K)
+    qa = layer.quantize_act(Xb, p["s"], p["O"])
+    Y = layer.dual_gemm_f64(qa["Aq"], qa["As"], p["Wq"], p["Ws"], qa["XO"], p["WO"])
+    bound = (2 * 2 ** -9 + 2 ** -16) * (np.abs(layer.as_f32(Xb)).astype(np.float64)
+                                         @ np.abs(layer.as_f32(Wb)).astype(np.float64).T)
+    assert np.all(np.abs(Y - ref) <= bound)
+
+
+def test_k_zero_is_pure_w4a4():
+    M, K, N = 8, 96, 12
+    X, W, _ = _small_layer(M, K, N, 11)
+    a, w = layer.act_max(X), layer.weight_range(W)
+    p = layer.plan(a, w, W, 0.6, 0)
+    assert p["O"].size == 0 and np.all(p["pos"] == -1) and p["WO"].shape == (N, 0)
+    qa = layer.quantize_act(X, p["s"], p["O"])
+    assert qa["XO"].shape == (M, 0)
+    Y = layer.dual_gemm_f64(qa["Aq"], qa["As"], p["Wq"], p["Ws"], qa["XO"], p["WO"])
+    # the bulk codes are exactly the uniform MXFP4 encodes of X/s and s*W
+    q = (X / p["s"][None, :]).astype(np.float32)
+    Aq, As = mxfp4.encode_rows(q)
+    assert np.array_equal(Aq, qa["Aq"]) and np.array_equal(As, qa["As"])
+    ref = mxfp4.decode_rows(Aq, As) @ mxfp4.decode_rows(p["Wq"], p["Ws"]).T
+    assert np.array_equal(Y, ref)
+
+
+def test_sign_symmetry_and_power_of_two():
+    M, K, N = 16, 64, 32
+    X, W, _ = _small_layer(M, K, N, 12)
+    a, w = layer.act_max(X), layer.weight_range(W)
+    p = layer.plan(a, w, W, 0.5, 4)
+    Y = layer.forward_f64(X, p)
+    Yn = layer.forward_f64(-X, p)
+    assert np.array_equal(Yn, -Y)
+    # smoothing off: X * 2^3 and W * 2^-2 scale Y by exactly 2^1
+    p0 = layer.plan(a, w, W, 0.5, 4, smooth=False)
+    p1 = layer.plan(a * 8, w / 4, (W / 4).astype(np.float32), 0.5, 4, smooth=False)
+    Y0 = layer.forward_f64(X, p0)
+    Y1 = layer.forward_f64((X * 8).astype(np.float32), p1)
+    assert np.array_equal(Y1, Y0 * 2)
+
+
+def test_fold_pack_tiles_match_rows_on_uniform_tiles():
+    """When every 32-row group of a 32-column block has the same amax in every
+    row, the 32x32 tile scale equals the 1x32 scale and the codes agree."""
+    N, K = 64, 64
+    g = np.random.default_rng(13)
+    W = (g.uniform(-0.5, 0.5, (N, K))).astype(np.float32)
+    W[:, ::32] = 0.5                      # every row of every block has amax 0.5
+    s = np.ones(K, np.float32)
+    O = np.zeros(0, np.int32)
+    r1 = layer.fold_pack(W, s, O, "1x32")
+    r2 = layer.fold_pack(W, s, O, "32x32")
+    assert np.array_equal(r1["Wq"], r2["Wq"]) and np.array_equal(r1["Ws"], r2["Ws"])
+    assert r2["Wst"].shape == (2, 2)
+
+
+def test_gelu_closed_form():
+    ys = np.array([-6.0, -1.5, -0.3, 0.0, 0.2, 1.0, 3.7, 10.0])
+    got = layer.gelu_tanh(ys)
+    for y, gv in zip(ys, got):
+        want = 0.5 * y * (1 + math.tanh(math.sqrt(2 / math.pi) * (y + 0.044715 * y ** 3)))
+        assert math.isclose(gv, want, rel_tol=1e-14, abs_tol=1e-300)
+    assert got[3] == 0.0 and math.isclose(got[-1], 10.0)
+    # close to the exact erf GELU (the tanh form's purpose), within its known 1e-3 error
+    for y, gv in zip(ys, got):
+        exact = 0.5 * y * (1 + math.erf(y / math.sqrt(2)))
+        assert abs(gv - exact) < 1e-3
+
+
+def test_bf16_rne_ties():
+    # 1 + 2^-8 is halfway between bf16 1.0 and 1.0078125: ties to even -> 1.0
+    assert int(_bf16([1 + 2 ** -8])[0]) == 0x3F80
+    # 1 + 3*2^-8 is halfway between 1.0078125 (odd) and 1.015625 (even)
+    assert int(_bf16([1 + 3 * 2 ** -8])[0]) == 0x3F82
+    assert int(_bf16([-2.0])[0]) == 0xC000
+
+
+def test_quantize_uses_division_not_reciprocal_product():
+    """The activation is divided by s (Reading: one IEEE f32 division).  At an
+    E2M1 tie the exact quotient picks the even code; a product with a rounded
+    reciprocal lands off the tie for these s and would pick the other code."""
+    g = np.random.default_rng(14)
+    found = 0
+    for t, even_code in ((0.25, 0), (0.75, 2), (1.25, 2), (1.75, 4), (2.5, 4), (3.5, 6), (5.0, 6)):
+        for _ in range(20000):
+            s = np.float32(np.ldexp(float(g.integers(1 << 12, 1 << 13)), int(g.integers(-14, -8))))
+            x = np.float32(t * float(s))
+            assert float(x) == t * float(s)
+            if np.float32(x * (np.float32(1.0) / s)) != np.float32(t):
+                break
+        else:
+            continue
+        found += 1
+        X = np.zeros((1, 32), np.float32)
+        X[0, 0] = np.float32(6.0) * s            # block amax -> quotient 6 -> scale 2^0
+        X[0, 1] = x
+        S = np.full(32, s, np.float32)
+        r = layer.quantize_act(X, S, np.zeros(0, np.int32))
+        assert int(r["As"][0, 0]) == 127
+        assert int(mxfp4.unpack_nibbles(r["Aq"])[0, 1]) == even_code, t
+    assert found >= 3
