@@ -1,0 +1,193 @@
+"""Benchmark of the dual-branch W4A4 FFN layer on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input:
+calibrate (per-channel activation maxima) -> weight column ranges -> plan
+(Eq. (2) scales, Eq. (4) top-k, fold + MXFP4 pack) -> fused activation
+quantize -> dual-branch GEMM (bf16 output), every stage a kernel of
+libmixed_gemm on torch's current HIP stream.
+
+Default workload: the Wan2.2-A14B FFN up-projection at 480p,
+M = 32760 tokens x K = 5120 -> N = 13824, alpha = 0.6, k = 64, 1x32 blocks.
+
+Prints ONE JSON line.  `value` = 2*M*K*N / (time of one whole step), in
+TFLOP/s; the dual-GEMM kernel's own rate is in `roofline`.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP4_TFLOPS = 10100.0          # MI355X dense MXFP4 MFMA (published)
+PEAK_HBM_GBS = 8000.0              # MI355X HBM3E (published)
+METRIC = "dual-branch W4A4 FFN GEMM effective TFLOPS, % MXFP4 MFMA peak (480p/720p)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dual_gemm_ffn0_480p_traffic.json")
+GEMM_SRC = os.path.join(ROOT, "mixed_gemm_amd", "csrc", "k_gemm.hip")
+
+
+def gemm_source_hash() -> str:
+    return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic() -> float | None:
+    """HBM bytes per dual-GEMM launch from the committed rocprofv3 counter
+    summary, or None when there is none or the kernel source changed since."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != gemm_source_hash():
+        return None
+    return float(t["bytes_per_launch"])
+
+
+def cpu_baseline(w, X, W, rows: int) -> dict:
+    """The oracle as it stands, on a bounded sample: the plan on the full W and
+    the per-row work (calibration, quantize, float64 dual GEMM) on `rows` rows;
+    the per-row cost is scaled to the workload's M."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import layer
+    t0 = time.perf_counter()
+    a = layer.act_max(X[:rows])
+    wr = layer.weight_range(W)
+    p = layer.plan(a, wr, W, w.alpha, w.k)
+    t1 = time.perf_counter()
+    qa = layer.quantize_act(X[:rows], p["s"], p["O"])
+    Y = layer.dual_gemm_f64(qa["Aq"], qa["As"], p["Wq"], p["Ws"], qa["XO"], p["WO"])
+    t2 = time.perf_counter()
+    assert Y.shape == (rows, w.N)
+    t_plan, t_rows = t1 - t0, t2 - t1
+    t_full = t_plan + t_rows * w.M / rows
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(w.flops() / t_full / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"oracle step on {rows} of {w.M} rows (plan on the full W: {t_plan:.1f} s; "
+                      f"per-row work {t_rows:.1f} s scaled x{w.M / rows:.0f}); est. full step {t_full:.0f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="ffn0_480p_32760x5120x13824")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=256)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer shards along tokens with no exchange in the forward pass)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import mixed_gemm_amd as mg
+    import synth
+
+    w = synth.ALL[args.workload]
+    torch.cuda.set_device(0)
+    X_h, W_h = w.make_x(), w.make_w()
+    bf = w.dtype == "bf16"
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        t = torch.from_numpy(a.view(np.int16) if bf else a).cuda()
+        return t.view(torch.bfloat16) if bf else t
+
+    X, W = dev(X_h), dev(W_h)
+    M, K, N = w.M, w.K, w.N
+    desc = mg.make_desc(K, N, w.k, w.alpha, "1x32", True)
+    plan = mg.Plan.empty(desc)
+    act = mg.Act.empty(desc, M)
+    act_max = torch.empty(K, dtype=torch.float32, device="cuda")
+    w_max = torch.empty(K, dtype=torch.float32, device="cuda")
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    stages = ("calib", "wrange", "plan", "quant", "gemm")
+    ev = {s: [] for s in stages}
+
+    def step(record: bool):
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] if record else None
+        if record:
+            marks[0].record(stream)
+        mg.mg_calib_reset(act_max)
+        mg.mg_calib_act(X, act_max)
+        if record:
+            marks[1].record(stream)
+        mg.mg_weight_range(W, w_max)
+        if record:
+            marks[2].record(stream)
+        mg.mg_plan_build(plan, act_max, w_max, W)
+        if record:
+            marks[3].record(stream)
+        mg.mg_quantize_act(plan, X, act)
+        if record:
+            marks[4].record(stream)
+        mg.mg_dual_gemm(plan, act, Y)
+        if record:
+            marks[5].record(stream)
+            for i, s in enumerate(stages):
+                ev[s].append((marks[i], marks[i + 1]))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    ms = {s: float(np.mean([a.elapsed_time(b) for a, b in ev[s]])) for s in stages}
+
+    flops = w.flops()
+    value = flops / (ms_step * 1e-3) / 1e12
+    gemm_tflops = flops / (ms["gemm"] * 1e-3) / 1e12
+    quant_bytes = M * K * (2 if bf else 4) + M * K // 2 + M * K // 32 + 2 * M * w.k
+    calib_bytes = M * K * (2 if bf else 4)
+    traffic = measured_traffic()
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4+bf16",
+        "data": "synthetic (seeded heavy-tailed activations, Gaussian weights)",
+        "config": {"workload": w.name, "M": M, "K": K, "N": N, "k": w.k, "alpha": w.alpha,
+                   "weight_blocks": "1x32", "output": "bf16"},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP4_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP4_TFLOPS, 4),
+                     "traffic": traffic},
+        "kernel_ms": {s: round(v, 4) for s, v in ms.items()},
+        "gemm_tflops": round(gemm_tflops, 2),
+        "gemm_pct_mxfp4_peak": round(100 * gemm_tflops / PEAK_FP4_TFLOPS, 2),
+        "quant_gbs": round(quant_bytes / (ms["quant"] * 1e-3) / 1e9, 1),
+        "quant_pct_hbm": round(100 * quant_bytes / (ms["quant"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+        "calib_gbs": round(calib_bytes / (ms["calib"] * 1e-3) / 1e9, 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, X_h, W_h, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,176 @@
+/*
+ * mixed_gemm.h -- C ABI of the smoothed, outlier-split, dual-branch W4A4
+ * linear layer for AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the one of "W4A4 Quantization for Inference on
+ * Wan2.2-I2V-A14B" (arXiv 2606.29337):
+ *   Eq. (1)  Y = (X / s)(s * W), s applied along input channels;
+ *   Eq. (2)  s_j = act_max_j^alpha / w_max_j^(1 - alpha);
+ *   Eq. (4)  O = top-k input channels by max_t |x_tj|;
+ *   Eq. (5)  Y = X_J W^(q)_J + X_O W^(hp)_O: MXFP4 W4A4 bulk + BF16 outliers.
+ * The life cycle is calibrate -> plan(alpha, k) -> forward.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - X is [M][K] row-major (tokens x input channels); W is [N][K] row-major
+ *    (nn.Linear layout, K contiguous); Y is [M][N] row-major bf16.
+ *  - bf16 values travel as uint16_t bit patterns.
+ *  - Every pointer argument is a DEVICE pointer owned by the caller; the
+ *    library allocates no device memory and keeps no device state between
+ *    calls.  Base pointers must be 16-byte aligned.
+ *  - Every call validates its arguments on the host, then enqueues its
+ *    kernels on `stream` and returns without synchronizing.  A device fault
+ *    surfaces at the caller's next synchronization on that stream.
+ *  - Return value: MG_OK (0) or a negative mg_status; mg_last_error() gives a
+ *    message for the last failing call on the calling thread.
+ *  - Inputs must be finite; NaN/Inf inputs give unspecified results.
+ *  - MXFP4 = E2M1 elements + one E8M0 scale per 32 consecutive K (OCP MX):
+ *    scale code c = floor(log2 amax) - 2 + 127 (clamped at 0), elements
+ *    rounded to nearest, ties to the even code, saturating at +-6, sign copied
+ *    (so -0 encodes as 0x8).  Two elements per byte, even K in the low nibble.
+ */
+#ifndef MIXED_GEMM_H
+#define MIXED_GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MG_OK = 0,
+    MG_ERR_ARG = -1,         /* null pointer, bad alpha, bad enum value          */
+    MG_ERR_SHAPE = -2,       /* K or N not a multiple of 32, k > K, negative size */
+    MG_ERR_DTYPE = -3,       /* dtype not MG_F32 / MG_BF16                        */
+    MG_ERR_ALIGN = -4,       /* a base pointer not 16-byte aligned                */
+    MG_ERR_UNSUPPORTED = -5, /* a size beyond the documented limits               */
+    MG_ERR_HIP = -6          /* a HIP runtime call failed (launch error)          */
+} mg_status;
+
+typedef enum { MG_F32 = 0, MG_BF16 = 1 } mg_dtype;
+
+/* Weight block-scale layout (the block-packing paragraph after Eq. (5)):
+ * MG_W_1X32   one E8M0 per (output row n, 32 consecutive K);
+ * MG_W_32X32  one E8M0 per aligned tile of 32 output rows x 32 K (requires N % 32 == 0). */
+typedef enum { MG_W_1X32 = 0, MG_W_32X32 = 1 } mg_wlayout;
+
+/* Plan descriptor.  K, N: input / output widths (multiples of 32, K <= 65536);
+ * k: number of outlier columns, 0 <= k <= K; layout: mg_wlayout;
+ * smooth: 1 to apply Eq. (2) with alpha in (0, 1), 0 for s = 1. */
+typedef struct {
+    int32_t K, N, k;
+    int32_t layout;
+    int32_t smooth;
+    int32_t reserved;   /* must be 0 */
+    double alpha;
+} mg_plan_desc;
+
+/* Plan buffers (caller-allocated, sizes from mg_plan_bytes, in this order):
+ *  s   [K]        f32  smoothing scales, Eq. (2), evaluated in f64, rounded once;
+ *  rcp [K]        f32  RN(1/s_j), used inside the exact division of the forward;
+ *  O   [k]        i32  outlier channels, ascending (null allowed when k == 0);
+ *  pos [K]        i32  index of channel j in O, or -1;
+ *  Wq  [N][K/2]   u8   MXFP4 payload of the folded bulk weights RN(s_j W[n][j]),
+ *                      outlier columns set to +0 before encoding;
+ *  Ws  [N][K/32]  u8   E8M0 scale of each (row, 32-block) -- for MG_W_32X32 the
+ *                      tile's code repeated on each of its 32 rows;
+ *  Wst [N/32][K/32] u8 compact tile codes (MG_W_32X32 only; null allowed otherwise);
+ *  WO  [N][k]     bf16 folded outlier columns (null allowed when k == 0). */
+typedef struct {
+    mg_plan_desc d;
+    float* s;
+    float* rcp;
+    int32_t* O;
+    int32_t* pos;
+    uint8_t* Wq;
+    uint8_t* Ws;
+    uint8_t* Wst;
+    uint16_t* WO;
+} mg_plan;
+
+/* Per-forward activation workspace (sizes from mg_act_bytes):
+ *  Aq [M][K/2] u8 MXFP4 payload of the bulk quotients, As [M][K/32] u8 E8M0,
+ *  XO [M][k] bf16 outlier quotients (null allowed when k == 0). */
+typedef struct {
+    uint8_t* Aq;
+    uint8_t* As;
+    uint16_t* XO;
+} mg_act;
+
+/* Library version (major*10000 + minor*100 + patch). */
+int mg_version(void);
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* mg_last_error(void);
+
+/* Host-only size queries.  out[8] = bytes of s, rcp, O, pos, Wq, Ws, Wst, WO;
+ * out[3] = bytes of Aq, As, XO for M rows.  A zero size means "may be null". */
+int mg_plan_bytes(const mg_plan_desc* d, size_t out[8]);
+int mg_act_bytes(const mg_plan_desc* d, int64_t M, size_t out[3]);
+
+/* ---- calibration: per-input-channel activation maxima and weight column
+ * ranges (the calibration paragraph before Eq. (4); Eq. (4)'s score). ---- */
+
+/* act_max[0..K) := +0.  Start of a calibration run. */
+int mg_calib_reset(float* act_max, int32_t K, hipStream_t stream);
+
+/* act_max[j] = max(act_max[j], max_t |X[t][j]|) over the M rows of X
+ * (dtype MG_F32 or MG_BF16).  Exact, order-independent: batches may be fed
+ * in any order and split anywhere.  M == 0 is a no-op. */
+int mg_calib_act(const void* X, int32_t dtype, int64_t M, int32_t K, float* act_max,
+                 hipStream_t stream);
+
+/* w_max[j] = max_n |W[n][j]| (overwrites w_max). */
+int mg_weight_range(const void* W, int32_t dtype, int32_t N, int32_t K, float* w_max,
+                    hipStream_t stream);
+
+/* ---- planning (offline, once per layer) ---- */
+
+/* Eq. (2): s, rcp from act_max and w_max (floor 1e-5 on both before the
+ * powers); s = rcp = 1 when d.smooth == 0. */
+int mg_smooth_scales(const mg_plan* p, const float* act_max, const float* w_max,
+                     hipStream_t stream);
+
+/* Eq. (4): O = the k channels first in the order (act_max desc, index asc),
+ * stored ascending, and pos. */
+int mg_outlier_set(const mg_plan* p, const float* act_max, hipStream_t stream);
+
+/* Eq. (1) fold + extraction + block packing of W [N][K] (dtype MG_F32 or
+ * MG_BF16) into Wq, Ws, (Wst), WO, reading p->s and p->pos. */
+int mg_fold_pack(const mg_plan* p, const void* W, int32_t dtype, hipStream_t stream);
+
+/* All three planning steps in order. */
+int mg_plan_build(const mg_plan* p, const float* act_max, const float* w_max, const void* W,
+                  int32_t dtype, hipStream_t stream);
+
+/* ---- forward (per batch) ---- */
+
+/* Runtime activation path: q = RN_f32(X[m][j] / s_j) (exact IEEE division),
+ * XO[m][pos_j] = bf16(q), bulk q with outlier columns set to +0 MXFP4-encoded
+ * into Aq/As.  M == 0 is a no-op. */
+int mg_quantize_act(const mg_plan* p, const void* X, int32_t dtype, int64_t M,
+                    const mg_act* a, hipStream_t stream);
+
+/* Eq. (5): Y[m][n] = sum_j Aq*Wq with their E8M0 scales + sum_i XO[m][i] WO[n][i],
+ * accumulated in fp32.  y_dtype MG_BF16: Y is the layer output [M][N] bf16,
+ * the fp32 sum rounded once to nearest-even.  y_dtype MG_F32: Y [M][N] f32
+ * holds the fp32 sums unrounded (for callers that keep fp32 activations and
+ * for checking the accumulation itself).  M == 0 is a no-op. */
+int mg_dual_gemm(const mg_plan* p, const mg_act* a, int64_t M, void* Y, int32_t y_dtype,
+                 hipStream_t stream);
+
+/* mg_quantize_act followed by mg_dual_gemm. */
+int mg_forward(const mg_plan* p, const void* X, int32_t dtype, int64_t M, const mg_act* a,
+               void* Y, int32_t y_dtype, hipStream_t stream);
+
+/* Between the two projections of the FFN block: out[i] = bf16_RNE(gelu_tanh(in[i]))
+ * computed in f32, for n bf16 values (in == out allowed). */
+int mg_gelu_tanh_bf16(const uint16_t* in, uint16_t* out, int64_t n, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MIXED_GEMM_H */

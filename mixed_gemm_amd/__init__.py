@@ -1,0 +1,290 @@
+"""Python binding of libmixed_gemm (the smoothed, outlier-split, dual-branch
+W4A4 linear layer of "W4A4 Quantization for Inference on Wan2.2-I2V-A14B" on
+MI355X / gfx950).
+
+Argument marshalling only: every function below has the name of the C entry
+point it calls (``include/mixed_gemm.h``), takes torch tensors for the device
+buffers, and passes their data pointers and torch's current HIP stream.  Every
+step of the layer runs in the library's HIP kernels; there is no fallback.
+If the library is not built this module raises on first use.
+
+bf16 data travels in ``torch.bfloat16`` (or 16-bit integer) tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmixed_gemm.so")
+
+MG_F32, MG_BF16 = 0, 1
+MG_W_1X32, MG_W_32X32 = 0, 1
+LAYOUTS = {"1x32": MG_W_1X32, "32x32": MG_W_32X32}
+
+STATUS = {0: "MG_OK", -1: "MG_ERR_ARG", -2: "MG_ERR_SHAPE", -3: "MG_ERR_DTYPE", -4: "MG_ERR_ALIGN",
+          -5: "MG_ERR_UNSUPPORTED", -6: "MG_ERR_HIP"}
+
+
+class MGError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class mg_plan_desc(ctypes.Structure):
+    _fields_ = [("K", ctypes.c_int32), ("N", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("layout", ctypes.c_int32), ("smooth", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("alpha", ctypes.c_double)]
+
+
+class mg_plan(ctypes.Structure):
+    _fields_ = [("d", mg_plan_desc), ("s", ctypes.c_void_p), ("rcp", ctypes.c_void_p),
+                ("O", ctypes.c_void_p), ("pos", ctypes.c_void_p), ("Wq", ctypes.c_void_p),
+                ("Ws", ctypes.c_void_p), ("Wst", ctypes.c_void_p), ("WO", ctypes.c_void_p)]
+
+
+class mg_act(ctypes.Structure):
+    _fields_ = [("Aq", ctypes.c_void_p), ("As", ctypes.c_void_p), ("XO", ctypes.c_void_p)]
+
+
+EXPORTS = ("mg_version", "mg_last_error", "mg_plan_bytes", "mg_act_bytes", "mg_calib_reset",
+           "mg_calib_act", "mg_weight_range", "mg_smooth_scales", "mg_outlier_set", "mg_fold_pack",
+           "mg_plan_build", "mg_quantize_act", "mg_dual_gemm", "mg_forward", "mg_gelu_tanh_bf16")
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmixed_gemm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m mixed_gemm_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        P = ctypes.POINTER
+        sig = {
+            "mg_version": ([], ctypes.c_int),
+            "mg_last_error": ([], ctypes.c_char_p),
+            "mg_plan_bytes": ([P(mg_plan_desc), P(sz)], ctypes.c_int),
+            "mg_act_bytes": ([P(mg_plan_desc), i64, P(sz)], ctypes.c_int),
+            "mg_calib_reset": ([vp, i32, vp], ctypes.c_int),
+            "mg_calib_act": ([vp, i32, i64, i32, vp, vp], ctypes.c_int),
+            "mg_weight_range": ([vp, i32, i32, i32, vp, vp], ctypes.c_int),
+            "mg_smooth_scales": ([P(mg_plan), vp, vp, vp], ctypes.c_int),
+            "mg_outlier_set": ([P(mg_plan), vp, vp], ctypes.c_int),
+            "mg_fold_pack": ([P(mg_plan), vp, i32, vp], ctypes.c_int),
+            "mg_plan_build": ([P(mg_plan), vp, vp, vp, i32, vp], ctypes.c_int),
+            "mg_quantize_act": ([P(mg_plan), vp, i32, i64, P(mg_act), vp], ctypes.c_int),
+            "mg_dual_gemm": ([P(mg_plan), P(mg_act), i64, vp, i32, vp], ctypes.c_int),
+            "mg_forward": ([P(mg_plan), vp, i32, i64, P(mg_act), vp, i32, vp], ctypes.c_int),
+            "mg_gelu_tanh_bf16": ([vp, vp, i64, vp], ctypes.c_int),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(code: int) -> None:
+    if code != 0:
+        raise MGError(code, lib().mg_last_error().decode())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    if t is None or t.numel() == 0:
+        return None
+    if not t.is_cuda:
+        raise ValueError("device tensor expected")
+    if not t.is_contiguous():
+        raise ValueError("contiguous tensor expected")
+    return t.data_ptr()
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MG_F32
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return MG_BF16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+# ----------------------------------------------------------------------------- plan / workspace
+
+def make_desc(K: int, N: int, k: int, alpha: float = 0.5, layout: str | int = "1x32",
+              smooth: bool = True) -> mg_plan_desc:
+    lay = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+    return mg_plan_desc(int(K), int(N), int(k), lay, int(bool(smooth)), 0, float(alpha))
+
+
+def mg_plan_bytes(desc: mg_plan_desc) -> list[int]:
+    out = (ctypes.c_size_t * 8)()
+    _check(lib().mg_plan_bytes(ctypes.byref(desc), out))
+    return list(out)
+
+
+def mg_act_bytes(desc: mg_plan_desc, M: int) -> list[int]:
+    out = (ctypes.c_size_t * 3)()
+    _check(lib().mg_act_bytes(ctypes.byref(desc), int(M), out))
+    return list(out)
+
+
+@dataclass
+class Plan:
+    """Device buffers of one layer's plan (allocated with torch from mg_plan_bytes)."""
+    desc: mg_plan_desc
+    s: torch.Tensor
+    rcp: torch.Tensor
+    O: torch.Tensor
+    pos: torch.Tensor
+    Wq: torch.Tensor
+    Ws: torch.Tensor
+    Wst: torch.Tensor
+    WO: torch.Tensor
+
+    @staticmethod
+    def empty(desc: mg_plan_desc, device="cuda") -> "Plan":
+        b = mg_plan_bytes(desc)
+        K, N, k = desc.K, desc.N, desc.k
+        e = lambda n, dt: torch.empty(n, dtype=dt, device=device)
+        return Plan(desc, e(K, torch.float32), e(K, torch.float32), e(k, torch.int32), e(K, torch.int32),
+                    e((N, K // 2), torch.uint8), e((N, K // 32), torch.uint8),
+                    e((N // 32, K // 32), torch.uint8) if b[6] else e(0, torch.uint8),
+                    e((N, k), torch.bfloat16))
+
+    def c(self) -> mg_plan:
+        return mg_plan(self.desc, _ptr(self.s), _ptr(self.rcp), _ptr(self.O), _ptr(self.pos), _ptr(self.Wq),
+                       _ptr(self.Ws), _ptr(self.Wst), _ptr(self.WO))
+
+    def tensors(self) -> dict:
+        return dict(s=self.s, rcp=self.rcp, O=self.O, pos=self.pos, Wq=self.Wq, Ws=self.Ws, Wst=self.Wst,
+                    WO=self.WO)
+
+
+@dataclass
+class Act:
+    """Per-forward activation workspace (Aq, As, XO) for M rows."""
+    M: int
+    Aq: torch.Tensor
+    As: torch.Tensor
+    XO: torch.Tensor
+
+    @staticmethod
+    def empty(desc: mg_plan_desc, M: int, device="cuda") -> "Act":
+        K, k = desc.K, desc.k
+        return Act(M, torch.empty((M, K // 2), dtype=torch.uint8, device=device),
+                   torch.empty((M, K // 32), dtype=torch.uint8, device=device),
+                   torch.empty((M, k), dtype=torch.bfloat16, device=device))
+
+    def c(self) -> mg_act:
+        return mg_act(_ptr(self.Aq), _ptr(self.As), _ptr(self.XO))
+
+
+# ----------------------------------------------------------------------------- entry points
+
+def mg_version() -> int:
+    return lib().mg_version()
+
+
+def mg_calib_reset(act_max: torch.Tensor, stream=None) -> None:
+    _check(lib().mg_calib_reset(_ptr(act_max), act_max.numel(), _stream(stream)))
+
+
+def mg_calib_act(X: torch.Tensor, act_max: torch.Tensor, stream=None) -> None:
+    M, K = X.shape
+    _check(lib().mg_calib_act(_ptr(X), _dtype(X), M, K, _ptr(act_max), _stream(stream)))
+
+
+def mg_weight_range(W: torch.Tensor, w_max: torch.Tensor, stream=None) -> None:
+    N, K = W.shape
+    _check(lib().mg_weight_range(_ptr(W), _dtype(W), N, K, _ptr(w_max), _stream(stream)))
+
+
+def mg_smooth_scales(plan: Plan, act_max, w_max, stream=None) -> None:
+    p = plan.c()
+    _check(lib().mg_smooth_scales(ctypes.byref(p), _ptr(act_max), _ptr(w_max), _stream(stream)))
+
+
+def mg_outlier_set(plan: Plan, act_max, stream=None) -> None:
+    p = plan.c()
+    _check(lib().mg_outlier_set(ctypes.byref(p), _ptr(act_max), _stream(stream)))
+
+
+def mg_fold_pack(plan: Plan, W: torch.Tensor, stream=None) -> None:
+    p = plan.c()
+    _check(lib().mg_fold_pack(ctypes.byref(p), _ptr(W), _dtype(W), _stream(stream)))
+
+
+def mg_plan_build(plan: Plan, act_max, w_max, W: torch.Tensor, stream=None) -> None:
+    p = plan.c()
+    _check(lib().mg_plan_build(ctypes.byref(p), _ptr(act_max), _ptr(w_max), _ptr(W), _dtype(W),
+                               _stream(stream)))
+
+
+def mg_quantize_act(plan: Plan, X: torch.Tensor, act: Act, stream=None) -> None:
+    p, a = plan.c(), act.c()
+    _check(lib().mg_quantize_act(ctypes.byref(p), _ptr(X), _dtype(X), X.shape[0], ctypes.byref(a),
+                                 _stream(stream)))
+
+
+def mg_dual_gemm(plan: Plan, act: Act, Y: torch.Tensor, stream=None) -> None:
+    p, a = plan.c(), act.c()
+    _check(lib().mg_dual_gemm(ctypes.byref(p), ctypes.byref(a), act.M, _ptr(Y), _dtype(Y), _stream(stream)))
+
+
+def mg_forward(plan: Plan, X: torch.Tensor, act: Act, Y: torch.Tensor, stream=None) -> None:
+    p, a = plan.c(), act.c()
+    _check(lib().mg_forward(ctypes.byref(p), _ptr(X), _dtype(X), X.shape[0], ctypes.byref(a), _ptr(Y),
+                            _dtype(Y), _stream(stream)))
+
+
+def mg_gelu_tanh_bf16(inp: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    _check(lib().mg_gelu_tanh_bf16(_ptr(inp), _ptr(out), inp.numel(), _stream(stream)))
+
+
+# ----------------------------------------------------------------------------- convenience
+
+def calibrate(batches, K: int, device="cuda", stream=None) -> torch.Tensor:
+    """Running per-channel activation maxima over an iterable of [M][K] device tensors."""
+    act_max = torch.empty(K, dtype=torch.float32, device=device)
+    mg_calib_reset(act_max, stream)
+    for X in batches:
+        mg_calib_act(X, act_max, stream)
+    return act_max
+
+
+def plan(act_max: torch.Tensor, W: torch.Tensor, alpha: float, k: int, layout: str = "1x32",
+         smooth: bool = True, stream=None) -> Plan:
+    """calibrated maxima + weights -> a built plan (weight ranges, Eq. (2), Eq. (4), fold + pack)."""
+    N, K = W.shape
+    desc = make_desc(K, N, k, alpha, layout, smooth)
+    p = Plan.empty(desc, W.device)
+    w_max = torch.empty(K, dtype=torch.float32, device=W.device)
+    mg_weight_range(W, w_max, stream)
+    mg_plan_build(p, act_max, w_max, W, stream)
+    return p
+
+
+def forward(p: Plan, X: torch.Tensor, act: Act | None = None, Y: torch.Tensor | None = None,
+            stream=None) -> torch.Tensor:
+    M = X.shape[0]
+    if act is None or act.M != M:
+        act = Act.empty(p.desc, M, X.device)
+    if Y is None:
+        Y = torch.empty((M, p.desc.N), dtype=torch.bfloat16, device=X.device)
+    mg_forward(p, X, act, Y, stream)
+    return Y

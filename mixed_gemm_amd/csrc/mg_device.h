@@ -1,0 +1,81 @@
+// Device-side numeric helpers shared by the kernels of the W4A4 layer (gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mg {
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Round-to-nearest-even f32 -> bf16 bits (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// E8M0 block-scale code from the bit pattern of a non-negative f32 amax:
+// floor(log2 amax) - 2 + 127 = biased exponent - 2, clamped at 0.
+__device__ __forceinline__ uint32_t e8m0_from_amax_bits(uint32_t amax_bits) {
+    int e = (int)(amax_bits >> 23);
+    return (uint32_t)(e > 2 ? e - 2 : 0);
+}
+
+// E2M1 magnitude code of r >= 0 (already divided by the block scale):
+// nearest of {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the even code, saturating.
+// Each midpoint is counted when r passes it; at the midpoints whose upper
+// neighbour has an even code (0.75, 1.75, 3.5) equality also counts.
+__device__ __forceinline__ uint32_t e2m1_code(float r) {
+    uint32_t m = 0;
+    m += r > 0.25f;
+    m += r >= 0.75f;
+    m += r > 1.25f;
+    m += r >= 1.75f;
+    m += r > 2.5f;
+    m += r >= 3.5f;
+    m += r > 5.0f;
+    return m;
+}
+
+// Nibble (sign << 3 | code) of v under block scale code c.  ldexp is exact
+// (power-of-two scaling into the normal range).
+__device__ __forceinline__ uint32_t e2m1_nibble(float v, uint32_t c) {
+    float r = __builtin_ldexpf(__builtin_fabsf(v), 127 - (int)c);
+    return ((__float_as_uint(v) >> 28) & 8u) | e2m1_code(r);
+}
+
+// IEEE f32 quotient x / s from rcp = RN(1/s) with Markstein's FMA-based
+// correction (P. Markstein, IBM J. Res. Dev. 1990; Muller et al., Handbook of
+// Floating-Point Arithmetic, division with a fused multiply-add): q0 = x*rcp,
+// r = x - q0*s (exact), q = q0 + r*rcp.  The result is the correctly rounded
+// quotient when the remainder cannot underflow and the quotient is normal;
+// callers check div_fast_ok() and otherwise divide with __fdiv_rn.  s > 0, so
+// the sign of the quotient is the sign of x (this also keeps -0 / s = -0).
+__device__ __forceinline__ float div_fast(float x, float s, float rcp) {
+    const float q0 = x * rcp;
+    const float r = __builtin_fmaf(-q0, s, x);
+    const float q = __builtin_fmaf(r, rcp, q0);
+    return __builtin_copysignf(q, x);
+}
+
+// Range where div_fast is exact: x == 0 or 2^-100 <= |x| <= 2^100, given a
+// divisor with 2^-20 <= s <= 2^20 (so the quotient stays far from underflow
+// and overflow and the exact remainder is representable).
+__device__ __forceinline__ bool div_fast_ok_x(float x) {
+    const float ax = __builtin_fabsf(x);
+    return ax == 0.0f || (ax >= 0x1p-100f && ax <= 0x1p100f);
+}
+__device__ __forceinline__ bool div_fast_ok_s(float s) { return s >= 0x1p-20f && s <= 0x1p20f; }
+
+// E8M0 code c -> the f32 scale 2^(c - 127) (c = 0 gives the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t c) {
+    return __uint_as_float(c ? (c << 23) : 0x00200000u);
+}
+
+// Hardware E2M1 encode of two f32 values divided by an f32 power-of-two scale
+// (v_cvt_scalef32_pk_fp4_f32: nearest, ties to even, saturating, sign kept),
+// written into byte `sel` of `word`.  Checked against the threshold encoder
+// e2m1_nibble over every f32 bit pattern at scales 2^-127 .. 2^127.
+#define MG_CVT_FP4X2(word, a, b, scale, sel) \
+    (word) = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((word), (a), (b), (scale), (sel))
+
+}  // namespace mg

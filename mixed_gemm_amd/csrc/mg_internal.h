@@ -1,0 +1,35 @@
+// Internal launcher interface between the C ABI (mg_api.hip) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mixed_gemm.h"
+
+namespace mg {
+
+// Largest supported input width (LDS-resident per-channel tables in the plan kernels).
+constexpr int32_t kMaxK = 65536;
+
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t st);
+hipError_t launch_colmax(const void* X, int32_t dtype, int64_t R, int32_t K, float* out,
+                         hipStream_t st);
+hipError_t launch_smooth(const float* a, const float* w, int32_t K, double alpha, int32_t smooth,
+                         float* s, float* rcp, hipStream_t st);
+hipError_t launch_topk(const float* a, int32_t K, int32_t k, int32_t* O, int32_t* pos,
+                       hipStream_t st);
+hipError_t launch_fold_pack(const void* W, int32_t dtype, int32_t N, int32_t K, int32_t k,
+                            int32_t layout, const float* s, const int32_t* pos, uint8_t* Wq,
+                            uint8_t* Ws, uint8_t* Wst, uint16_t* WO, hipStream_t st);
+hipError_t launch_quant(const void* X, int32_t dtype, int64_t M, int32_t K, int32_t k,
+                        const float* s, const float* rcp, const int32_t* pos, uint8_t* Aq,
+                        uint8_t* As, uint16_t* XO, hipStream_t st);
+hipError_t launch_dual_gemm(const uint8_t* Aq, const uint8_t* As, const uint16_t* XO,
+                            const uint8_t* Wq, const uint8_t* Ws, const uint16_t* WO, int64_t M,
+                            int32_t N, int32_t K, int32_t k, void* Y, int32_t y_dtype,
+                            hipStream_t st);
+hipError_t launch_gelu(const uint16_t* in, uint16_t* out, int64_t n, hipStream_t st);
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+}  // namespace mg

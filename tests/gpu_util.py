@@ -1,0 +1,75 @@
+"""Helpers shared by the GPU tests: moving seeded numpy inputs to the device and
+running the library's entry points stage by stage."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import mixed_gemm_amd as mg
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    """numpy -> cuda tensor; uint16 arrays are bf16 bit patterns."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    t = t.detach()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def run_pipeline(X: np.ndarray, W: np.ndarray, alpha: float, k: int, layout: str = "1x32",
+                 smooth: bool = True, calib_batches: int = 1) -> dict:
+    """calibrate (optionally in several batches) -> weight ranges -> plan -> quantize -> GEMM,
+    each through its own entry point; returns every artefact on the host."""
+    Xd, Wd = dev(X), dev(W)
+    M, K = X.shape
+    N = W.shape[0]
+    act_max = torch.empty(K, dtype=torch.float32, device="cuda")
+    mg.mg_calib_reset(act_max)
+    for part in np.array_split(np.arange(M), calib_batches):
+        if part.size:
+            mg.mg_calib_act(Xd[part[0]:part[-1] + 1], act_max)
+    w_max = torch.empty(K, dtype=torch.float32, device="cuda")
+    mg.mg_weight_range(Wd, w_max)
+    desc = mg.make_desc(K, N, k, alpha, layout, smooth)
+    p = mg.Plan.empty(desc)
+    mg.mg_plan_build(p, act_max, w_max, Wd)
+    a = mg.Act.empty(desc, M)
+    mg.mg_quantize_act(p, Xd, a)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    mg.mg_dual_gemm(p, a, Y)
+    Y32 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    mg.mg_dual_gemm(p, a, Y32)
+    torch.cuda.synchronize()
+    out = dict(act_max=host(act_max), w_max=host(w_max), Y=host(Y), Y32=host(Y32))
+    out.update({n: host(t) for n, t in p.tensors().items()})
+    out.update(Aq=host(a.Aq), As=host(a.As), XO=host(a.XO))
+    return out
+
+
+def bf16_to_f64(b: np.ndarray) -> np.ndarray:
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def check_output(Y_bf16: np.ndarray, Y32: np.ndarray, Y64: np.ndarray, tol: float = 2e-3) -> float:
+    """The GEMM's fp32 result against the unrounded float64 oracle:
+    max|Y32 - Y64| / max|Y64| <= tol; the bf16 output is exactly the fp32
+    result rounded to nearest-even; and every bf16 element is within one bf16
+    rounding (2^-8 relative) of the oracle plus the fp32 error."""
+    err = float(np.abs(Y32.astype(np.float64) - Y64).max() / np.abs(Y64).max())
+    assert err <= tol, err
+    assert np.array_equal(Y_bf16, f32_to_bf16_bits(Y32))
+    yb = bf16_to_f64(Y_bf16)
+    assert np.all(np.abs(yb - Y64) <= 2.0 ** -8 * np.abs(Y64) + 2 * err * np.abs(Y64).max() + 1e-30)
+    return err

@@ -1,0 +1,110 @@
+"""The C ABI on the CPU: the library loads, exports every entry point the header
+declares, answers size queries with the closed-form byte counts, and rejects
+bad arguments on the host (no GPU call is reached by these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixed_gemm_amd as mg
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "mixed_gemm.h")
+FAKE = 1 << 20          # aligned, never dereferenced: every call below fails validation first
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(mg_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) >= 15
+    L = mg.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(mg.EXPORTS)
+    assert mg.mg_version() >= 100
+
+
+def test_plan_and_act_sizes():
+    d = mg.make_desc(5120, 13824, 64, 0.6, "1x32")
+    b = mg.mg_plan_bytes(d)
+    assert b == [4 * 5120, 4 * 5120, 4 * 64, 4 * 5120, 13824 * 2560, 13824 * 160, 0, 2 * 13824 * 64]
+    d2 = mg.make_desc(512, 1024, 8, 0.5, "32x32")
+    assert mg.mg_plan_bytes(d2)[6] == 32 * 16
+    assert mg.mg_act_bytes(d, 32760) == [32760 * 2560, 32760 * 160, 2 * 32760 * 64]
+    assert mg.mg_act_bytes(d, 0) == [0, 0, 0]
+
+
+@pytest.mark.parametrize("K,N,k,alpha,layout,smooth,code", [
+    (100, 64, 4, 0.5, 0, 1, -2),      # K % 32
+    (0, 64, 0, 0.5, 0, 1, -2),        # K == 0
+    (64, 48, 4, 0.5, 0, 1, -2),       # N % 32
+    (64, 64, 65, 0.5, 0, 1, -2),      # k > K
+    (64, 64, -1, 0.5, 0, 1, -2),      # k < 0
+    (64, 64, 4, 0.0, 0, 1, -1),       # alpha
+    (64, 64, 4, 1.0, 0, 1, -1),       # alpha
+    (64, 64, 4, 0.5, 2, 1, -1),       # layout
+    (64, 64, 4, 0.5, 0, 3, -1),       # smooth flag
+    (131072, 64, 4, 0.5, 0, 1, -5),   # K beyond the limit
+])
+def test_desc_validation(K, N, k, alpha, layout, smooth, code):
+    d = mg.mg_plan_desc(K, N, k, layout, smooth, 0, alpha)
+    out = (ctypes.c_size_t * 8)()
+    assert mg.lib().mg_plan_bytes(ctypes.byref(d), out) == code
+    assert mg.lib().mg_last_error()
+
+
+def test_alpha_ignored_without_smoothing():
+    d = mg.make_desc(64, 64, 4, 0.0, "1x32", smooth=False)
+    assert mg.mg_plan_bytes(d)[0] == 256
+
+
+def _plan(K=64, N=64, k=4, **over):
+    d = mg.make_desc(K, N, k, 0.5)
+    p = mg.mg_plan(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE)
+    for n, v in over.items():
+        setattr(p, n, v)
+    return p
+
+
+def test_pointer_validation():
+    L = mg.lib()
+    # null and misaligned pointers
+    assert L.mg_calib_act(None, 1, 8, 64, FAKE, None) == -1
+    assert L.mg_calib_act(FAKE + 2, 1, 8, 64, FAKE, None) == -4
+    assert L.mg_calib_act(FAKE, 7, 8, 64, FAKE, None) == -3
+    assert L.mg_calib_act(FAKE, 1, -1, 64, FAKE, None) == -2
+    assert L.mg_calib_act(FAKE, 1, 8, 60, FAKE, None) == -2
+    assert L.mg_weight_range(FAKE, 1, 0, 64, FAKE, None) == -2
+    assert L.mg_calib_reset(None, 64, None) == -1
+    p = _plan(s=None)
+    assert L.mg_smooth_scales(ctypes.byref(p), FAKE, FAKE, None) == -1
+    p = _plan(Wq=FAKE + 8)
+    assert L.mg_fold_pack(ctypes.byref(p), FAKE, 1, None) == -4
+    p = _plan(WO=None)
+    assert L.mg_fold_pack(ctypes.byref(p), FAKE, 1, None) == -1
+    p = _plan()
+    a = mg.mg_act(FAKE, FAKE, None)                 # XO missing while k > 0
+    assert L.mg_quantize_act(ctypes.byref(p), FAKE, 1, 16, ctypes.byref(a), None) == -1
+    assert L.mg_dual_gemm(ctypes.byref(p), ctypes.byref(a), 16, FAKE, 1, None) == -1
+    a = mg.mg_act(FAKE, FAKE, FAKE)
+    assert L.mg_forward(ctypes.byref(p), FAKE, 1, 16, ctypes.byref(a), None, 1, None) == -1
+    assert L.mg_dual_gemm(ctypes.byref(p), ctypes.byref(a), 16, FAKE, 9, None) == -3
+    assert L.mg_quantize_act(ctypes.byref(p), FAKE, 5, 16, ctypes.byref(a), None) == -3
+    assert L.mg_gelu_tanh_bf16(FAKE, FAKE, -5, None) == -2
+    assert L.mg_gelu_tanh_bf16(None, FAKE, 5, None) == -1
+    assert b"null" in L.mg_last_error()
+    # k == 0 allows null O / WO / XO: validation passes and only the GPU work would remain,
+    # so check it through a descriptor-level query instead
+    d = mg.make_desc(64, 64, 0, 0.5)
+    assert mg.mg_act_bytes(d, 5)[2] == 0
+
+
+def test_tile_layout_needs_wst():
+    L = mg.lib()
+    d = mg.make_desc(64, 64, 4, 0.5, "32x32")
+    p = mg.mg_plan(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE)
+    assert L.mg_fold_pack(ctypes.byref(p), FAKE, 1, None) == -1
