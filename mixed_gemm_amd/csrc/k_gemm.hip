@@ -15,6 +15,8 @@
 //   B (src1): lane l holds column l%32 and the same K range;
 //   E8M0 scale of lane l: the 32-block of its K range, byte 0 of the operand;
 //   D: lane l, register r holds row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+#include <stdlib.h>
+
 #include "mg_device.h"
 #include "mg_internal.h"
 
@@ -99,6 +101,385 @@ __global__ void __launch_bounds__(256) dual_gemm_simple(const uint8_t* __restric
     }
 }
 
+// ---------------------------------------------------------------------------
+// Tiled kernel.  Workgroup = 4 waves computes a 256x256 tile of Y; each wave
+// owns a 128x128 quarter = 4x4 MFMA tiles of 32x32 (256 fp32 accumulators per
+// lane, held in the accumulation registers).
+//
+// The K dimension is walked in stages that each move 128 bytes per tile row
+// into LDS: a bulk stage carries 256 FP4 values (128 B) of Aq / Wq, an outlier
+// stage carries 64 bf16 values (128 B) of XO / WO.  Both kinds use the same LDS
+// layout and the same fragment addressing -- sub-step ss of a stage reads
+// bytes [32 ss + 16 h, 32 ss + 16 h + 16) of a row for lane half h -- which is
+// 64 FP4 (one scaled FP4 MFMA) or 16 bf16 (one BF16 MFMA).  Bulk stages come
+// first, outlier stages follow, all accumulating into the same registers.
+//
+// Pipeline: double-buffered LDS (2 x 64 KB); the global loads of stage s+1 are
+// issued into registers before the MFMAs of stage s and written to the other
+// LDS buffer after them; one barrier per stage.  LDS rows are 128 B; the eight
+// 16-byte chunks of row r are stored XOR-swizzled (chunk ^ (r & 7)) so the 32
+// rows read by one fragment load spread over the banks.
+//
+// Loads use buffer descriptors sized to each operand: rows past M (or N) and
+// chunks past K / k are given an out-of-range offset and read as zeros.
+// Tiles are ordered so that each XCD (workgroups are dealt round-robin to the
+// 8 XCDs) works on a contiguous run of tiles, grouped 8 row-tiles at a time,
+// which keeps the operand panels of concurrently running tiles in its L2.
+// ---------------------------------------------------------------------------
+
+constexpr int TBM = 256, TBN = 256;
+constexpr int ROWB = 128;                         // bytes per tile row per stage
+constexpr int TILE_BYTES = TBM * ROWB;            // 32 KB
+constexpr int STAGE_BYTES = 2 * TILE_BYTES;       // A + B
+constexpr int GEMM_LDS_BYTES = 2 * STAGE_BYTES;   // double buffer: 128 KB
+constexpr uint32_t OOB = 0xC0000000u;             // offset that reads as zero
+constexpr int NXCD = 8;
+constexpr int GROUP_M = 8;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint64_t bytes) {
+    const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+template <int OPSEL>
+__device__ __forceinline__ v16f mfma_fp4_op(const u32x4& a, const u32x4& b, uint32_t sa, uint32_t sb, v16f c) {
+    v8i av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+    v8i bv = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, OPSEL, (int)sa, OPSEL, (int)sb);
+}
+
+__device__ __forceinline__ v16f mfma_bf16_v(const u32x4& a, const u32x4& b, v16f c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c,
+                                                   0, 0, 0);
+}
+
+struct GemmArgs {
+    const uint8_t* Aq;
+    const uint8_t* As;
+    const uint16_t* XO;
+    const uint8_t* Wq;
+    const uint8_t* Ws;
+    const uint16_t* WO;
+    void* Y;
+    int64_t M;
+    int32_t N, K, k;
+    int32_t MT, NT;     // tile counts
+};
+
+// K8: k % 8 == 0 (outlier rows are whole 16-byte chunks); NB8: (K/32) % 8 == 0
+// (each stage's 8 scale bytes of a row are one aligned 8-byte word).
+template <typename OutT, bool K8, bool NB8>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+dual_gemm_tiled(GemmArgs g) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
+    const int wm = wave >> 1, wn = wave & 1;
+    const int h = lane >> 5;
+    const int l32 = lane & 31;
+
+    // ---- tile index: XCD-contiguous runs, grouped row-major inside
+    const int T = g.MT * g.NT;
+    const int per = (T + NXCD - 1) / NXCD;
+    const int t = (int)(blockIdx.x % NXCD) * per + (int)(blockIdx.x / NXCD);
+    if (t >= T) return;
+    const int grp = t / (GROUP_M * g.NT);
+    const int gsz = min(GROUP_M, g.MT - grp * GROUP_M);
+    const int rin = t - grp * GROUP_M * g.NT;
+    const int tm = grp * GROUP_M + rin % gsz;
+    const int tn = rin / gsz;
+    const int64_t m0 = (int64_t)tm * TBM;
+    const int n0 = tn * TBN;
+
+    const int K = g.K, k = g.k, N = g.N;
+    const int64_t M = g.M;
+    const uint32_t rowA = (uint32_t)(K / 2);       // bytes per Aq / Wq row
+    const int nb = K / 32;
+    const int S4 = (K / 2 + ROWB - 1) / ROWB;      // bulk stages
+    const int S16 = (2 * k + ROWB - 1) / ROWB;     // outlier stages
+    const int S = S4 + S16;
+
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.Aq, (uint64_t)M * rowA);
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(g.Wq, (uint64_t)N * rowA);
+    const __amdgpu_buffer_rsrc_t rAs = make_rsrc(g.As, (uint64_t)M * nb);
+    const __amdgpu_buffer_rsrc_t rBs = make_rsrc(g.Ws, (uint64_t)N * nb);
+    const __amdgpu_buffer_rsrc_t rXO = make_rsrc(g.XO, (uint64_t)M * k * 2);
+    const __amdgpu_buffer_rsrc_t rWO = make_rsrc(g.WO, (uint64_t)N * k * 2);
+
+    // ---- global -> LDS copies.  Each load instruction of a wave moves 8 tile
+    // rows x 128 B = 1 KB straight into LDS, lane L landing at byte 16 L, i.e.
+    // row L/8, physical chunk L%8; that slot holds logical chunk
+    // (L%8) ^ (row & 7), so the lane reads that chunk from global memory.
+    // Wave w copies rows [64 w, 64 w + 64) of the A and of the B tile.
+    const int lrow = lane >> 3;
+    const uint32_t c16 = (uint32_t)((((lane & 7) ^ lrow)) << 4);
+    const int64_t ra0 = m0 + wave * 64 + lrow;          // + 8 gi
+    const int64_t rb0 = (int64_t)n0 + wave * 64 + lrow;
+    // rows past M / N fall beyond the descriptor's range and read as zero
+    const uint32_t vA = (uint32_t)(ra0 * rowA) + c16;
+    const uint32_t vB = (uint32_t)(rb0 * rowA) + c16;
+    const uint32_t vXA = (uint32_t)(ra0 * k * 2) + c16;
+    const uint32_t vXB = (uint32_t)(rb0 * k * 2) + c16;
+    const uint32_t lds_w = (uint32_t)(wave * 64 * ROWB);
+
+    // ---- fragment read offsets (within a stage buffer)
+    uint32_t fa[4], fb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        fa[i] = (uint32_t)((wm * 128 + i * 32 + l32) * ROWB);
+        fb[i] = (uint32_t)(TILE_BYTES + (wn * 128 + i * 32 + l32) * ROWB);
+    }
+    const int sw = l32 & 7;   // row & 7 of every fragment row of this lane
+
+    // ---- scale slots: rows of this lane's 4 A row-tiles and 4 B column-tiles
+    uint32_t offAs[4], offBs[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t ra = m0 + wm * 128 + i * 32 + l32;
+        const int64_t rb = (int64_t)n0 + wn * 128 + i * 32 + l32;
+        offAs[i] = ra < M ? (uint32_t)(ra * nb) : OOB;
+        offBs[i] = rb < N ? (uint32_t)(rb * nb) : OOB;
+    }
+
+    v16f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+
+    uint32_t scA[4][2], scB[4][2], nA[4][2], nB[4][2];
+
+    auto load_scales = [&](int st) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (NB8) {
+                const uint32_t sof = __builtin_amdgcn_readfirstlane((uint32_t)st * 8);
+                const u32x2 va = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rAs, offAs[i], sof, 0));
+                const u32x2 vb = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rBs, offBs[i], sof, 0));
+                nA[i][0] = va[0]; nA[i][1] = va[1];
+                nB[i][0] = vb[0]; nB[i][1] = vb[1];
+            } else {
+                uint32_t wa[2] = {0, 0}, wb[2] = {0, 0};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const bool ok = st * 8 + e < nb;
+                    const uint32_t ba = ok ? __builtin_amdgcn_raw_buffer_load_b8(rAs, offAs[i], (uint32_t)(st * 8 + e), 0) : 0u;
+                    const uint32_t bb = ok ? __builtin_amdgcn_raw_buffer_load_b8(rBs, offBs[i], (uint32_t)(st * 8 + e), 0) : 0u;
+                    wa[e >> 2] |= (ba & 0xFFu) << (8 * (e & 3));
+                    wb[e >> 2] |= (bb & 0xFFu) << (8 * (e & 3));
+                }
+                nA[i][0] = wa[0]; nA[i][1] = wa[1];
+                nB[i][0] = wb[0]; nB[i][1] = wb[1];
+            }
+        }
+    };
+
+    // Stage st of the A and B tiles into LDS buffer `buf` (asynchronous; the
+    // caller waits with vmcnt(0) before the barrier that publishes it).
+    auto load_stage = [&](int st, int buf) {
+        uint8_t* base = lds + buf * STAGE_BYTES + lds_w;
+        if (st < S4) {
+            const uint32_t so = (uint32_t)st * ROWB;
+            const bool ok = (int)(so + c16) < (int)rowA;     // chunk inside K
+            const uint32_t va = ok ? vA : OOB, vb = ok ? vB : OOB;
+#pragma unroll
+            for (int gi = 0; gi < 8; ++gi) {
+                const uint32_t sof = __builtin_amdgcn_readfirstlane(so + (uint32_t)gi * 8 * rowA);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(base + gi * 8 * ROWB), 16, va, sof, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr_t)(base + TILE_BYTES + gi * 8 * ROWB), 16, vb,
+                                                         sof, 0, 0);
+            }
+            load_scales(st);
+        } else {
+            const int u = st - S4;
+            const uint32_t so = (uint32_t)u * ROWB;
+            const uint32_t rowX = (uint32_t)(2 * k);
+            if constexpr (K8) {
+                const bool ok = (int)(so + c16) < (int)rowX;
+                const uint32_t va = ok ? vXA : OOB, vb = ok ? vXB : OOB;
+#pragma unroll
+                for (int gi = 0; gi < 8; ++gi) {
+                    const uint32_t sof = __builtin_amdgcn_readfirstlane(so + (uint32_t)gi * 8 * rowX);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rXO, (lds_ptr_t)(base + gi * 8 * ROWB), 16, va, sof, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rWO, (lds_ptr_t)(base + TILE_BYTES + gi * 8 * ROWB), 16,
+                                                             vb, sof, 0, 0);
+                }
+            } else {
+                // k % 8 != 0: outlier rows are not 16-byte aligned; gather the
+                // bf16 values one by one and store the chunk through registers.
+                const int cl = (int)(c16 >> 4);
+#pragma unroll
+                for (int gi = 0; gi < 8; ++gi) {
+                    const int64_t ra = ra0 + 8 * gi, rb = rb0 + 8 * gi;
+                    uint32_t wa[4], wb[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        uint32_t xa = 0, xb = 0;
+#pragma unroll
+                        for (int q = 0; q < 2; ++q) {
+                            const int col = u * 64 + cl * 8 + 2 * e + q;
+                            const uint32_t ea = (col < k && ra < M)
+                                ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rXO, (uint32_t)((ra * k + col) * 2), 0, 0) : 0u;
+                            const uint32_t eb = (col < k && rb < N)
+                                ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rWO, (uint32_t)((rb * k + col) * 2), 0, 0) : 0u;
+                            xa |= (ea & 0xFFFFu) << (16 * q);
+                            xb |= (eb & 0xFFFFu) << (16 * q);
+                        }
+                        wa[e] = xa; wb[e] = xb;
+                    }
+                    *reinterpret_cast<u32x4*>(base + gi * 8 * ROWB + lane * 16) = u32x4{wa[0], wa[1], wa[2], wa[3]};
+                    *reinterpret_cast<u32x4*>(base + TILE_BYTES + gi * 8 * ROWB + lane * 16) = u32x4{wb[0], wb[1], wb[2], wb[3]};
+                }
+            }
+        }
+    };
+
+    auto take_scales = [&]() {
+        // lane half h uses the odd scale bytes: shift them down so sub-step ss
+        // finds its byte at position 2*(ss&1) of word ss>>1.
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            scA[i][0] = h ? nA[i][0] >> 8 : nA[i][0];
+            scA[i][1] = h ? nA[i][1] >> 8 : nA[i][1];
+            scB[i][0] = h ? nB[i][0] >> 8 : nB[i][0];
+            scB[i][1] = h ? nB[i][1] >> 8 : nB[i][1];
+        }
+    };
+
+    auto fetch = [&](const uint8_t* base, int ss, u32x4 (&fA)[4], u32x4 (&fB)[4]) {
+        const uint32_t co = (uint32_t)(((2 * ss + h) ^ sw) << 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            fA[i] = *reinterpret_cast<const u32x4*>(base + fa[i] + co);
+            fB[i] = *reinterpret_cast<const u32x4*>(base + fb[i] + co);
+        }
+    };
+
+    auto bulk_compute = [&](const uint8_t* base) {
+#pragma unroll
+        for (int ss = 0; ss < 4; ++ss) {
+            u32x4 fA[4], fB[4];
+            fetch(base, ss, fA, fB);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if ((ss & 1) == 0)
+                        acc[i][j] = mfma_fp4_op<0>(fA[i], fB[j], scA[i][ss >> 1], scB[j][ss >> 1], acc[i][j]);
+                    else
+                        acc[i][j] = mfma_fp4_op<2>(fA[i], fB[j], scA[i][ss >> 1], scB[j][ss >> 1], acc[i][j]);
+                }
+        }
+    };
+    auto outlier_compute = [&](const uint8_t* base) {
+#pragma unroll
+        for (int ss = 0; ss < 4; ++ss) {
+            u32x4 fA[4], fB[4];
+            fetch(base, ss, fA, fB);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16_v(fA[i], fB[j], acc[i][j]);
+        }
+    };
+    // Wait for this wave's copies of the next stage, then for every wave.  The
+    // scheduling barrier keeps the MFMAs of the current stage above it, so they
+    // are issued (and run) while the copies are still in flight.
+    auto stage_sync = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
+
+    load_stage(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    take_scales();
+    __syncthreads();
+
+    // bulk: FP4 x FP4 with E8M0 block scales; the loop body is one basic block
+    for (int st = 0; st + 1 < S4; ++st) {
+        load_stage(st + 1, (st + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);        // all copies issued before the MFMAs
+        bulk_compute(lds + (st & 1) * STAGE_BYTES);
+        stage_sync();
+        take_scales();
+    }
+    if (S16 > 0) load_stage(S4, S4 & 1);
+    bulk_compute(lds + ((S4 - 1) & 1) * STAGE_BYTES);
+    stage_sync();
+    // outliers: BF16 x BF16 into the same accumulators
+    for (int st = S4; st < S; ++st) {
+        if (st + 1 < S) load_stage(st + 1, (st + 1) & 1);
+        outlier_compute(lds + (st & 1) * STAGE_BYTES);
+        stage_sync();
+    }
+
+    // ---- epilogue: fp32 accumulators -> Y.  Lane (l32, h) of tile (i, j)
+    // register r holds row 32 i + 8 (r/4) + 4 h + r%4, column 32 j + l32.
+    OutT* Y = static_cast<OutT*>(g.Y) + (m0 + wm * 128 + 4 * h) * (int64_t)N + n0 + wn * 128 + l32;
+    const bool full = m0 + TBM <= M && n0 + TBN <= N;
+    const int64_t rowlim = M - (m0 + wm * 128 + 4 * h);       // rows available from Y
+    const int collim = N - (n0 + wn * 128 + l32);
+    if (full) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                OutT* yr = Y + (int64_t)(32 * i + 8 * (r >> 2) + (r & 3)) * N;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) store_out(yr + 32 * j, acc[i][j][r]);
+            }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int dr = 32 * i + 8 * (r >> 2) + (r & 3);
+                if (dr >= rowlim) continue;
+                OutT* yr = Y + (int64_t)dr * N;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (32 * j < collim) store_out(yr + 32 * j, acc[i][j][r]);
+            }
+    }
+}
+
+template <typename OutT, bool K8, bool NB8>
+static hipError_t launch_tiled(const GemmArgs& a, hipStream_t st) {
+    static thread_local int configured_dev = -1;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorNoDevice;
+    if (configured_dev != dev) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dual_gemm_tiled<OutT, K8, NB8>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_LDS_BYTES);
+        if (e != hipSuccess) return e;
+        configured_dev = dev;
+    }
+    const int T = a.MT * a.NT;
+    const int per = (T + NXCD - 1) / NXCD;
+    hipLaunchKernelGGL((dual_gemm_tiled<OutT, K8, NB8>), dim3((unsigned)(per * NXCD)), dim3(256), GEMM_LDS_BYTES, st, a);
+    return hipGetLastError();
+}
+
+template <typename OutT>
+static hipError_t launch_tiled_t(const GemmArgs& a, hipStream_t st) {
+    const bool k8 = a.k % 8 == 0;
+    const bool nb8 = (a.K / 32) % 8 == 0;
+    if (k8 && nb8) return launch_tiled<OutT, true, true>(a, st);
+    if (k8) return launch_tiled<OutT, true, false>(a, st);
+    if (nb8) return launch_tiled<OutT, false, true>(a, st);
+    return launch_tiled<OutT, false, false>(a, st);
+}
+
 }  // namespace
 
 hipError_t launch_dual_gemm(const uint8_t* Aq, const uint8_t* As, const uint16_t* XO,
@@ -106,14 +487,19 @@ hipError_t launch_dual_gemm(const uint8_t* Aq, const uint8_t* As, const uint16_t
                             int32_t N, int32_t K, int32_t k, void* Y, int32_t y_dtype,
                             hipStream_t st) {
     if (M <= 0) return hipSuccess;
-    dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
-    if (y_dtype == MG_BF16)
-        hipLaunchKernelGGL(dual_gemm_simple<uint16_t>, grid, dim3(256), 0, st, Aq, As, XO, Wq, Ws, WO, M, N, K, k,
-                           static_cast<uint16_t*>(Y));
-    else
-        hipLaunchKernelGGL(dual_gemm_simple<float>, grid, dim3(256), 0, st, Aq, As, XO, Wq, Ws, WO, M, N, K, k,
-                           static_cast<float*>(Y));
-    return hipGetLastError();
+    static const char* impl = getenv("MG_GEMM_IMPL");
+    if (impl && impl[0] == 's') {   // the straightforward kernel (cross-checks)
+        dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
+        if (y_dtype == MG_BF16)
+            hipLaunchKernelGGL(dual_gemm_simple<uint16_t>, grid, dim3(256), 0, st, Aq, As, XO, Wq, Ws, WO, M, N, K,
+                               k, static_cast<uint16_t*>(Y));
+        else
+            hipLaunchKernelGGL(dual_gemm_simple<float>, grid, dim3(256), 0, st, Aq, As, XO, Wq, Ws, WO, M, N, K, k,
+                               static_cast<float*>(Y));
+        return hipGetLastError();
+    }
+    GemmArgs a{Aq, As, XO, Wq, Ws, WO, Y, M, N, K, k, (int32_t)((M + TBM - 1) / TBM), (N + TBN - 1) / TBN};
+    return y_dtype == MG_BF16 ? launch_tiled_t<uint16_t>(a, st) : launch_tiled_t<float>(a, st);
 }
 
 }  // namespace mg
