@@ -71,6 +71,16 @@ int check_plan(const mg_plan* p, bool need_w) {
     return MG_OK;
 }
 
+// The GEMM addresses each operand with 32-bit offsets below 3 GiB.
+int check_gemm_size(const mg_plan* p, int64_t M) {
+    const uint64_t lim = 0xC0000000ull;
+    const uint64_t K = (uint64_t)p->d.K, N = (uint64_t)p->d.N, k = (uint64_t)p->d.k;
+    if ((uint64_t)M * K / 2 >= lim || N * K / 2 >= lim || (uint64_t)M * 2 * k >= lim || N * 2 * k >= lim)
+        return fail(MG_ERR_UNSUPPORTED, "operands of M=%lld, N=%d, K=%d, k=%d exceed 3 GiB", (long long)M, p->d.N,
+                    p->d.K, p->d.k);
+    return MG_OK;
+}
+
 int check_act(const mg_plan* p, const mg_act* a) {
     if (!a) return fail(MG_ERR_ARG, "null activation workspace");
     MG_CHECK_PTR(a->Aq, "act.Aq");
@@ -218,6 +228,7 @@ int mg_dual_gemm(const mg_plan* p, const mg_act* a, int64_t M, void* Y, int32_t 
     if (M < 0) return fail(MG_ERR_SHAPE, "M=%lld must be >= 0", (long long)M);
     if (M == 0) return MG_OK;
     if (int e = check_act(p, a)) return e;
+    if (int e = check_gemm_size(p, M)) return e;
     MG_CHECK_PTR(Y, "Y");
     hipError_t h = mg::launch_dual_gemm(a->Aq, a->As, a->XO, p->Wq, p->Ws, p->WO, M, p->d.N, p->d.K, p->d.k, Y,
                                         y_dtype, stream);
