@@ -365,9 +365,10 @@ dual_gemm_tiled(GemmArgs g) {
         }
     };
 
-    // Two one-lane-per-row loads that bring the 128-byte rows of a future
-    // stage into L2 (4 bytes per lane land in a scratch area of LDS).  Always
-    // exactly two instructions, so the stage wait can leave them in flight.
+    // One-lane-per-row loads that bring both 64-byte halves of the 128-byte
+    // rows of a future stage into L2 (4 bytes per lane land in a scratch area
+    // of LDS).  Always exactly NTOUCH instructions, so the stage wait can
+    // leave them in flight.
     auto touch = [&](const TileOrg* o, int st) {
         uint8_t* junk = lds + JUNK_OFF + wave * 256;
         uint32_t va = OOB, vb = OOB, so = 0;
@@ -383,8 +384,11 @@ dual_gemm_tiled(GemmArgs g) {
             ra = rXO; rb = rWO;
         }
         so = __builtin_amdgcn_readfirstlane(so);
+        const uint32_t so2 = __builtin_amdgcn_readfirstlane(so + 64);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)junk, 4, va, so, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)junk, 4, vb, so, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)junk, 4, va, so2, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)junk, 4, vb, so2, 0, 0);
     };
 
     auto take_scales = [&]() {
@@ -460,7 +464,7 @@ dual_gemm_tiled(GemmArgs g) {
         }
         interleave_schedule();
     };
-    // Wait for this wave's copies of the next stage (everything but the two
+    // Wait for this wave's copies of the next stage (everything but the four
     // L2 touches), then for every wave.  The scheduling barrier keeps the
     // MFMAs of the current stage above it, so they run while copies fly.
     // (__syncthreads would add a release fence, i.e. wait for every
@@ -468,7 +472,7 @@ dual_gemm_tiled(GemmArgs g) {
     // the previous tile; only this wave's copies matter here.)
     auto stage_sync = [&]() {
         __builtin_amdgcn_sched_barrier(0);
-        asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -566,7 +570,7 @@ dual_gemm_tiled(GemmArgs g) {
     else if (tn < t_end) { const TileOrg nx = tile_org(tn); touch(&nx, 0); }
     else touch(nullptr, 0);
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     take_scales();
     __syncthreads();
     int buf = 0;
