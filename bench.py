@@ -75,6 +75,50 @@ def cpu_baseline(w, X, W, rows: int) -> dict:
                       f"per-row work {t_rows:.1f} s scaled x{w.M / rows:.0f}); est. full step {t_full:.0f} s"}
 
 
+COPY_BYTES = 256 << 20            # plain copy used to calibrate the HBM byte counters
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, out_json: str) -> dict:
+    """HBM bytes per dual-GEMM launch from two rocprofv3 --pmc runs of this
+    script with --copy-calibration (FETCH_SIZE, then WRITE_SIZE, in KiB per
+    dispatch).  Each counter is scaled by what it reads for the plain copy of
+    COPY_BYTES (read COPY_BYTES, write COPY_BYTES) in the same run."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            vals.setdefault(name, {}).setdefault(r["Dispatch_Id"], 0.0)
+            vals[name][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        return {k: sorted(v.values()) for k, v in vals.items()}
+
+    def pick(d, pred):
+        ks = [k for k in d if pred(k)]
+        assert ks, "kernel not found in counter file"
+        vals = [v for k in ks for v in d[k]]
+        return sorted(vals)[len(vals) // 2]          # median dispatch
+
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w = per_kernel(write_csv, "WRITE_SIZE")
+    is_gemm = lambda k: "dual_gemm_tiled" in k
+    is_copy = lambda k: "copyBuffer" in k      # the runtime's device-to-device copy kernel
+    fetch_kib, write_kib = pick(f, is_gemm), pick(w, is_gemm)
+    copy_fetch_kib, copy_write_kib = pick(f, is_copy), pick(w, is_copy)
+    fetch_scale = COPY_BYTES / (copy_fetch_kib * 1024)
+    write_scale = COPY_BYTES / (copy_write_kib * 1024)
+    res = {"kernel": "dual_gemm_tiled (bf16 output)", "workload": "ffn0_480p_32760x5120x13824",
+           "fetch_kib": fetch_kib, "write_kib": write_kib,
+           "copy_fetch_kib": copy_fetch_kib, "copy_write_kib": copy_write_kib,
+           "fetch_scale": fetch_scale, "write_scale": write_scale,
+           "bytes_per_launch": fetch_kib * 1024 * fetch_scale + write_kib * 1024 * write_scale,
+           "kernel_source_sha256_16": gemm_source_hash()}
+    json.dump(res, open(out_json, "w"), indent=1)
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -83,7 +127,14 @@ def main() -> int:
     ap.add_argument("--workload", default="ffn0_480p_32760x5120x13824")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, run a plain device copy of 256 MiB (HBM counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the dual-GEMM traffic summary from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        print(json.dumps(summarize_pmc(*args.summarize_pmc, TRAFFIC_FILE)))
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the layer shards along tokens with no exchange in the forward pass)", file=sys.stderr)
@@ -183,6 +234,12 @@ def main() -> int:
         "quant_pct_hbm": round(100 * quant_bytes / (ms["quant"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
         "calib_gbs": round(calib_bytes / (ms["calib"] * 1e-3) / 1e9, 1),
     }
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, X_h, W_h, args.cpu_rows)
     print(json.dumps(out), flush=True)

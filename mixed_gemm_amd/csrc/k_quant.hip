@@ -62,6 +62,11 @@ __global__ void __launch_bounds__(256) quant_kernel(const void* __restrict__ X, 
         omask |= (p >= 0 ? 1u : 0u) << i;
         s_ok &= div_fast_ok_s(sv[i]);
     }
+    // The first outlier channel of the lane (if any) is written with one store
+    // per row; further outlier channels of the same lane (rare) take a loop.
+    const int oc0 = omask ? __builtin_ctz(omask) : 8;
+    const int64_t op0 = oc0 < 8 ? (int64_t)pos[j0 + oc0] : 0;
+    const uint32_t omask_rest = omask & (omask - 1);
     const int64_t rstride = (int64_t)gridDim.y * kWaves;
     const int64_t ld = K;                                     // row stride of X in elements
     for (int64_t r0 = (int64_t)blockIdx.y * kWaves + wave; r0 < M; r0 += rstride * RPI) {
@@ -109,9 +114,17 @@ __global__ void __launch_bounds__(256) quant_kernel(const void* __restrict__ X, 
                 for (int i = 0; i < 8; ++i) q[i] = __fdiv_rn(xin[u][i], sv[i]);
             }
             if (omask) {
+                float qo = q[0];
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    if (omask & (1u << i)) XO[r * k + (int64_t)pos[j0 + i]] = (uint16_t)f32_to_bf16_rne(q[i]);
+                for (int i = 1; i < 8; ++i) qo = oc0 == i ? q[i] : qo;
+                XO[r * k + op0] = (uint16_t)f32_to_bf16_rne(qo);
+                for (uint32_t m = omask_rest; m; m &= m - 1) {
+                    const int i = __builtin_ctz(m);
+                    float qi = q[0];
+#pragma unroll
+                    for (int t = 1; t < 8; ++t) qi = i == t ? q[t] : qi;
+                    XO[r * k + pos[j0 + i]] = (uint16_t)f32_to_bf16_rne(qi);
+                }
             }
             float amax = 0.0f;
 #pragma unroll
@@ -122,12 +135,11 @@ __global__ void __launch_bounds__(256) quant_kernel(const void* __restrict__ X, 
             amax = quad_max(amax);
             const uint32_t c = e8m0_from_amax_bits(__float_as_uint(amax));
             const float scale = e8m0_to_f32(c);
-            uint32_t b0 = 0, b1 = 0, b2 = 0, b3 = 0;
-            MG_CVT_FP4X2(b0, q[0], q[1], scale, 0);
-            MG_CVT_FP4X2(b1, q[2], q[3], scale, 0);
-            MG_CVT_FP4X2(b2, q[4], q[5], scale, 0);
-            MG_CVT_FP4X2(b3, q[6], q[7], scale, 0);
-            const uint32_t word = (b0 & 0xFFu) | ((b1 & 0xFFu) << 8) | ((b2 & 0xFFu) << 16) | (b3 << 24);
+            uint32_t word = 0;
+            MG_CVT_FP4X2(word, q[0], q[1], scale, 0);
+            MG_CVT_FP4X2(word, q[2], q[3], scale, 1);
+            MG_CVT_FP4X2(word, q[4], q[5], scale, 2);
+            MG_CVT_FP4X2(word, q[6], q[7], scale, 3);
             if (valid) {
                 *reinterpret_cast<uint32_t*>(Aq + r * (K / 2) + j0 / 2) = word;
                 if ((lane & 3) == 0) As[r * (K / 32) + j0 / 32] = (uint8_t)c;

@@ -73,7 +73,8 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t c) {
 
 // Hardware E2M1 encode of two f32 values divided by an f32 power-of-two scale
 // (v_cvt_scalef32_pk_fp4_f32: nearest, ties to even, saturating, sign kept),
-// written into byte `sel` of `word`.  Checked against the threshold encoder
+// written into byte `sel` of `word` (first value in the low nibble); the
+// other bytes of `word` are kept.  Checked against the threshold encoder
 // e2m1_nibble over every f32 bit pattern at scales 2^-127 .. 2^127.
 #define MG_CVT_FP4X2(word, a, b, scale, sel) \
     (word) = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((word), (a), (b), (scale), (sel))
