@@ -17,6 +17,9 @@
 //   D: lane l, register r holds row 8*(r/4) + 4*(l/32) + r%4, column l%32.
 #include <stdlib.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "mg_device.h"
 #include "mg_internal.h"
 
@@ -115,14 +118,26 @@ __global__ void __launch_bounds__(256) dual_gemm_simple(const uint8_t* __restric
 // 64 FP4 (one scaled FP4 MFMA) or 16 bf16 (one BF16 MFMA).  Bulk stages come
 // first, outlier stages follow, all accumulating into the same registers.
 //
+// E8M0 scales.  A bulk stage needs 8 scale bytes per tile row.  They are not
+// fetched per lane (one cache line per row, per wave, per stage): the 16 bytes
+// of two consecutive bulk stages ("a window") of all 512 tile rows are copied
+// into LDS with one 16-byte load per row, next to the operand copies, and
+// each wave reads its rows' 8 bytes from there.  Windows alternate between two
+// LDS slots.
+//
 // Pipeline.  The stages of all of a workgroup's tiles form one sequence over
 // two LDS buffers (2 x 64 KB).  While stage g is multiplied out of one buffer,
 // the copies of stage g+1 (which may be the first stage of the next tile) run
-// straight from global memory into the other buffer, and two one-lane-per-row
-// loads touch the rows of stage g+2 so they are in L2 when their copies are
-// issued.  One barrier per stage.  After a tile's last stage its 256x256 bf16
-// result is staged through the freed buffer and written as whole 512-byte rows
-// while the next tile's first stage already sits in LDS.
+// straight from global memory into the other buffer.  One barrier per stage.
+// In the steady state (a bulk stage followed by bulk stages of the same tile)
+// the instruction order of a stage is fixed slot by slot: each of its 64 MFMAs
+// is followed by at most one fragment read, scale read or copy, so memory
+// instructions never hold up a run of MFMAs, and sub-step 3 -- whose
+// fragments are read before the barrier -- is multiplied after it, so the
+// matrix cores stay busy while the next stage's first fragments are read.
+// After a tile's last stage its 256x256 bf16 result is staged through the
+// freed buffer and written as whole 512-byte rows while the next tile's first
+// stage already sits in LDS.
 //
 // LDS rows are 128 B; logical 16-byte chunk c of tile row r is stored at
 // physical chunk c ^ ((r >> 1) & 7), which spreads the 16 rows a fragment load
@@ -137,8 +152,10 @@ constexpr int TBM = 256, TBN = 256;
 constexpr int ROWB = 128;                         // bytes per tile row per stage
 constexpr int TILE_BYTES = TBM * ROWB;            // 32 KB
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;       // A + B
-constexpr int JUNK_OFF = 2 * STAGE_BYTES;         // landing area of the L2 touches
-constexpr int GEMM_LDS_BYTES = 2 * STAGE_BYTES + 1024;
+constexpr int SCW_ROWB = 16;                      // scale bytes per row per window (two bulk stages)
+constexpr int SCW_BYTES = (TBM + TBN) * SCW_ROWB; // one window slot: A rows then B rows (8 KB)
+constexpr int SCW_OFF = 2 * STAGE_BYTES;
+constexpr int GEMM_LDS_BYTES = 2 * STAGE_BYTES + 2 * SCW_BYTES;
 constexpr uint32_t OOB = 0xC0000000u;             // offset that reads as zero
 constexpr int NXCD = 8;
 constexpr int GROUP_M = 8;
@@ -167,6 +184,16 @@ __device__ __forceinline__ v16f mfma_bf16_v(const u32x4& a, const u32x4& b, v16f
                                                    0, 0, 0);
 }
 
+// f(integral_constant<int, Q>) for Q = 0 .. N-1, expanded at compile time
+template <typename F, int... Qs>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Qs...>) {
+    (f(std::integral_constant<int, Qs>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 struct GemmArgs {
     const uint8_t* Aq;
     const uint8_t* As;
@@ -186,9 +213,9 @@ struct TileOrg {
     int n0;
 };
 
-// K8: k % 8 == 0 (outlier rows are whole 16-byte chunks); NB8: (K/32) % 8 == 0
-// (each stage's 8 scale bytes of a row are one aligned 8-byte word).
-template <typename OutT, bool K8, bool NB8>
+// K8: k % 8 == 0 (outlier rows are whole 16-byte chunks); NB16: (K/32) % 16
+// == 0 (every scale window of a row is one aligned 16-byte chunk).
+template <typename OutT, bool K8, bool NB16>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 dual_gemm_tiled(GemmArgs g) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -238,11 +265,12 @@ dual_gemm_tiled(GemmArgs g) {
     const uint32_t c16o = c16e ^ 64u;                                          // odd groups
     const uint32_t lrA0 = (uint32_t)(wave * 64 + lrow) * rowA;                 // copy row (group 0)
     const uint32_t lrX0 = (uint32_t)(wave * 64 + lrow) * rowX;
-    const uint32_t ltA = (uint32_t)(wave * 64 + lane) * rowA;                  // L2-touch row
-    const uint32_t ltX = (uint32_t)(wave * 64 + lane) * rowX;
-    const uint32_t lsA = (uint32_t)(wm * 128 + l32) * (uint32_t)nb;            // scale rows
-    const uint32_t lsB = (uint32_t)(wn * 128 + l32) * (uint32_t)nb;
     const uint32_t lds_w = (uint32_t)(wave * 64 * ROWB);
+    // scale windows: lane L of wave w copies window row 64 w + L of A and of
+    // B; a lane reads its fragment rows' 8 bytes at these offsets (+ 512 i)
+    const uint32_t lwr = (uint32_t)(wave * 64 + lane);
+    const uint32_t scw_a = (uint32_t)((wm * 128 + l32) * SCW_ROWB);
+    const uint32_t scw_b = (uint32_t)(TBM * SCW_ROWB + (wn * 128 + l32) * SCW_ROWB);
     uint32_t fa[4], fb[4];                        // fragment rows within a stage buffer
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -263,63 +291,104 @@ dual_gemm_tiled(GemmArgs g) {
 
     v16f acc[4][4];
     uint32_t scA[4][2], scB[4][2], nA[4][2], nB[4][2];
+    int wiss = 0;      // scale windows issued so far (slot of the next one: wiss & 1)
+    int wuse = 0;      // scale windows taken into use so far
+    int wcur = 0;      // slot of the window of the current bulk stage
 
-    auto load_scales = [&](const TileOrg& o, int st) {
-        const uint32_t sa0 = __builtin_amdgcn_readfirstlane((uint32_t)o.m0 * (uint32_t)nb);
-        const uint32_t sb0 = __builtin_amdgcn_readfirstlane((uint32_t)o.n0 * (uint32_t)nb);
+    // ---- scale window w (bulk stages 2w, 2w+1) of a tile into the next slot
+    auto load_window = [&](const TileOrg& o, int w) {
+        const int slot = wiss & 1;
+        ++wiss;
+        uint8_t* dst = lds + SCW_OFF + slot * SCW_BYTES + wave * 64 * SCW_ROWB;
+        if constexpr (NB16) {
+            uint32_t r = lwr;
+            asm volatile("" : "+v"(r));
+            const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)w * SCW_ROWB);
+            const uint32_t ra = __builtin_amdgcn_readfirstlane((uint32_t)o.m0);
+            const uint32_t rb = __builtin_amdgcn_readfirstlane((uint32_t)o.n0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rAs, (lds_ptr_t)dst, 16, (ra + r) * (uint32_t)nb, so, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rBs, (lds_ptr_t)(dst + TBM * SCW_ROWB), 16,
+                                                     (rb + r) * (uint32_t)nb, so, 0, 0);
+        } else {
+            // rows not 16-byte aligned: gather the bytes, store through registers
+            const int64_t ra = o.m0 + lwr, rb = (int64_t)o.n0 + lwr;
+            uint32_t wa[4], wb[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t va = lsA + sa0 + (uint32_t)(32 * i * nb);   // rows past M are out of range
-            const uint32_t vb = lsB + sb0 + (uint32_t)(32 * i * nb);
-            if constexpr (NB8) {
-                const uint32_t sof = __builtin_amdgcn_readfirstlane((uint32_t)st * 8);
-                const u32x2 xa = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rAs, va, sof, 0));
-                const u32x2 xb = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rBs, vb, sof, 0));
-                nA[i][0] = xa[0]; nA[i][1] = xa[1];
-                nB[i][0] = xb[0]; nB[i][1] = xb[1];
-            } else {
-                uint32_t wa[2] = {0, 0}, wb[2] = {0, 0};
+            for (int e = 0; e < 4; ++e) {
+                uint32_t xa = 0, xb = 0;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const bool ok = st * 8 + e < nb;
-                    const uint32_t ba = ok ? __builtin_amdgcn_raw_buffer_load_b8(rAs, va + (uint32_t)(st * 8 + e), 0, 0) : 0u;
-                    const uint32_t bb = ok ? __builtin_amdgcn_raw_buffer_load_b8(rBs, vb + (uint32_t)(st * 8 + e), 0, 0) : 0u;
-                    wa[e >> 2] |= (ba & 0xFFu) << (8 * (e & 3));
-                    wb[e >> 2] |= (bb & 0xFFu) << (8 * (e & 3));
+                for (int q = 0; q < 4; ++q) {
+                    const int col = w * SCW_ROWB + 4 * e + q;
+                    const uint32_t ba = (col < nb && ra < M)
+                        ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rAs, (uint32_t)(ra * nb + col), 0, 0) : 0u;
+                    const uint32_t bb = (col < nb && rb < N)
+                        ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rBs, (uint32_t)(rb * nb + col), 0, 0) : 0u;
+                    xa |= (ba & 0xFFu) << (8 * q);
+                    xb |= (bb & 0xFFu) << (8 * q);
                 }
-                nA[i][0] = wa[0]; nA[i][1] = wa[1];
-                nB[i][0] = wb[0]; nB[i][1] = wb[1];
+                wa[e] = xa; wb[e] = xb;
             }
+            *reinterpret_cast<u32x4*>(dst + lane * 16) = u32x4{wa[0], wa[1], wa[2], wa[3]};
+            *reinterpret_cast<u32x4*>(dst + TBM * SCW_ROWB + lane * 16) = u32x4{wb[0], wb[1], wb[2], wb[3]};
         }
     };
 
-    // Copies of stage st of a tile into LDS buffer `buf` (asynchronous).
+    // ---- this lane's scale words of bulk stage st (from its window)
+    auto read_scales_i = [&](const uint8_t* wsc, int q) {
+        if (q < 4) {
+            const u32x2 x = *reinterpret_cast<const u32x2*>(wsc + scw_a + q * 32 * SCW_ROWB);
+            nA[q][0] = x[0]; nA[q][1] = x[1];
+        } else {
+            const u32x2 x = *reinterpret_cast<const u32x2*>(wsc + scw_b + (q - 4) * 32 * SCW_ROWB);
+            nB[q - 4][0] = x[0]; nB[q - 4][1] = x[1];
+        }
+    };
+    auto window_of = [&](int st) -> const uint8_t* {
+        if ((st & 1) == 0) { wcur = wuse & 1; ++wuse; }
+        return lds + SCW_OFF + wcur * SCW_BYTES + (st & 1) * 8;
+    };
+    // lane half h uses the odd scale bytes: shift them down so sub-step ss
+    // finds its byte at position 2*(ss&1) of word ss>>1.
+    const uint32_t sc_shift = (uint32_t)h * 8u;
+    auto take_scales = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            scA[i][0] = nA[i][0] >> sc_shift;
+            scA[i][1] = nA[i][1] >> sc_shift;
+            scB[i][0] = nB[i][0] >> sc_shift;
+            scB[i][1] = nB[i][1] >> sc_shift;
+        }
+    };
+
+    // ---- copies of one 8-row group of bulk stage st of the A (B) tile
+    auto copy_bulk = [&](const TileOrg& o, int st, int b, int part, bool isB) {
+        uint8_t* dst = lds + b * STAGE_BYTES + lds_w + (isB ? TILE_BYTES : 0) + part * 8 * ROWB;
+        uint32_t lr = lrA0;
+        asm volatile("" : "+v"(lr));
+        const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)st * ROWB);
+        const uint32_t r0 = __builtin_amdgcn_readfirstlane((isB ? (uint32_t)o.n0 : (uint32_t)o.m0) * rowA);
+        const uint32_t c = (part & 1) ? c16o : c16e;
+        const bool ok = so + c < rowA;                // chunks past K (only when K % 256 != 0)
+        const uint32_t v = ok ? lr + c + r0 + (uint32_t)part * 8 * rowA : OOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(isB ? rB : rA, (lds_ptr_t)dst, 16, v, so, 0, 0);
+    };
+
+    // Copies of stage st of a tile into LDS buffer `buf` (asynchronous), with
+    // the scale window the stage opens.
     auto load_stage = [&](const TileOrg& o, int st, int buf) {
         uint8_t* base = lds + buf * STAGE_BYTES + lds_w;
-        // opaque per call: the per-group row offsets below are formed here
-        // instead of being hoisted out of the loops and held in registers
-        uint32_t lrA = lrA0, lrX = lrX0;
-        asm volatile("" : "+v"(lrA), "+v"(lrX));
         if (st < S4) {
-            const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)st * ROWB);   // column offset in the row
-            const uint32_t ra = __builtin_amdgcn_readfirstlane((uint32_t)o.m0 * rowA);
-            const uint32_t rb = __builtin_amdgcn_readfirstlane((uint32_t)o.n0 * rowA);
-            // chunks past K (only when K % 256 != 0) read as zero
-            const bool oke = so + c16e < rowA, oko = so + c16o < rowA;
 #pragma unroll
             for (int gi = 0; gi < 8; ++gi) {
-                const uint32_t c = (gi & 1) ? c16o : c16e;
-                const bool ok = (gi & 1) ? oko : oke;
-                const uint32_t va = ok ? lrA + c + ra + (uint32_t)gi * 8 * rowA : OOB;
-                const uint32_t vb = ok ? lrA + c + rb + (uint32_t)gi * 8 * rowA : OOB;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(base + gi * 8 * ROWB), 16, va, so, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr_t)(base + TILE_BYTES + gi * 8 * ROWB), 16, vb,
-                                                         so, 0, 0);
+                copy_bulk(o, st, buf, gi, false);
+                copy_bulk(o, st, buf, gi, true);
             }
-            load_scales(o, st);
+            if ((st & 1) == 0) load_window(o, st >> 1);
         } else {
             const int u = st - S4;
             const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)u * ROWB);
+            uint32_t lrX = lrX0;
+            asm volatile("" : "+v"(lrX));
             if constexpr (K8) {
                 const uint32_t ra = __builtin_amdgcn_readfirstlane((uint32_t)o.m0 * rowX);
                 const uint32_t rb = __builtin_amdgcn_readfirstlane((uint32_t)o.n0 * rowX);
@@ -365,44 +434,7 @@ dual_gemm_tiled(GemmArgs g) {
         }
     };
 
-    // One-lane-per-row loads that bring both 64-byte halves of the 128-byte
-    // rows of a future stage into L2 (4 bytes per lane land in a scratch area
-    // of LDS).  Always exactly NTOUCH instructions, so the stage wait can
-    // leave them in flight.
-    auto touch = [&](const TileOrg* o, int st) {
-        uint8_t* junk = lds + JUNK_OFF + wave * 256;
-        uint32_t va = OOB, vb = OOB, so = 0;
-        __amdgpu_buffer_rsrc_t ra = rA, rb = rB;
-        if (o != nullptr && st < S4) {
-            va = ltA + (uint32_t)o->m0 * rowA;
-            vb = ltA + (uint32_t)o->n0 * rowA;
-            so = (uint32_t)st * ROWB;
-        } else if (o != nullptr && st < S) {
-            va = ltX + (uint32_t)o->m0 * rowX;
-            vb = ltX + (uint32_t)o->n0 * rowX;
-            so = (uint32_t)(st - S4) * ROWB;
-            ra = rXO; rb = rWO;
-        }
-        so = __builtin_amdgcn_readfirstlane(so);
-        const uint32_t so2 = __builtin_amdgcn_readfirstlane(so + 64);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)junk, 4, va, so, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)junk, 4, vb, so, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)junk, 4, va, so2, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)junk, 4, vb, so2, 0, 0);
-    };
-
-    auto take_scales = [&]() {
-        // lane half h uses the odd scale bytes: shift them down so sub-step ss
-        // finds its byte at position 2*(ss&1) of word ss>>1.
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            scA[i][0] = h ? nA[i][0] >> 8 : nA[i][0];
-            scA[i][1] = h ? nA[i][1] >> 8 : nA[i][1];
-            scB[i][0] = h ? nB[i][0] >> 8 : nB[i][0];
-            scB[i][1] = h ? nB[i][1] >> 8 : nB[i][1];
-        }
-    };
-
+    // fragments of sub-step ss: A rows fa[i], B rows fb[i], 16 bytes each
     auto fetch = [&](const uint8_t* base, int ss, u32x4 (&fA)[4], u32x4 (&fB)[4]) {
         const uint32_t co = (uint32_t)(((2 * ss + h) ^ sw) << 4);
 #pragma unroll
@@ -412,9 +444,9 @@ dual_gemm_tiled(GemmArgs g) {
         }
     };
 
-    // Instruction order of one stage: the 8 fragment reads of sub-step 0, then
-    // for each sub-step the reads of the next one threaded between its first 8
-    // MFMAs, so LDS latency hides behind matrix-core work.
+    // Instruction order of a stage outside the steady state: the 8 fragment
+    // reads of sub-step 0, then for each sub-step the reads of the next one
+    // threaded between its first 8 MFMAs.
     auto interleave_schedule = [&]() {
         __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);          // DS reads
 #pragma unroll
@@ -429,9 +461,15 @@ dual_gemm_tiled(GemmArgs g) {
         __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
     };
 
-    // One stage: 4 sub-steps of 16 MFMAs; the fragments of sub-step ss+1 are
-    // read from LDS while the MFMAs of sub-step ss run.
-    auto bulk_compute = [&](const uint8_t* base) {
+    // A bulk stage outside the steady state: scales from the window, then 4
+    // sub-steps of 16 MFMAs, the fragments of sub-step ss+1 read while the
+    // MFMAs of sub-step ss run.
+    auto bulk_compute = [&](const uint8_t* base, int st) {
+        const uint8_t* wsc = window_of(st);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) read_scales_i(wsc, q);
+        take_scales();
+        __builtin_amdgcn_sched_barrier(0);
         u32x4 fA[2][4], fB[2][4];
         fetch(base, 0, fA[0], fB[0]);
 #pragma unroll
@@ -464,15 +502,14 @@ dual_gemm_tiled(GemmArgs g) {
         }
         interleave_schedule();
     };
-    // Wait for this wave's copies of the next stage (everything but the four
-    // L2 touches), then for every wave.  The scheduling barrier keeps the
-    // MFMAs of the current stage above it, so they run while copies fly.
-    // (__syncthreads would add a release fence, i.e. wait for every
-    // outstanding memory operation including the L2 touches and the stores of
-    // the previous tile; only this wave's copies matter here.)
+    // End of a stage: this wave's copies into the other buffer have landed and
+    // its reads of the current buffer are done, then every wave arrives.  The
+    // scheduling barriers keep the stage's MFMAs above the wait, so they run
+    // while copies fly.  (__syncthreads would add a release fence and wait
+    // for the previous tile's stores as well.)
     auto stage_sync = [&]() {
         __builtin_amdgcn_sched_barrier(0);
-        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -480,6 +517,65 @@ dual_gemm_tiled(GemmArgs g) {
     auto lds_sync = [&]() {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
+    };
+
+    // ---- steady-state bulk stage st (buffer b) whose next stage st+1 is a
+    // bulk stage of the same tile.  Fixed issue order, one slot per MFMA:
+    //   slots  0-15  sub-step 3 of the previous stage (DEFER; its fragments
+    //                and scales are in registers), with: slots 0-7 this
+    //                stage's scale words and sub-step 0 fragments (A0 B0 B1
+    //                B2 B3 A1 A2 A3, the order its MFMAs need them), slot 12
+    //                the scale shuffle, slots 8-15 the A copies of stage st+1;
+    //   slots 16-31  sub-step 0, with sub-step 1's fragments and the B copies
+    //                (slots 16-23) and the next scale window (slot 24);
+    //   slots 32-47  sub-step 1, sub-step 2's fragments in slots 32-39;
+    //   slots 48-63  sub-step 2, sub-step 3's fragments in slots 48-55.
+    u32x4 pf[2][2][4];                 // fragment sets [set][A/B][i]
+    uint32_t pA[4], pB[4];             // sub-step 3 scales of the previous stage
+    auto frag_read = [&](const uint8_t* base, int ss, int set, int q) {
+        const uint32_t co = (uint32_t)(((2 * ss + h) ^ sw) << 4);
+        const bool isA = q == 0 || q >= 5;
+        const int r = q == 0 ? 0 : (q < 5 ? q - 1 : q - 4);
+        if (isA) pf[set][0][r] = *reinterpret_cast<const u32x4*>(base + fa[r] + co);
+        else     pf[set][1][r] = *reinterpret_cast<const u32x4*>(base + fb[r] + co);
+    };
+    auto steady_stage = [&](auto DEFER, const TileOrg& o, int st, int b) {
+        const uint8_t* base = lds + b * STAGE_BYTES;
+        const uint8_t* wsc = window_of(st);
+        const bool opens_window = ((st + 1) & 1) == 0;
+        static_for<64>([&](auto QC) {
+            constexpr int q = decltype(QC)::value;
+            if constexpr (q < 16) {
+                if constexpr (decltype(DEFER)::value) {
+                    const int i = q >> 2, j = q & 3;
+                    acc[i][j] = mfma_fp4_op<2>(pf[1][1][j], pf[1][0][i], pB[j], pA[i], acc[i][j]);
+                }
+            } else {
+                constexpr int ss = (q - 16) >> 4, r = (q - 16) & 15, i = r >> 2, j = r & 3, set = ss & 1;
+                acc[i][j] = mfma_fp4_op<(ss & 1) ? 2 : 0>(pf[set][1][j], pf[set][0][i], scB[j][ss >> 1],
+                                                          scA[i][ss >> 1], acc[i][j]);
+            }
+            if constexpr (q < 8) {
+                read_scales_i(wsc, q);
+                frag_read(base, 0, 0, q);
+            } else if constexpr (q < 16) {
+                if constexpr (q == 12) take_scales();
+                copy_bulk(o, st + 1, b ^ 1, q - 8, false);
+            } else if constexpr (q < 24) {
+                frag_read(base, 1, 1, q - 16);
+                copy_bulk(o, st + 1, b ^ 1, q - 16, true);
+            } else if constexpr (q == 24) {
+                if (opens_window) load_window(o, (st + 1) >> 1);
+            } else if constexpr (q >= 32 && q < 40) {
+                frag_read(base, 2, 0, q - 32);
+            } else if constexpr (q >= 48 && q < 56) {
+                frag_read(base, 3, 1, q - 48);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { pA[i] = scA[i][1]; pB[i] = scB[i][1]; }
+        stage_sync();
     };
 
     // ---- epilogue of one tile.  The MFMAs take the weight fragment as their
@@ -566,12 +662,8 @@ dual_gemm_tiled(GemmArgs g) {
     TileOrg cur = tile_org(t);
     int tn = t + nl;
     load_stage(cur, 0, 0);
-    if (S > 1) touch(&cur, 1);
-    else if (tn < t_end) { const TileOrg nx = tile_org(tn); touch(&nx, 0); }
-    else touch(nullptr, 0);
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    take_scales();
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __syncthreads();
     int buf = 0;
 
@@ -583,41 +675,40 @@ dual_gemm_tiled(GemmArgs g) {
         const bool has_next = tn < t_end;
         // steady state: bulk stages whose next two stages are bulk stages of this tile
         int st = 0;
-        for (; st + 2 < S4; ++st) {
-            load_stage(cur, st + 1, buf ^ 1);
-            touch(&cur, st + 2);
-            __builtin_amdgcn_sched_barrier(0);        // all copies issued before the MFMAs
-            bulk_compute(lds + buf * STAGE_BYTES);
-            stage_sync();
+        if (S4 > 2) {
+            steady_stage(std::false_type{}, cur, 0, buf);
             buf ^= 1;
-            take_scales();
+            for (st = 1; st + 2 < S4; ++st) {
+                steady_stage(std::true_type{}, cur, st, buf);
+                buf ^= 1;
+            }
+            // the deferred sub-step of the last steady stage
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = mfma_fp4_op<2>(pf[1][1][j], pf[1][0][i], pB[j], pA[i], acc[i][j]);
         }
         // the remaining stages (the last bulk stages, then the outlier stages)
         // with general bookkeeping for what comes next: a stage of this tile
         // or the first stage of the next tile.  Bulk and outlier stages run in
         // separate loops so each loop body has one kind of MFMA.
         auto prefetch_next = [&](int s0) {
-            const TileOrg nx = tile_org(has_next ? tn : t);
             if (s0 + 1 < S) load_stage(cur, s0 + 1, buf ^ 1);
-            else if (has_next) load_stage(nx, 0, buf ^ 1);
-            if (s0 + 2 < S) touch(&cur, s0 + 2);
-            else if (has_next && s0 + 2 - S < S) touch(&nx, s0 + 2 - S);
-            else touch(nullptr, 0);
+            else if (has_next) load_stage(tile_org(tn), 0, buf ^ 1);
             __builtin_amdgcn_sched_barrier(0);
         };
         for (; st < S4; ++st) {
             prefetch_next(st);
-            bulk_compute(lds + buf * STAGE_BYTES);
+            bulk_compute(lds + buf * STAGE_BYTES, st);
             stage_sync();
             buf ^= 1;
-            if ((st + 1 < S4) || (st + 1 == S && has_next)) take_scales();
         }
         for (; st < S; ++st) {
             prefetch_next(st);
             outlier_compute(lds + buf * STAGE_BYTES);
             stage_sync();
             buf ^= 1;
-            if (st + 1 == S && has_next) take_scales();
         }
         // buffer buf^1 held the last stage and is free; buf holds the next
         // tile's first stage (if any)
@@ -629,13 +720,13 @@ dual_gemm_tiled(GemmArgs g) {
     }
 }
 
-template <typename OutT, bool K8, bool NB8>
+template <typename OutT, bool K8, bool NB16>
 static hipError_t launch_tiled(const GemmArgs& a, hipStream_t st) {
     static thread_local int configured_dev = -1;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return hipErrorNoDevice;
     if (configured_dev != dev) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dual_gemm_tiled<OutT, K8, NB8>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dual_gemm_tiled<OutT, K8, NB16>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_LDS_BYTES);
         if (e != hipSuccess) return e;
         configured_dev = dev;
@@ -644,7 +735,7 @@ static hipError_t launch_tiled(const GemmArgs& a, hipStream_t st) {
     const int per = (T + NXCD - 1) / NXCD;
     const int cus_per_xcd = device_cu_count() / NXCD;
     const int wg_per_xcd = per < cus_per_xcd ? per : (cus_per_xcd > 0 ? cus_per_xcd : 1);
-    hipLaunchKernelGGL((dual_gemm_tiled<OutT, K8, NB8>), dim3((unsigned)(wg_per_xcd * NXCD)), dim3(256),
+    hipLaunchKernelGGL((dual_gemm_tiled<OutT, K8, NB16>), dim3((unsigned)(wg_per_xcd * NXCD)), dim3(256),
                        GEMM_LDS_BYTES, st, a);
     return hipGetLastError();
 }
@@ -652,10 +743,10 @@ static hipError_t launch_tiled(const GemmArgs& a, hipStream_t st) {
 template <typename OutT>
 static hipError_t launch_tiled_t(const GemmArgs& a, hipStream_t st) {
     const bool k8 = a.k % 8 == 0;
-    const bool nb8 = (a.K / 32) % 8 == 0;
-    if (k8 && nb8) return launch_tiled<OutT, true, true>(a, st);
+    const bool nb16 = (a.K / 32) % 16 == 0;
+    if (k8 && nb16) return launch_tiled<OutT, true, true>(a, st);
     if (k8) return launch_tiled<OutT, true, false>(a, st);
-    if (nb8) return launch_tiled<OutT, false, true>(a, st);
+    if (nb16) return launch_tiled<OutT, false, true>(a, st);
     return launch_tiled<OutT, false, false>(a, st);
 }
 
