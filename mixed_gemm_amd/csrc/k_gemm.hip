@@ -360,148 +360,80 @@ dual_gemm_tiled(GemmArgs g) {
         }
     };
 
-    // ---- copies of one 8-row group of bulk stage st of the A (B) tile
-    auto copy_bulk = [&](const TileOrg& o, int st, int b, int part, bool isB) {
-        uint8_t* dst = lds + b * STAGE_BYTES + lds_w + (isB ? TILE_BYTES : 0) + part * 8 * ROWB;
-        uint32_t lr = lrA0;
-        asm volatile("" : "+v"(lr));
-        const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)st * ROWB);
-        const uint32_t r0 = __builtin_amdgcn_readfirstlane((isB ? (uint32_t)o.n0 : (uint32_t)o.m0) * rowA);
-        const uint32_t c = (part & 1) ? c16o : c16e;
-        const bool ok = so + c < rowA;                // chunks past K (only when K % 256 != 0)
-        const uint32_t v = ok ? lr + c + r0 + (uint32_t)part * 8 * rowA : OOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(isB ? rB : rA, (lds_ptr_t)dst, 16, v, so, 0, 0);
+    // ---- the stage whose copies are issued during the current one: stage
+    // `st` of tile `o` (bulk stages first, then outlier stages), or nothing
+    // (st < 0).  Wave-uniform.
+    struct NextCopy {
+        TileOrg o;
+        int st;
     };
 
-    // Copies of stage st of a tile into LDS buffer `buf` (asynchronous), with
-    // the scale window the stage opens.
-    auto load_stage = [&](const TileOrg& o, int st, int buf) {
-        uint8_t* base = lds + buf * STAGE_BYTES + lds_w;
-        if (st < S4) {
+    // Copies of one 8-row group of the A (B) tile of stage nc (asynchronous,
+    // straight into LDS buffer b).  With nothing to copy every lane reads out
+    // of range, which lands zeros in the free buffer.
+    auto copy_part = [&](const NextCopy& nc, int b, int part, bool isB) {
+        uint8_t* dst = lds + b * STAGE_BYTES + lds_w + (isB ? TILE_BYTES : 0) + part * 8 * ROWB;
+        const bool bulk = nc.st < S4;
+        const uint32_t rowb = bulk ? rowA : rowX;
+        uint32_t lr = bulk ? lrA0 : lrX0;
+        asm volatile("" : "+v"(lr));
+        const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)(bulk ? nc.st : nc.st - S4) * ROWB);
+        const uint32_t r0 = __builtin_amdgcn_readfirstlane((isB ? (uint32_t)nc.o.n0 : (uint32_t)nc.o.m0) * rowb);
+        const uint32_t c = (part & 1) ? c16o : c16e;
+        const bool ok = nc.st >= 0 && so + c < rowb;      // chunks past K / k read as zero
+        const uint32_t v = ok ? lr + c + r0 + (uint32_t)part * 8 * rowb : OOB;
+        if (bulk)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(isB ? rB : rA, (lds_ptr_t)dst, 16, v, so, 0, 0);
+        else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(isB ? rWO : rXO, (lds_ptr_t)dst, 16, v, so, 0, 0);
+    };
+
+    // Outlier stage u of tile o when k % 8 != 0: the rows are not 16-byte
+    // aligned, so the bf16 values are gathered one by one and each chunk is
+    // stored through registers.
+    auto gather_outlier = [&](const TileOrg& o, int u, int b) {
+        uint8_t* base = lds + b * STAGE_BYTES + lds_w;
+        const int64_t ra0 = o.m0 + wave * 64 + lrow, rb0 = (int64_t)o.n0 + wave * 64 + lrow;
+#pragma unroll
+        for (int gi = 0; gi < 8; ++gi) {
+            const int cl = (int)(((gi & 1) ? c16o : c16e) >> 4);
+            const int64_t ra = ra0 + 8 * gi, rb = rb0 + 8 * gi;
+            uint32_t wa[4], wb[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                uint32_t xa = 0, xb = 0;
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const int col = u * 64 + cl * 8 + 2 * e + q;
+                    const uint32_t ea = (col < k && ra < M)
+                        ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rXO, (uint32_t)((ra * k + col) * 2), 0, 0) : 0u;
+                    const uint32_t eb = (col < k && rb < N)
+                        ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rWO, (uint32_t)((rb * k + col) * 2), 0, 0) : 0u;
+                    xa |= (ea & 0xFFFFu) << (16 * q);
+                    xb |= (eb & 0xFFFFu) << (16 * q);
+                }
+                wa[e] = xa; wb[e] = xb;
+            }
+            *reinterpret_cast<u32x4*>(base + gi * 8 * ROWB + lane * 16) = u32x4{wa[0], wa[1], wa[2], wa[3]};
+            *reinterpret_cast<u32x4*>(base + TILE_BYTES + gi * 8 * ROWB + lane * 16) = u32x4{wb[0], wb[1], wb[2], wb[3]};
+        }
+    };
+
+    // All copies of stage nc at once (the very first stage), with the scale
+    // window it opens.
+    auto load_stage = [&](const NextCopy& nc, int b) {
+        if (!K8 && nc.st >= S4) {
+            gather_outlier(nc.o, nc.st - S4, b);
+        } else {
 #pragma unroll
             for (int gi = 0; gi < 8; ++gi) {
-                copy_bulk(o, st, buf, gi, false);
-                copy_bulk(o, st, buf, gi, true);
-            }
-            if ((st & 1) == 0) load_window(o, st >> 1);
-        } else {
-            const int u = st - S4;
-            const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)u * ROWB);
-            uint32_t lrX = lrX0;
-            asm volatile("" : "+v"(lrX));
-            if constexpr (K8) {
-                const uint32_t ra = __builtin_amdgcn_readfirstlane((uint32_t)o.m0 * rowX);
-                const uint32_t rb = __builtin_amdgcn_readfirstlane((uint32_t)o.n0 * rowX);
-                const bool oke = so + c16e < rowX, oko = so + c16o < rowX;
-#pragma unroll
-                for (int gi = 0; gi < 8; ++gi) {
-                    const uint32_t c = (gi & 1) ? c16o : c16e;
-                    const bool ok = (gi & 1) ? oko : oke;
-                    const uint32_t va = ok ? lrX + c + ra + (uint32_t)gi * 8 * rowX : OOB;
-                    const uint32_t vb = ok ? lrX + c + rb + (uint32_t)gi * 8 * rowX : OOB;
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rXO, (lds_ptr_t)(base + gi * 8 * ROWB), 16, va, so, 0, 0);
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rWO, (lds_ptr_t)(base + TILE_BYTES + gi * 8 * ROWB), 16,
-                                                             vb, so, 0, 0);
-                }
-            } else {
-                // k % 8 != 0: outlier rows are not 16-byte aligned; gather the
-                // bf16 values one by one and store the chunk through registers.
-                const int64_t ra0 = o.m0 + wave * 64 + lrow, rb0 = (int64_t)o.n0 + wave * 64 + lrow;
-#pragma unroll
-                for (int gi = 0; gi < 8; ++gi) {
-                    const int cl = (int)(((gi & 1) ? c16o : c16e) >> 4);
-                    const int64_t ra = ra0 + 8 * gi, rb = rb0 + 8 * gi;
-                    uint32_t wa[4], wb[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        uint32_t xa = 0, xb = 0;
-#pragma unroll
-                        for (int q = 0; q < 2; ++q) {
-                            const int col = u * 64 + cl * 8 + 2 * e + q;
-                            const uint32_t ea = (col < k && ra < M)
-                                ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rXO, (uint32_t)((ra * k + col) * 2), 0, 0) : 0u;
-                            const uint32_t eb = (col < k && rb < N)
-                                ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rWO, (uint32_t)((rb * k + col) * 2), 0, 0) : 0u;
-                            xa |= (ea & 0xFFFFu) << (16 * q);
-                            xb |= (eb & 0xFFFFu) << (16 * q);
-                        }
-                        wa[e] = xa; wb[e] = xb;
-                    }
-                    *reinterpret_cast<u32x4*>(base + gi * 8 * ROWB + lane * 16) = u32x4{wa[0], wa[1], wa[2], wa[3]};
-                    *reinterpret_cast<u32x4*>(base + TILE_BYTES + gi * 8 * ROWB + lane * 16) = u32x4{wb[0], wb[1], wb[2], wb[3]};
-                }
+                copy_part(nc, b, gi, false);
+                copy_part(nc, b, gi, true);
             }
         }
+        if (nc.st >= 0 && nc.st < S4 && (nc.st & 1) == 0) load_window(nc.o, nc.st >> 1);
     };
 
-    // fragments of sub-step ss: A rows fa[i], B rows fb[i], 16 bytes each
-    auto fetch = [&](const uint8_t* base, int ss, u32x4 (&fA)[4], u32x4 (&fB)[4]) {
-        const uint32_t co = (uint32_t)(((2 * ss + h) ^ sw) << 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            fA[i] = *reinterpret_cast<const u32x4*>(base + fa[i] + co);
-            fB[i] = *reinterpret_cast<const u32x4*>(base + fb[i] + co);
-        }
-    };
-
-    // Instruction order of a stage outside the steady state: the 8 fragment
-    // reads of sub-step 0, then for each sub-step the reads of the next one
-    // threaded between its first 8 MFMAs.
-    auto interleave_schedule = [&]() {
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);          // DS reads
-#pragma unroll
-        for (int ss = 0; ss < 3; ++ss) {
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-    };
-
-    // A bulk stage outside the steady state: scales from the window, then 4
-    // sub-steps of 16 MFMAs, the fragments of sub-step ss+1 read while the
-    // MFMAs of sub-step ss run.
-    auto bulk_compute = [&](const uint8_t* base, int st) {
-        const uint8_t* wsc = window_of(st);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) read_scales_i(wsc, q);
-        take_scales();
-        __builtin_amdgcn_sched_barrier(0);
-        u32x4 fA[2][4], fB[2][4];
-        fetch(base, 0, fA[0], fB[0]);
-#pragma unroll
-        for (int ss = 0; ss < 4; ++ss) {
-            if (ss < 3) fetch(base, ss + 1, fA[(ss + 1) & 1], fB[(ss + 1) & 1]);
-            const int c = ss & 1;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if ((ss & 1) == 0)
-                        acc[i][j] = mfma_fp4_op<0>(fB[c][j], fA[c][i], scB[j][ss >> 1], scA[i][ss >> 1], acc[i][j]);
-                    else
-                        acc[i][j] = mfma_fp4_op<2>(fB[c][j], fA[c][i], scB[j][ss >> 1], scA[i][ss >> 1], acc[i][j]);
-                }
-        }
-        interleave_schedule();
-    };
-    auto outlier_compute = [&](const uint8_t* base) {
-        u32x4 fA[2][4], fB[2][4];
-        fetch(base, 0, fA[0], fB[0]);
-#pragma unroll
-        for (int ss = 0; ss < 4; ++ss) {
-            if (ss < 3) fetch(base, ss + 1, fA[(ss + 1) & 1], fB[(ss + 1) & 1]);
-            const int c = ss & 1;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16_v(fB[c][j], fA[c][i], acc[i][j]);
-        }
-        interleave_schedule();
-    };
     // End of a stage: this wave's copies into the other buffer have landed and
     // its reads of the current buffer are done, then every wave arrives.  The
     // scheduling barriers keep the stage's MFMAs above the wait, so they run
@@ -513,23 +445,24 @@ dual_gemm_tiled(GemmArgs g) {
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
     };
-    // LDS-only barrier: this wave's LDS writes are done, then every wave arrives.
-    auto lds_sync = [&]() {
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-    };
 
-    // ---- steady-state bulk stage st (buffer b) whose next stage st+1 is a
-    // bulk stage of the same tile.  Fixed issue order, one slot per MFMA:
-    //   slots  0-15  sub-step 3 of the previous stage (DEFER; its fragments
-    //                and scales are in registers), with: slots 0-7 this
-    //                stage's scale words and sub-step 0 fragments (A0 B0 B1
-    //                B2 B3 A1 A2 A3, the order its MFMAs need them), slot 12
-    //                the scale shuffle, slots 8-15 the A copies of stage st+1;
-    //   slots 16-31  sub-step 0, with sub-step 1's fragments and the B copies
-    //                (slots 16-23) and the next scale window (slot 24);
-    //   slots 32-47  sub-step 1, sub-step 2's fragments in slots 32-39;
-    //   slots 48-63  sub-step 2, sub-step 3's fragments in slots 48-55.
+    // ---- one stage, in a fixed issue order of one slot per MFMA.  A stage
+    // is 4 sub-steps of 16 MFMAs (FP4 for a bulk stage, BF16 for an outlier
+    // stage); sub-step 3 is normally read before the stage barrier and
+    // multiplied after it, at the start of the next stage (DEFER_OUT), so
+    // the matrix cores have 16 MFMAs of work while the next stage's first
+    // fragments are read.  Slots:
+    //   0-15   the previous stage's sub-step 3 (kind DK: 0 none, 1 FP4, 2
+    //          BF16); slots 0-7 also read this stage's scale words and
+    //          sub-step 0's fragments (A0 B0 B1 B2 B3 A1 A2 A3, the order its
+    //          MFMAs need them), slot 12 shuffles the scales;
+    //   16-63  sub-steps 0, 1, 2; the next sub-step's fragments are read in
+    //          the first 8 slots of each;
+    //   64-79  sub-step 3 when it is not deferred (the last stage of a tile).
+    // The next stage's 16 copies go one per 2 slots from slot 2 to 32, the
+    // scale window it opens (if any) in slot 36: never two memory
+    // instructions back to back, so the address unit is shared evenly
+    // between the four waves.
     u32x4 pf[2][2][4];                 // fragment sets [set][A/B][i]
     uint32_t pA[4], pB[4];             // sub-step 3 scales of the previous stage
     auto frag_read = [&](const uint8_t* base, int ss, int set, int q) {
@@ -539,42 +472,56 @@ dual_gemm_tiled(GemmArgs g) {
         if (isA) pf[set][0][r] = *reinterpret_cast<const u32x4*>(base + fa[r] + co);
         else     pf[set][1][r] = *reinterpret_cast<const u32x4*>(base + fb[r] + co);
     };
-    auto steady_stage = [&](auto DEFER, const TileOrg& o, int st, int b) {
+    auto run_stage = [&](auto CUR_BULK, auto DK, auto DEFER_OUT, const NextCopy& nc, int st, int b) {
+        constexpr bool cb = decltype(CUR_BULK)::value;
+        constexpr int dk = decltype(DK)::value;
+        constexpr bool dout = decltype(DEFER_OUT)::value;
         const uint8_t* base = lds + b * STAGE_BYTES;
-        const uint8_t* wsc = window_of(st);
-        const bool opens_window = ((st + 1) & 1) == 0;
-        static_for<64>([&](auto QC) {
+        const uint8_t* wsc = nullptr;
+        if constexpr (cb) wsc = window_of(st);
+        const bool dma_next = K8 || nc.st < S4;
+        const bool opens_window = nc.st >= 0 && nc.st < S4 && (nc.st & 1) == 0;
+        static_for<80>([&](auto QC) {
             constexpr int q = decltype(QC)::value;
-            if constexpr (q < 16) {
-                if constexpr (decltype(DEFER)::value) {
-                    const int i = q >> 2, j = q & 3;
-                    acc[i][j] = mfma_fp4_op<2>(pf[1][1][j], pf[1][0][i], pB[j], pA[i], acc[i][j]);
+            if constexpr (q < 64 || !dout) {
+                if constexpr (q < 16) {
+                    constexpr int i = q >> 2, j = q & 3;
+                    if constexpr (dk == 1)
+                        acc[i][j] = mfma_fp4_op<2>(pf[1][1][j], pf[1][0][i], pB[j], pA[i], acc[i][j]);
+                    else if constexpr (dk == 2)
+                        acc[i][j] = mfma_bf16_v(pf[1][1][j], pf[1][0][i], acc[i][j]);
+                } else {
+                    constexpr int ss = (q - 16) >> 4, r = (q - 16) & 15, i = r >> 2, j = r & 3, set = ss & 1;
+                    if constexpr (cb)
+                        acc[i][j] = mfma_fp4_op<(ss & 1) ? 2 : 0>(pf[set][1][j], pf[set][0][i], scB[j][ss >> 1],
+                                                                  scA[i][ss >> 1], acc[i][j]);
+                    else
+                        acc[i][j] = mfma_bf16_v(pf[set][1][j], pf[set][0][i], acc[i][j]);
                 }
-            } else {
-                constexpr int ss = (q - 16) >> 4, r = (q - 16) & 15, i = r >> 2, j = r & 3, set = ss & 1;
-                acc[i][j] = mfma_fp4_op<(ss & 1) ? 2 : 0>(pf[set][1][j], pf[set][0][i], scB[j][ss >> 1],
-                                                          scA[i][ss >> 1], acc[i][j]);
+                if constexpr (q < 8) {
+                    if constexpr (cb) read_scales_i(wsc, q);
+                    frag_read(base, 0, 0, q);
+                }
+                if constexpr (cb && q == 12) take_scales();
+                if constexpr (q >= 16 && q < 24) frag_read(base, 1, 1, q - 16);
+                if constexpr (q >= 32 && q < 40) frag_read(base, 2, 0, q - 32);
+                if constexpr (q >= 48 && q < 56) frag_read(base, 3, 1, q - 48);
+                if constexpr (q >= 2 && q <= 32 && q % 2 == 0) {
+                    if (dma_next) copy_part(nc, b ^ 1, (q - 2) >> 2, ((q - 2) & 2) != 0);
+                }
+                if constexpr (!K8 && q == 2) {
+                    if (!dma_next) gather_outlier(nc.o, nc.st - S4, b ^ 1);
+                }
+                if constexpr (q == 36) {
+                    if (opens_window) load_window(nc.o, nc.st >> 1);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            if constexpr (q < 8) {
-                read_scales_i(wsc, q);
-                frag_read(base, 0, 0, q);
-            } else if constexpr (q < 16) {
-                if constexpr (q == 12) take_scales();
-                copy_bulk(o, st + 1, b ^ 1, q - 8, false);
-            } else if constexpr (q < 24) {
-                frag_read(base, 1, 1, q - 16);
-                copy_bulk(o, st + 1, b ^ 1, q - 16, true);
-            } else if constexpr (q == 24) {
-                if (opens_window) load_window(o, (st + 1) >> 1);
-            } else if constexpr (q >= 32 && q < 40) {
-                frag_read(base, 2, 0, q - 32);
-            } else if constexpr (q >= 48 && q < 56) {
-                frag_read(base, 3, 1, q - 48);
-            }
-            __builtin_amdgcn_sched_barrier(0);
         });
+        if constexpr (cb && dout) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { pA[i] = scA[i][1]; pB[i] = scB[i][1]; }
+            for (int i = 0; i < 4; ++i) { pA[i] = scA[i][1]; pB[i] = scB[i][1]; }
+        }
         stage_sync();
     };
 
@@ -585,52 +532,67 @@ dual_gemm_tiled(GemmArgs g) {
     // columns per register group.
     auto epilogue = [&](const TileOrg& o, uint8_t* stagebuf) {
         if constexpr (sizeof(OutT) == 2) {
-            // bf16: round pairs with the hardware converter (nearest even) and
-            // write the tile in 4 passes; pass p stages the rows of accumulator
-            // row-block p of every wave -- 64 rows x 512 B -- in one half of
-            // the free buffer (alternating halves), then all threads write
-            // those rows with 16-byte streaming stores.  In a staged row r'
-            // (= 32 wm + l32) the 8-byte unit u lives at unit u ^ (2 (r' % 32)):
-            // the 32 rows written by one instruction spread over the banks and
-            // the 16-byte chunk c stays contiguous at chunk c ^ (r' % 32).
-            uint16_t* Yb = static_cast<uint16_t*>(g.Y);
-            const bool full = o.m0 + TBM <= M && o.n0 + TBN <= N;
-            // Every lane-dependent value below is derived from an opaque copy of
-            // the thread index, so it is formed here, once per tile, instead of
-            // being hoisted out of the tile loop and held (or spilled) across it.
+            // bf16: round pairs with the hardware converter (nearest even).
+            // Each wave stages its own 128x128 quarter through its own 16 KB
+            // of the free buffer, 64 rows x 256 B per pass, and writes the
+            // rows back out with 16-byte streaming stores (four 256-byte row
+            // pieces per instruction).  No wave reads another wave's staging,
+            // so a pass needs no barrier: one wave's LDS accesses are
+            // processed in order.  In a staged row r the 16-byte chunk c
+            // (columns 8c .. 8c+7 of the quarter) sits at chunk c ^ (r & 15).
+            // the tile's rows of Y: rows past M are out of the descriptor's
+            // range and columns past N get an out-of-range offset, so the
+            // stores need no branches
+            const uint32_t rowY = (uint32_t)N * 2u;
+            const int64_t rows_left = M - o.m0;
+            const uint32_t nrec = (uint32_t)(rows_left < TBM ? rows_left : TBM) * rowY;
+            const __amdgpu_buffer_rsrc_t rY =
+                make_rsrc(static_cast<uint16_t*>(g.Y) + o.m0 * (int64_t)N, (uint64_t)nrec);
+            uint8_t* wbuf = stagebuf + wave * 16384;
+            // Lane-dependent values come from an opaque copy of the thread
+            // index, so they are formed here, once per tile, instead of being
+            // hoisted out of the tile loop and held (or spilled) across it.
             uint32_t et = (uint32_t)tid;
             asm volatile("" : "+v"(et));
             const uint32_t el32 = et & 31u, eh = (et >> 5) & 1u;
-            const uint32_t eb = ((uint32_t)wm * 32 + el32) * 512 + eh * 8, em = el32 << 4;
+            const uint32_t rl = (et & 63u) >> 4, cl = et & 15u;       // read side: row (of 4), chunk
+            const int gcol = o.n0 + wn * 128 + (int)cl * 8;
+            const bool col_ok = gcol < N;
+            const uint32_t cofs = (uint32_t)gcol * 2u;
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                uint8_t* sb = stagebuf + (p & 1) * 32768;
-                // read row-block p's accumulators here, not earlier
+            for (int p = 0; p < 2; ++p) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[p][j]));
+                for (int ii = 0; ii < 2; ++ii) {
+                    const int i = 2 * p + ii;
+                    // read row-block i's accumulators here, not earlier
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                    for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
+                    const uint32_t r = (uint32_t)(32 * ii) + el32;
+                    const uint32_t rb = r * 256 + eh * 8, rs = r & 15u;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const f32x2 lo = {acc[p][j][4 * q], acc[p][j][4 * q + 1]};
-                        const f32x2 hi = {acc[p][j][4 * q + 2], acc[p][j][4 * q + 3]};
-                        const u32x2 w = {__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2)),
-                                         __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2))};
-                        const uint32_t cu = (uint32_t)((wn * 32 + 8 * j + 2 * q) << 3);
-                        *reinterpret_cast<u32x2*>(sb + eb + (cu ^ em)) = w;
-                    }
-                lds_sync();
+                    for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int qq = 0; qq < 8; ++qq) {
-                    const int c = (int)et + 256 * qq;      // 16-byte chunk of the 64 staged rows
-                    const int rr = c >> 5, cc16 = c & 31;
-                    const u32x4 v = *reinterpret_cast<const u32x4*>(sb + rr * 512 + ((cc16 ^ (rr & 31)) << 4));
-                    const int64_t grow = o.m0 + (rr >> 5) * 128 + 32 * p + (rr & 31);
-                    const int gcol = o.n0 + cc16 * 8;
-                    // streaming store: Y is written once and must not push the
-                    // operand panels out of L2
-                    if (full || (grow < M && gcol < N))
-                        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(Yb + grow * N + gcol));
+                        for (int q = 0; q < 4; ++q) {
+                            const f32x2 lo = {acc[i][j][4 * q], acc[i][j][4 * q + 1]};
+                            const f32x2 hi = {acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                            const u32x2 w = {__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2)),
+                                             __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2))};
+                            *reinterpret_cast<u32x2*>(wbuf + rb + ((((uint32_t)(4 * j + q)) ^ rs) << 4)) = w;
+                        }
+                }
+                u32x4 v[16];
+#pragma unroll
+                for (int sI = 0; sI < 16; ++sI) {
+                    const uint32_t rr = (uint32_t)(4 * sI) + rl;
+                    v[sI] = *reinterpret_cast<const u32x4*>(wbuf + rr * 256 + ((cl ^ (rr & 15u)) << 4));
+                }
+#pragma unroll
+                for (int sI = 0; sI < 16; ++sI) {
+                    const uint32_t rr = (uint32_t)(4 * sI) + rl;
+                    const uint32_t off = col_ok ? ((uint32_t)(wm * 128 + 64 * p) + rr) * rowY + cofs : OOB;
+                    // streaming store (nt): Y is written once and must not
+                    // push the operand panels out of L2
+                    __builtin_amdgcn_raw_buffer_store_b128(v[sI], rY, off, 0, 2);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -661,53 +623,47 @@ dual_gemm_tiled(GemmArgs g) {
     // ---- prologue: first stage of the first tile
     TileOrg cur = tile_org(t);
     int tn = t + nl;
-    load_stage(cur, 0, 0);
+    load_stage(NextCopy{cur, 0}, 0);
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __syncthreads();
     int buf = 0;
 
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    using D0 = std::integral_constant<int, 0>;
+    using D1 = std::integral_constant<int, 1>;
     while (true) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
         const bool has_next = tn < t_end;
-        // steady state: bulk stages whose next two stages are bulk stages of this tile
-        int st = 0;
-        if (S4 > 2) {
-            steady_stage(std::false_type{}, cur, 0, buf);
-            buf ^= 1;
-            for (st = 1; st + 2 < S4; ++st) {
-                steady_stage(std::true_type{}, cur, st, buf);
-                buf ^= 1;
-            }
-            // the deferred sub-step of the last steady stage
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = mfma_fp4_op<2>(pf[1][1][j], pf[1][0][i], pB[j], pA[i], acc[i][j]);
-        }
-        // the remaining stages (the last bulk stages, then the outlier stages)
-        // with general bookkeeping for what comes next: a stage of this tile
-        // or the first stage of the next tile.  Bulk and outlier stages run in
-        // separate loops so each loop body has one kind of MFMA.
-        auto prefetch_next = [&](int s0) {
-            if (s0 + 1 < S) load_stage(cur, s0 + 1, buf ^ 1);
-            else if (has_next) load_stage(tile_org(tn), 0, buf ^ 1);
-            __builtin_amdgcn_sched_barrier(0);
+        const TileOrg nxt = tile_org(has_next ? tn : t);
+        // the stage after st: the next one of this tile, the first one of the
+        // next tile, or none
+        auto next_of = [&](int st) {
+            NextCopy nc{cur, st + 1};
+            if (st + 1 == S) nc = has_next ? NextCopy{nxt, 0} : NextCopy{cur, -1};
+            return nc;
         };
+        // bulk stages, each leaving its sub-step 3 to the next
+        run_stage(T_{}, D0{}, T_{}, next_of(0), 0, buf);
+        buf ^= 1;
+        int st = 1;
         for (; st < S4; ++st) {
-            prefetch_next(st);
-            bulk_compute(lds + buf * STAGE_BYTES, st);
-            stage_sync();
+            run_stage(T_{}, D1{}, T_{}, next_of(st), st, buf);
             buf ^= 1;
         }
+        // the last bulk stage's sub-step 3
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = mfma_fp4_op<2>(pf[1][1][j], pf[1][0][i], pB[j], pA[i], acc[i][j]);
+        // outlier stages, each complete in itself
         for (; st < S; ++st) {
-            prefetch_next(st);
-            outlier_compute(lds + buf * STAGE_BYTES);
-            stage_sync();
+            run_stage(F_{}, D0{}, F_{}, next_of(st), st, buf);
             buf ^= 1;
         }
         // buffer buf^1 held the last stage and is free; buf holds the next
@@ -716,7 +672,7 @@ dual_gemm_tiled(GemmArgs g) {
         if (!has_next) break;
         t = tn;
         tn += nl;
-        cur = tile_org(t);
+        cur = nxt;
     }
 }
 
