@@ -50,29 +50,19 @@ __device__ int block_inclusive_scan(int v, int* buf) {
     return r;
 }
 
-__device__ int block_sum(int v, int* buf) {
-    const int t = threadIdx.x;
-    buf[t] = v;
-    __syncthreads();
-    for (int off = kTopkThreads / 2; off > 0; off >>= 1) {
-        if (t < off) buf[t] += buf[t + off];
-        __syncthreads();
-    }
-    int r = buf[0];
-    __syncthreads();
-    return r;
-}
 
 // One workgroup.  Scores are non-negative floats, compared through their bit
-// patterns (same order).  T = the k-th largest score is found by bisection on
-// the bit pattern; channels above T are in O, and of the channels equal to T
-// the lowest indices fill the remaining places (tie rule: index ascending).
-// Thread t owns the contiguous index range [t*C, (t+1)*C) so block scans give
-// ascending order directly.
+// patterns (same order).  T = the k-th largest score is found by an MSB-first
+// radix select, 8 bits per pass with a 256-bin histogram in LDS; channels above
+// T are in O, and of the channels equal to T the lowest indices fill the
+// remaining places (tie rule: index ascending).  Thread t owns the contiguous
+// index range [t*C, (t+1)*C) so block scans give ascending order directly.
 __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const float* __restrict__ a, int32_t K,
                                                             int32_t k, int32_t* __restrict__ O,
                                                             int32_t* __restrict__ pos) {
     __shared__ int buf[kTopkThreads];
+    __shared__ int hist[256];
+    __shared__ uint32_t sel[2];
     const uint32_t* ab = reinterpret_cast<const uint32_t*>(a);
     const int t = threadIdx.x;
     const int C = (K + kTopkThreads - 1) / kTopkThreads;
@@ -82,17 +72,34 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const float* __restr
     uint32_t T = 0;
     int need = 0;
     if (k > 0 && k < K) {
-        uint32_t lo = 0, hi = 0x7F800000u;       // count(score >= 0) = K >= k
-        while (lo < hi) {
-            const uint32_t mid = lo + (hi - lo + 1) / 2;
-            int c = 0;
-            for (int j = j0; j < j1; ++j) c += ab[j] >= mid;
-            if (block_sum(c, buf) >= k) lo = mid; else hi = mid - 1;
+        uint32_t prefix = 0, pmask = 0;
+        int remaining = k;                        // still to pick among keys matching the prefix
+        for (int shift = 24; shift >= 0; shift -= 8) {
+            if (t < 256) hist[t] = 0;
+            __syncthreads();
+            for (int j = j0; j < j1; ++j) {
+                const uint32_t key = ab[j];
+                if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+            }
+            __syncthreads();
+            if (t == 0) {
+                // the bin holding the remaining-th largest key, counted from the top
+                int above = 0, b = 255;
+                for (; b > 0; --b) {
+                    if (above + hist[b] >= remaining) break;
+                    above += hist[b];
+                }
+                sel[0] = (uint32_t)b;
+                sel[1] = (uint32_t)(remaining - above);
+            }
+            __syncthreads();
+            prefix |= sel[0] << shift;
+            pmask |= 255u << shift;
+            remaining = (int)sel[1];
+            __syncthreads();
         }
-        T = lo;
-        int g = 0;
-        for (int j = j0; j < j1; ++j) g += ab[j] > T;
-        need = k - block_sum(g, buf);
+        T = prefix;
+        need = remaining;                         // keys equal to T that are taken
     }
     // ties before my range
     int ties = 0;
@@ -127,9 +134,23 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const float* __restr
 
 // ---------------------------------------------------------------------------- fold + pack
 
-// Workgroup = 32 rows x 8 blocks of 32 K.  Thread (ty, tx) folds, extracts and
-// encodes row n = 32*blockIdx.y + ty, block b = 8*blockIdx.x + tx.  For the
-// 32x32 layout the 32 rows of a tile share their amax through LDS.
+constexpr int kFoldWaves = 4;
+constexpr int kFoldWavesPerCU = 32;
+
+__device__ __forceinline__ float quad_max_f(float v) {
+    // max over the 4 lanes of a quad (one 32-block): quad_perm [1,0,3,2] then [2,3,0,1]
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
+    return v;
+}
+
+// Lane layout as in the activation quantizer: a lane owns 8 consecutive
+// input channels (one 16-byte load of a bf16 row), 4 lanes form a 32-block,
+// a wave covers 512 channels of a row and walks rows.  Per row and lane:
+// W'[n][j] = RN(s_j * W[n][j]); outlier channels go to WO as bf16 and become
+// +0; the block amax gives the E8M0 code (1x32), or, for the 32x32 layout, the
+// amax over the 32 rows of the tile does (a first pass over the tile's rows,
+// the second pass re-reads them from L2); the hardware converter encodes.
 template <bool BF16, bool TILE>
 __global__ void __launch_bounds__(256) fold_pack_kernel(const void* __restrict__ W, int32_t N, int32_t K,
                                                         int32_t k, const float* __restrict__ s,
@@ -137,75 +158,110 @@ __global__ void __launch_bounds__(256) fold_pack_kernel(const void* __restrict__
                                                         uint8_t* __restrict__ Wq, uint8_t* __restrict__ Ws,
                                                         uint8_t* __restrict__ Wst,
                                                         uint16_t* __restrict__ WO) {
-    const int tx = threadIdx.x & 7;
-    const int ty = threadIdx.x >> 3;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int j0 = (blockIdx.x * 64 + lane) * 8;
+    const bool valid = j0 < K;                       // whole quads agree (K % 32 == 0)
     const int nb = K / 32;
-    const int b = blockIdx.x * 8 + tx;
-    const int64_t n = (int64_t)blockIdx.y * 32 + ty;
-    const bool valid = b < nb && n < N;
-    float v[32];
-    uint32_t amax = 0;
-    if (valid) {
-        const int j0 = b * 32;
-        if constexpr (BF16) {
-            const uint4* src = reinterpret_cast<const uint4*>(
-                reinterpret_cast<const uint16_t*>(W) + n * K + j0);
+    float sv[8];
+    uint32_t keep[8];
+    uint32_t omask = 0;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint4 d = src[q];
+    for (int i = 0; i < 8; ++i) {
+        sv[i] = valid ? s[j0 + i] : 0.0f;
+        const int p = valid ? pos[j0 + i] : -1;
+        keep[i] = p >= 0 ? 0u : 0xFFFFFFFFu;
+        omask |= (p >= 0 ? 1u : 0u) << i;
+    }
+
+    // RN(s * W) of the lane's 8 channels of row n (zeros when out of range)
+    auto fold_row = [&](int64_t n, float (&f)[8]) {
+        float x[8];
+        if (valid && n < N) {
+            if constexpr (BF16) {
+                const uint4 d = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W) + n * K + j0);
                 const uint32_t wd[4] = {d.x, d.y, d.z, d.w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    v[8 * q + 2 * i] = bf16_to_f32(wd[i] & 0xFFFFu);
-                    v[8 * q + 2 * i + 1] = bf16_to_f32(wd[i] >> 16);
+                    x[2 * i] = __uint_as_float(wd[i] << 16);
+                    x[2 * i + 1] = __uint_as_float(wd[i] & 0xFFFF0000u);
                 }
+            } else {
+                const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(W) + n * K + j0);
+                const float4 d0 = src[0], d1 = src[1];
+                x[0] = d0.x; x[1] = d0.y; x[2] = d0.z; x[3] = d0.w;
+                x[4] = d1.x; x[5] = d1.y; x[6] = d1.z; x[7] = d1.w;
             }
         } else {
-            const float4* src = reinterpret_cast<const float4*>(
-                reinterpret_cast<const float*>(W) + n * K + j0);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const float4 d = src[q];
-                v[4 * q] = d.x; v[4 * q + 1] = d.y; v[4 * q + 2] = d.z; v[4 * q + 3] = d.w;
+            for (int i = 0; i < 8; ++i) x[i] = 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = __fmul_rn(sv[i], x[i]);
+    };
+    // outlier channels of row n to WO, then masked to +0 in f; returns the
+    // lane's amax of the masked values
+    auto extract = [&](int64_t n, float (&f)[8]) {
+        if (omask) {
+            for (uint32_t m = omask; m; m &= m - 1) {
+                const int i = __builtin_ctz(m);
+                float fi = f[0];
+#pragma unroll
+                for (int t = 1; t < 8; ++t) fi = i == t ? f[t] : fi;
+                WO[n * k + pos[j0 + i]] = (uint16_t)f32_to_bf16_rne(fi);
             }
         }
+        float amax = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            float f = __fmul_rn(s[j0 + i], v[i]);          // RN(s_j * W[n][j])
-            const int p = pos[j0 + i];
-            if (p >= 0) {
-                WO[n * k + p] = (uint16_t)f32_to_bf16_rne(f);
-                f = 0.0f;
-            }
-            v[i] = f;
-            amax = max(amax, __float_as_uint(f) & 0x7FFFFFFFu);
+        for (int i = 0; i < 8; ++i) {
+            f[i] = __uint_as_float(__float_as_uint(f[i]) & keep[i]);
+            amax = fmaxf(amax, __builtin_fabsf(f[i]));
         }
-    }
-    if constexpr (TILE) {
-        __shared__ uint32_t tmax[32][8];
-        tmax[ty][tx] = amax;
-        __syncthreads();
-        if (ty == 0) {
-            uint32_t m = 0;
-            for (int r = 0; r < 32; ++r) m = max(m, tmax[r][tx]);
-            tmax[0][tx] = m;
-        }
-        __syncthreads();
-        amax = tmax[0][tx];
-    }
-    if (!valid) return;
-    const uint32_t c = e8m0_from_amax_bits(amax);
-    uint32_t packed[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
+        return amax;
+    };
+    auto encode_store = [&](int64_t n, const float (&f)[8], uint32_t c) {
+        const float scale = e8m0_to_f32(c);
         uint32_t word = 0;
+        MG_CVT_FP4X2(word, f[0], f[1], scale, 0);
+        MG_CVT_FP4X2(word, f[2], f[3], scale, 1);
+        MG_CVT_FP4X2(word, f[4], f[5], scale, 2);
+        MG_CVT_FP4X2(word, f[6], f[7], scale, 3);
+        *reinterpret_cast<uint32_t*>(Wq + n * (K / 2) + j0 / 2) = word;
+        if ((lane & 3) == 0) Ws[n * nb + j0 / 32] = (uint8_t)c;
+    };
+
+    const int64_t wstride = (int64_t)gridDim.y * kFoldWaves;
+    if constexpr (!TILE) {
+        for (int64_t n = (int64_t)blockIdx.y * kFoldWaves + wave; n < N; n += wstride) {
+            float f[8];
+            fold_row(n, f);
+            const float amax = quad_max_f(extract(n, f));
+            if (valid) encode_store(n, f, e8m0_from_amax_bits(__float_as_uint(amax)));
+        }
+    } else {
+        const int64_t NG = ((int64_t)N + 31) / 32;
+        for (int64_t gi = (int64_t)blockIdx.y * kFoldWaves + wave; gi < NG; gi += wstride) {
+            const int64_t n0 = gi * 32;
+            float tmax = 0.0f;
+            for (int r = 0; r < 32; ++r) {
+                float f[8];
+                fold_row(n0 + r, f);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) word |= e2m1_nibble(v[8 * q + i], c) << (4 * i);
-        packed[q] = word;
+                for (int i = 0; i < 8; ++i)
+                    tmax = fmaxf(tmax, __builtin_fabsf(__uint_as_float(__float_as_uint(f[i]) & keep[i])));
+            }
+            const uint32_t c = e8m0_from_amax_bits(__float_as_uint(quad_max_f(tmax)));
+            for (int r = 0; r < 32; ++r) {
+                const int64_t n = n0 + r;
+                if (n >= N) break;                       // uniform
+                float f[8];
+                fold_row(n, f);
+                (void)extract(n, f);
+                if (valid) encode_store(n, f, c);
+            }
+            if (valid && (lane & 3) == 0) Wst[gi * nb + j0 / 32] = (uint8_t)c;
+        }
     }
-    *reinterpret_cast<uint4*>(Wq + n * (K / 2) + b * 16) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-    Ws[n * nb + b] = (uint8_t)c;
-    if (TILE && ty == 0) Wst[(n / 32) * nb + b] = (uint8_t)c;
 }
 
 }  // namespace
@@ -226,9 +282,17 @@ hipError_t launch_topk(const float* a, int32_t K, int32_t k, int32_t* O, int32_t
 hipError_t launch_fold_pack(const void* W, int32_t dtype, int32_t N, int32_t K, int32_t k,
                             int32_t layout, const float* s, const int32_t* pos, uint8_t* Wq,
                             uint8_t* Ws, uint8_t* Wst, uint16_t* WO, hipStream_t st) {
-    dim3 grid((unsigned)((K / 32 + 7) / 8), (unsigned)((N + 31) / 32));
+    if (N <= 0) return hipSuccess;
     const bool bf = dtype == MG_BF16;
     const bool tile = layout == MG_W_32X32;
+    const int64_t gx = ((int64_t)K / 8 + 63) / 64;
+    const int64_t units = tile ? ((int64_t)N + 31) / 32 : (int64_t)N;   // rows, or 32-row groups
+    int64_t gy = (units + kFoldWaves - 1) / kFoldWaves;
+    int64_t cap = (int64_t)device_cu_count() * (kFoldWavesPerCU / kFoldWaves) / gx;
+    if (cap < 1) cap = 1;
+    if (gy > cap) gy = cap;
+    if (gy > 65535) gy = 65535;
+    dim3 grid((unsigned)gx, (unsigned)gy);
     if (bf && tile)
         hipLaunchKernelGGL((fold_pack_kernel<true, true>), grid, dim3(256), 0, st, W, N, K, k, s, pos, Wq, Ws, Wst, WO);
     else if (bf)

@@ -46,15 +46,15 @@ __device__ __forceinline__ uint32_t e2m1_nibble(float v, uint32_t c) {
 // IEEE f32 quotient x / s from rcp = RN(1/s) with Markstein's FMA-based
 // correction (P. Markstein, IBM J. Res. Dev. 1990; Muller et al., Handbook of
 // Floating-Point Arithmetic, division with a fused multiply-add): q0 = x*rcp,
-// r = x - q0*s (exact), q = q0 + r*rcp.  The result is the correctly rounded
+// t = q0*s - x (exact), q = q0 - t*rcp.  The result is the correctly rounded
 // quotient when the remainder cannot underflow and the quotient is normal;
-// callers check div_fast_ok() and otherwise divide with __fdiv_rn.  s > 0, so
-// the sign of the quotient is the sign of x (this also keeps -0 / s = -0).
+// callers check the operand ranges (div_fast_ok_*) and otherwise divide with
+// __fdiv_rn.  The remainder is formed as q0*s - x and subtracted, so a zero x
+// keeps its sign (-0 / s = -0) without a separate sign fix-up.
 __device__ __forceinline__ float div_fast(float x, float s, float rcp) {
     const float q0 = x * rcp;
-    const float r = __builtin_fmaf(-q0, s, x);
-    const float q = __builtin_fmaf(r, rcp, q0);
-    return __builtin_copysignf(q, x);
+    const float t = __builtin_fmaf(q0, s, -x);
+    return __builtin_fmaf(-t, rcp, q0);
 }
 
 // Range where div_fast is exact: x == 0 or 2^-100 <= |x| <= 2^100, given a
