@@ -288,3 +288,62 @@ def forward(p: Plan, X: torch.Tensor, act: Act | None = None, Y: torch.Tensor | 
         Y = torch.empty((M, p.desc.N), dtype=torch.bfloat16, device=X.device)
     mg_forward(p, X, act, Y, stream)
     return Y
+
+
+def reference_plan(W: torch.Tensor, stream=None) -> Plan:
+    """A plan that routes every channel through the bf16 branch with no
+    smoothing (k = K, s = 1): forward() then computes the plain bf16 GEMM
+    X W^T with fp32 accumulation -- the unquantized layer."""
+    N, K = W.shape
+    act_max = torch.ones(K, dtype=torch.float32, device=W.device)
+    return plan(act_max, W, 0.5, K, "1x32", smooth=False, stream=stream)
+
+
+@dataclass
+class FFNBlock:
+    """ffn.0 -> GELU-tanh -> ffn.2 with one plan per projection."""
+    plan0: Plan
+    plan2: Plan
+
+
+def ffn_block_stats(calib_batches, W0: torch.Tensor, on_hidden=None, stream=None):
+    """Calibration statistics of both projections of an FFN block from the
+    same batches: ffn.0's from the batches themselves, ffn.2's from the
+    unquantized block's hidden activations h = bf16(gelu(bf16(X W0^T))).
+    `calib_batches` is an iterable of [M][K0] device tensors; `on_hidden(h)`,
+    if given, sees each batch's h.  Returns (act_max0, act_max2)."""
+    K0, N0 = W0.shape[1], W0.shape[0]
+    act0 = torch.empty(K0, dtype=torch.float32, device=W0.device)
+    act2 = torch.empty(N0, dtype=torch.float32, device=W0.device)
+    mg_calib_reset(act0, stream)
+    mg_calib_reset(act2, stream)
+    ref0 = reference_plan(W0, stream)
+    act = y = h = None
+    for X in calib_batches:
+        mg_calib_act(X, act0, stream)
+        if act is None or act.M != X.shape[0]:
+            act = Act.empty(ref0.desc, X.shape[0], X.device)
+            y = torch.empty((X.shape[0], N0), dtype=torch.bfloat16, device=X.device)
+            h = torch.empty_like(y)
+        mg_forward(ref0, X, act, y, stream)
+        mg_gelu_tanh_bf16(y, h, stream)
+        mg_calib_act(h, act2, stream)
+        if on_hidden is not None:
+            on_hidden(h)
+    return act0, act2
+
+
+def ffn_block_plans(act0: torch.Tensor, act2: torch.Tensor, W0: torch.Tensor, W2: torch.Tensor,
+                    alpha0: float, k0: int, alpha2: float, k2: int, layout: str = "1x32",
+                    stream=None) -> FFNBlock:
+    return FFNBlock(plan(act0, W0, alpha0, k0, layout, stream=stream),
+                    plan(act2, W2, alpha2, k2, layout, stream=stream))
+
+
+def ffn_block_forward(blk: FFNBlock, X: torch.Tensor, stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Y2 = ffn.2(gelu(ffn.0(X))); returns (h, Y2)."""
+    y0 = forward(blk.plan0, X, stream=stream)
+    h = torch.empty_like(y0)
+    mg_gelu_tanh_bf16(y0, h, stream)
+    del y0
+    return h, forward(blk.plan2, h, stream=stream)
