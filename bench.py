@@ -13,6 +13,12 @@ Prints ONE JSON line.  `value` = 2*M*K*N / (time of one whole step), in
 TFLOP/s; the dual-GEMM kernel's own rate is in `roofline`.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py --suite      one JSON line per configuration point: the
+                                 480p up/down-projections, the 720p (k, alpha)
+                                 sweep and the 720p FFN block (both weight-scale
+                                 layouts), each with kernel rates (warm, and the
+                                 GEMM also cold) and the fidelity of the three
+                                 modes against the unquantized float64 layer
 """
 from __future__ import annotations
 
@@ -119,6 +125,198 @@ def summarize_pmc(fetch_csv: str, write_csv: str, out_json: str) -> dict:
     return res
 
 
+# ----------------------------------------------------------------------------- suite
+
+FID_ROWS = 64
+COLD_BYTES = 1 << 30      # written between cold timings: evicts the L2s and the 256 MB MALL
+
+
+def _suite_tools():
+    import numpy as np
+    import torch
+
+    import mixed_gemm_amd as mg
+    import synth
+
+    stream = torch.cuda.current_stream()
+    scratch = torch.empty(COLD_BYTES // 4, dtype=torch.float32, device="cuda")
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    def to_f64(a):
+        a = np.asarray(a)
+        return (synth.bf16_bits_to_f32(a) if a.dtype == np.uint16 else a).astype(np.float64)
+
+    def y_host(t):
+        return t.view(torch.int16).cpu().numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.cpu().numpy()
+
+    def timed(fn, reps=10, warmup=2, cold=False):
+        """mean ms of fn() over reps launches, HIP events on the current stream;
+        cold: a 1 GiB write before each launch, outside the timed interval."""
+        for _ in range(warmup):
+            fn()
+        ts = []
+        for _ in range(reps):
+            if cold:
+                scratch.fill_(1.0)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.mean(ts))
+
+    def rel_fro(Y, Yref):
+        return float(np.linalg.norm(to_f64(Y) - Yref) / np.linalg.norm(Yref))
+
+    return np, torch, mg, synth, dev, to_f64, y_host, timed, rel_fro
+
+
+def _emit(d):
+    print(json.dumps(d), flush=True)
+
+
+def suite(args) -> int:
+    np, torch, mg, synth, dev, to_f64, y_host, timed, rel_fro = _suite_tools()
+    torch.cuda.set_device(0)
+    g = np.random.default_rng(12345)
+
+    def layer_point(w, X_h, W_h, Xd, Wd, points, layout="1x32"):
+        """Timings + fidelity of one layer for each (k, alpha) in points."""
+        M, K, N = X_h.shape[0], w.K, w.N
+        bf = w.dtype == "bf16"
+        act_max = torch.empty(K, dtype=torch.float32, device="cuda")
+        w_max = torch.empty(K, dtype=torch.float32, device="cuda")
+
+        def calib():
+            mg.mg_calib_reset(act_max)
+            mg.mg_calib_act(Xd, act_max)
+        t_calib = timed(calib)
+        t_wr = timed(lambda: mg.mg_weight_range(Wd, w_max))
+        rows = np.arange(M) if M <= FID_ROWS else np.sort(g.choice(M, FID_ROWS, replace=False))
+        Xs = Xd[torch.from_numpy(rows).cuda()].contiguous()
+        Yref = to_f64(X_h[rows]) @ to_f64(W_h).T
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+        def fidelity(k, alpha, smooth):
+            p = mg.Plan.empty(mg.make_desc(K, N, k, alpha, layout, smooth))
+            mg.mg_plan_build(p, act_max, w_max, Wd)
+            return rel_fro(y_host(mg.forward(p, Xs)), Yref)
+
+        uniform = fidelity(0, 0.5, False)
+        smooth_only = {}
+        for k, alpha in points:
+            desc = mg.make_desc(K, N, k, alpha, layout, True)
+            p = mg.Plan.empty(desc)
+            t_plan = timed(lambda: mg.mg_plan_build(p, act_max, w_max, Wd))
+            a = mg.Act.empty(desc, M)
+            t_quant = timed(lambda: mg.mg_quantize_act(p, Xd, a))
+            t_gemm = timed(lambda: mg.mg_dual_gemm(p, a, Y))
+            t_gemm_cold = timed(lambda: mg.mg_dual_gemm(p, a, Y), reps=5, warmup=1, cold=True)
+            if alpha not in smooth_only:
+                smooth_only[alpha] = fidelity(0, alpha, True)
+            fl = 2.0 * M * K * N
+            xb = 2 if bf else 4
+            quant_bytes = M * K * xb + M * K // 2 + M * K // 32 + 2 * M * k
+            pack_bytes = N * K * xb + N * K // 2 + N * K // 32 + 2 * N * k
+            _emit({"suite": "dual-branch W4A4 layer",
+                   "config": {"workload": w.name, "M": M, "K": K, "N": N, "k": k, "alpha": alpha,
+                              "weight_blocks": layout, "output": "bf16"},
+                   "gemm_ms": round(t_gemm, 4), "gemm_tflops": round(fl / t_gemm / 1e9, 1),
+                   "gemm_pct_mxfp4_peak": round(100 * fl / t_gemm / 1e9 / PEAK_FP4_TFLOPS, 2),
+                   "gemm_ms_cold": round(t_gemm_cold, 4),
+                   "gemm_tflops_cold": round(fl / t_gemm_cold / 1e9, 1),
+                   "quant_ms": round(t_quant, 4), "quant_gbs": round(quant_bytes / t_quant / 1e6, 1),
+                   "quant_pct_hbm": round(100 * quant_bytes / t_quant / 1e6 / PEAK_HBM_GBS, 2),
+                   "calib_ms": round(t_calib, 4), "calib_gbs": round(M * K * xb / t_calib / 1e6, 1),
+                   "weight_range_ms": round(t_wr, 4),
+                   "plan_ms": round(t_plan, 4), "plan_gbs": round(pack_bytes / t_plan / 1e6, 1),
+                   "fidelity_rel_fro": {"uniform": round(uniform, 5),
+                                        "smooth_only": round(smooth_only[alpha], 5),
+                                        "smooth_split": round(fidelity(k, alpha, True), 5)},
+                   "fidelity_rows": int(rows.size)})
+            del a
+        del Y
+
+    def layer_config(w, points, layouts=("1x32",)):
+        X_h, W_h = w.make_x(), w.make_w()
+        Xd, Wd = dev(X_h), dev(W_h)
+        for lay in layouts:
+            layer_point(w, X_h, W_h, Xd, Wd, points, lay)
+        del Xd, Wd
+        torch.cuda.empty_cache()
+
+    layer_config(synth.TINY, [(synth.TINY.k, synth.TINY.alpha)])
+    layer_config(synth.FFN0_480P, [(synth.FFN0_480P.k, synth.FFN0_480P.alpha)], ("1x32", "32x32"))
+    layer_config(synth.FFN2_480P, [(synth.FFN2_480P.k, synth.FFN2_480P.alpha)])
+    layer_config(synth.FFN0_720P, [(k, a) for a in synth.SWEEP_ALPHA for k in synth.SWEEP_K])
+
+    # ---- the 720p FFN block
+    w0, w2, M = synth.BLOCK_FFN0, synth.BLOCK_FFN2, synth.BLOCK_M
+    W0_h, W2_h = w0.make_w(), w2.make_w()
+    W0d, W2d = dev(W0_h), dev(W2_h)
+    Xcal = [dev(w0.make_x(M=M, x_seed=sd)) for sd in synth.BLOCK_CALIB_SEEDS]
+    act0, act2 = mg.ffn_block_stats(Xcal, W0d)
+    del Xcal
+    torch.cuda.empty_cache()
+    X5_h = w0.make_x(M=M, x_seed=synth.BLOCK_EVAL_SEED)
+    X5 = dev(X5_h)
+    rows = np.sort(g.choice(M, FID_ROWS, replace=False))
+    Xs = X5[torch.from_numpy(rows).cuda()].contiguous()
+    z = to_f64(X5_h[rows]) @ to_f64(W0_h).T
+    c = float(np.sqrt(2.0 / np.pi))
+    href = 0.5 * z * (1.0 + np.tanh(c * (z + 0.044715 * z ** 3)))     # float64 GELU-tanh
+    Yref = href @ to_f64(W2_h).T
+    for lay in ("1x32", "32x32"):
+        def block_fid(k0, a0, k2, a2, smooth):
+            p0 = mg.Plan.empty(mg.make_desc(w0.K, w0.N, k0, a0, lay, smooth))
+            p2 = mg.Plan.empty(mg.make_desc(w2.K, w2.N, k2, a2, lay, smooth))
+            for p, am, Wd_ in ((p0, act0, W0d), (p2, act2, W2d)):
+                wm = torch.empty(p.desc.K, dtype=torch.float32, device="cuda")
+                mg.mg_weight_range(Wd_, wm)
+                mg.mg_plan_build(p, am, wm, Wd_)
+            _, y = mg.ffn_block_forward(mg.FFNBlock(p0, p2), Xs)
+            return rel_fro(y_host(y), Yref)
+        blk = mg.ffn_block_plans(act0, act2, W0d, W2d, w0.alpha, w0.k, w2.alpha, w2.k, lay)
+        a0 = mg.Act.empty(blk.plan0.desc, M)
+        a2 = mg.Act.empty(blk.plan2.desc, M)
+        Y0 = torch.empty((M, w0.N), dtype=torch.bfloat16, device="cuda")
+        h = torch.empty_like(Y0)
+        Y2 = torch.empty((M, w2.N), dtype=torch.bfloat16, device="cuda")
+
+        def run_block():
+            mg.mg_forward(blk.plan0, X5, a0, Y0)
+            mg.mg_gelu_tanh_bf16(Y0, h)
+            mg.mg_forward(blk.plan2, h, a2, Y2)
+        t_block = timed(run_block, reps=5)
+        t_g0 = timed(lambda: mg.mg_dual_gemm(blk.plan0, a0, Y0))
+        t_gelu = timed(lambda: mg.mg_gelu_tanh_bf16(Y0, h))
+        t_q2 = timed(lambda: mg.mg_quantize_act(blk.plan2, h, a2))
+        t_g2 = timed(lambda: mg.mg_dual_gemm(blk.plan2, a2, Y2))
+        fl0, fl2 = 2.0 * M * w0.K * w0.N, 2.0 * M * w2.K * w2.N
+        _emit({"suite": "dual-branch W4A4 layer",
+               "config": {"workload": "ffn_block_720p_75600x5120x13824x5120", "M": M, "k": [w0.k, w2.k],
+                          "alpha": [w0.alpha, w2.alpha], "weight_blocks": lay, "output": "bf16"},
+               "block_ms": round(t_block, 4), "block_tflops": round((fl0 + fl2) / t_block / 1e9, 1),
+               "ffn0_gemm_tflops": round(fl0 / t_g0 / 1e9, 1), "ffn2_gemm_tflops": round(fl2 / t_g2 / 1e9, 1),
+               "gelu_ms": round(t_gelu, 4), "gelu_gbs": round(4 * M * w0.N / t_gelu / 1e6, 1),
+               "ffn2_quant_ms": round(t_q2, 4),
+               "ffn2_quant_gbs": round((M * w2.K * 2.53125 + 2 * M * w2.k) / t_q2 / 1e6, 1),
+               "fidelity_rel_fro": {"uniform": round(block_fid(0, 0.5, 0, 0.5, False), 5),
+                                    "smooth_only": round(block_fid(0, w0.alpha, 0, w2.alpha, True), 5),
+                                    "smooth_split": round(block_fid(w0.k, w0.alpha, w2.k, w2.alpha, True), 5)},
+               "fidelity_rows": int(rows.size)})
+        del a0, a2, Y0, h, Y2, blk
+        torch.cuda.empty_cache()
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,12 +327,16 @@ def main() -> int:
     ap.add_argument("--cpu-rows", type=int, default=256)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run a plain device copy of 256 MiB (HBM counter calibration)")
+    ap.add_argument("--suite", action="store_true",
+                    help="one JSON line per configuration point (see the module docstring)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the dual-GEMM traffic summary from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
     if args.summarize_pmc:
         print(json.dumps(summarize_pmc(*args.summarize_pmc, TRAFFIC_FILE)))
         return 0
+    if args.gpus == 1 and args.suite:
+        return suite(args)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the layer shards along tokens with no exchange in the forward pass)", file=sys.stderr)

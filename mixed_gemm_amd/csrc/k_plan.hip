@@ -34,22 +34,22 @@ __global__ void __launch_bounds__(256) smooth_kernel(const float* __restrict__ a
 
 constexpr int kTopkThreads = 1024;
 
-// Block-wide inclusive scan of one value per thread (Hillis-Steele in LDS).
+// Block-wide inclusive scan of one value per thread: a shuffle scan inside
+// each wave, then the wave totals (through LDS) added on.
 __device__ int block_inclusive_scan(int v, int* buf) {
-    const int t = threadIdx.x;
-    buf[t] = v;
-    __syncthreads();
-    for (int off = 1; off < kTopkThreads; off <<= 1) {
-        int add = t >= off ? buf[t - off] : 0;
-        __syncthreads();
-        buf[t] += add;
-        __syncthreads();
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(v, o, 64);
+        if (lane >= o) v += u;
     }
-    int r = buf[t];
+    if (lane == 63) buf[w] = v;
     __syncthreads();
-    return r;
+    int add = 0;
+    for (int i = 0; i < w; ++i) add += buf[i];
+    __syncthreads();                  // buf is free again for the next scan
+    return v + add;
 }
-
 
 // One workgroup.  Scores are non-negative floats, compared through their bit
 // patterns (same order).  T = the k-th largest score is found by an MSB-first
@@ -82,15 +82,14 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const float* __restr
                 if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
             }
             __syncthreads();
-            if (t == 0) {
-                // the bin holding the remaining-th largest key, counted from the top
-                int above = 0, b = 255;
-                for (; b > 0; --b) {
-                    if (above + hist[b] >= remaining) break;
-                    above += hist[b];
-                }
-                sel[0] = (uint32_t)b;
-                sel[1] = (uint32_t)(remaining - above);
+            // the bin holding the remaining-th largest key: counts from the top
+            // bin down (thread t < 256 takes bin 255 - t), then the thread whose
+            // running count first reaches `remaining` records it
+            const int hv = t < 256 ? hist[255 - t] : 0;
+            const int incl = block_inclusive_scan(hv, buf);
+            if (t < 256 && incl - hv < remaining && incl >= remaining) {
+                sel[0] = (uint32_t)(255 - t);
+                sel[1] = (uint32_t)(remaining - (incl - hv));
             }
             __syncthreads();
             prefix |= sel[0] << shift;
@@ -163,15 +162,23 @@ __global__ void __launch_bounds__(256) fold_pack_kernel(const void* __restrict__
     const int j0 = (blockIdx.x * 64 + lane) * 8;
     const bool valid = j0 < K;                       // whole quads agree (K % 32 == 0)
     const int nb = K / 32;
-    float sv[8];
+    float sv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int pv[8] = {-1, -1, -1, -1, -1, -1, -1, -1};
+    if (valid) {                                     // j0 is a multiple of 8: 16-byte loads
+#pragma unroll
+        for (int h4 = 0; h4 < 2; ++h4) {
+            const float4 a = *reinterpret_cast<const float4*>(s + j0 + 4 * h4);
+            const int4 c = *reinterpret_cast<const int4*>(pos + j0 + 4 * h4);
+            sv[4 * h4] = a.x; sv[4 * h4 + 1] = a.y; sv[4 * h4 + 2] = a.z; sv[4 * h4 + 3] = a.w;
+            pv[4 * h4] = c.x; pv[4 * h4 + 1] = c.y; pv[4 * h4 + 2] = c.z; pv[4 * h4 + 3] = c.w;
+        }
+    }
     uint32_t keep[8];
     uint32_t omask = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        sv[i] = valid ? s[j0 + i] : 0.0f;
-        const int p = valid ? pos[j0 + i] : -1;
-        keep[i] = p >= 0 ? 0u : 0xFFFFFFFFu;
-        omask |= (p >= 0 ? 1u : 0u) << i;
+        keep[i] = pv[i] >= 0 ? 0u : 0xFFFFFFFFu;
+        omask |= (pv[i] >= 0 ? 1u : 0u) << i;
     }
 
     // RN(s * W) of the lane's 8 channels of row n (zeros when out of range)
@@ -208,7 +215,10 @@ __global__ void __launch_bounds__(256) fold_pack_kernel(const void* __restrict__
                 float fi = f[0];
 #pragma unroll
                 for (int t = 1; t < 8; ++t) fi = i == t ? f[t] : fi;
-                WO[n * k + pos[j0 + i]] = (uint16_t)f32_to_bf16_rne(fi);
+                int pi = pv[0];
+#pragma unroll
+                for (int t = 1; t < 8; ++t) pi = i == t ? pv[t] : pi;
+                WO[n * k + pi] = (uint16_t)f32_to_bf16_rne(fi);
             }
         }
         float amax = 0.0f;

@@ -93,15 +93,25 @@ __global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restr
     // Whole 32-blocks are either in range or not (K % 32 == 0), so the 4 lanes
     // of a quad agree on `valid` and the quad reduction mixes one block only.
     const bool valid = j0 < K;
-    float sv[8], rv[8];
+    // the lane's 8 channels: three pairs of 16-byte loads (j0 is a multiple of 8)
+    float sv[8] = {1, 1, 1, 1, 1, 1, 1, 1}, rv[8] = {1, 1, 1, 1, 1, 1, 1, 1};
+    int pv[8] = {-1, -1, -1, -1, -1, -1, -1, -1};
+    if (valid) {
+#pragma unroll
+        for (int h4 = 0; h4 < 2; ++h4) {
+            const float4 a = *reinterpret_cast<const float4*>(s + j0 + 4 * h4);
+            const float4 b = *reinterpret_cast<const float4*>(rcp + j0 + 4 * h4);
+            const int4 c = *reinterpret_cast<const int4*>(pos + j0 + 4 * h4);
+            sv[4 * h4] = a.x; sv[4 * h4 + 1] = a.y; sv[4 * h4 + 2] = a.z; sv[4 * h4 + 3] = a.w;
+            rv[4 * h4] = b.x; rv[4 * h4 + 1] = b.y; rv[4 * h4 + 2] = b.z; rv[4 * h4 + 3] = b.w;
+            pv[4 * h4] = c.x; pv[4 * h4 + 1] = c.y; pv[4 * h4 + 2] = c.z; pv[4 * h4 + 3] = c.w;
+        }
+    }
     uint32_t omask = 0;
     bool s_ok = true;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        sv[i] = valid ? s[j0 + i] : 1.0f;
-        rv[i] = valid ? rcp[j0 + i] : 1.0f;
-        const int p = valid ? pos[j0 + i] : -1;
-        omask |= (p >= 0 ? 1u : 0u) << i;
+        omask |= (pv[i] >= 0 ? 1u : 0u) << i;
         s_ok &= div_fast_ok_s(sv[i]);
     }
     // keep masks of the input words (outlier channels -> +0 in the bulk)
@@ -112,12 +122,13 @@ __global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restr
     // The first outlier channel of the lane (if any) is written with one store
     // per row; further outlier channels of the same lane (rare) take a loop.
     const int oc0 = omask ? __builtin_ctz(omask) : 0;
-    const int op0 = omask ? pos[j0 + oc0] : 0;
     float so = sv[0], ro = rv[0];
+    int op0 = pv[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) {
         so = oc0 == i ? sv[i] : so;
         ro = oc0 == i ? rv[i] : ro;
+        op0 = oc0 == i ? pv[i] : op0;
     }
     const uint32_t omask_rest = omask & (omask - 1);
 
