@@ -94,16 +94,31 @@ def outlier_set(a: np.ndarray, k: int) -> tuple[np.ndarray, np.ndarray]:
     return O, pos
 
 
+def outlier_score(a: np.ndarray, s: np.ndarray, mode: str = "max") -> np.ndarray:
+    """The per-channel score Eq. (4) ranks.  "max": the calibration maximum
+    a_j (Eq. (4) as written).  "smoothed": the maximum of the smoothed
+    activations, max_t |x_tj / s_j| = RN32(a_j / s_j) (RN is monotone), i.e.
+    the channels that stay largest after the fold (the reading in which the
+    split follows the smoothing)."""
+    if mode == "max":
+        return a.astype(np.float32)
+    if mode == "smoothed":
+        return (a.astype(np.float32) / s.astype(np.float32)).astype(np.float32)
+    raise ValueError(mode)
+
+
 def fold_pack(W: np.ndarray, s: np.ndarray, O: np.ndarray, layout: str = "1x32") -> dict:
     """Eq. (1) fold and the block packing of the weights.
 
     W' = RN_f32(s_j * W[n][j]) (s folded into the master weights before
     packing); the outlier columns W'[:, O] are extracted to bf16 (WO [N][k]);
     the bulk weights are W' with the O columns set to +0 (masked in place,
-    keeping 32-block alignment) and MXFP4-encoded with 1x32 K-blocks or
-    32x32 tiles.  Returns Wq [N][K/2], Ws [N][K/32] (per-row codes; for tiles
-    the tile code repeated over its 32 rows), Wst [N/32][K/32] (tiles only),
-    WO [N][k]."""
+    keeping 32-block alignment) and MXFP4-encoded with 1x32 K-blocks, 32x32
+    tiles or 128x1 K-major stripes (the block-packing paragraph and Fig. 8 of
+    the paper's text).  Returns Wq [N][K/2], Ws [N][K/32] (per-block codes; for
+    tiles the tile code repeated over its 32 rows, for stripes the stripe code
+    repeated over its 4 blocks), Wst (the compact codes: [N/32][K/32] for tiles,
+    [N][ceil(K/128)] for stripes; None for 1x32), WO [N][k]."""
     Wf = (as_f32(W) * s[None, :].astype(np.float32)).astype(np.float32)
     WO = bf16_rne(Wf[:, O]) if O.size else np.zeros((W.shape[0], 0), np.uint16)
     WB = Wf.copy()
@@ -113,15 +128,17 @@ def fold_pack(W: np.ndarray, s: np.ndarray, O: np.ndarray, layout: str = "1x32")
         Wst = None
     elif layout == "32x32":
         Wq, Ws, Wst = mxfp4.encode_tiles(WB)
+    elif layout == "128x1":
+        Wq, Ws, Wst = mxfp4.encode_stripes(WB, 128)
     else:
         raise ValueError(layout)
     return dict(Wq=Wq, Ws=Ws, Wst=Wst, WO=WO)
 
 
 def plan(a: np.ndarray, w: np.ndarray, W: np.ndarray, alpha: float, k: int,
-         layout: str = "1x32", smooth: bool = True) -> dict:
+         layout: str = "1x32", smooth: bool = True, score: str = "max") -> dict:
     s, rcp = smooth_scales(a, w, alpha, smooth)
-    O, pos = outlier_set(a, k)
+    O, pos = outlier_set(outlier_score(a, s, score), k)
     p = dict(s=s, rcp=rcp, O=O, pos=pos)
     p.update(fold_pack(W, s, O, layout))
     return p

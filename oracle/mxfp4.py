@@ -112,6 +112,23 @@ def encode_tiles(v: np.ndarray) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
     return pack_nibbles(nib), c_rows, ct
 
 
+def encode_stripes(v: np.ndarray, width: int = 128) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """K-major stripes of `width` consecutive K of one row (the 128x1 layout;
+    the last stripe of a row may be shorter).  [R][K] f32 -> (packed [R][K/2]
+    u8, per-block scales [R][K/32] u8 = the stripe's code on each of its
+    32-blocks, compact stripe scales [R][ceil(K/width)] u8)."""
+    v = np.asarray(v, dtype=np.float32)
+    R, K = v.shape
+    assert K % BLOCK == 0 and width % BLOCK == 0
+    ns = -(-K // width)
+    pad = ns * width - K
+    a = np.abs(np.pad(v, ((0, 0), (0, pad)))).reshape(R, ns, width).max(axis=2)
+    cs = e8m0_from_amax(a)
+    c_blocks = np.repeat(cs, width // BLOCK, axis=1)[:, :K // BLOCK]
+    nib = encode_with_scale(v, np.repeat(c_blocks, BLOCK, axis=1))
+    return pack_nibbles(nib), c_blocks, cs
+
+
 def decode_rows(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """(packed [R][K/2], scales [R][K/32]) -> exact float64 [R][K]."""
     nib = unpack_nibbles(packed)

@@ -308,3 +308,46 @@ def test_quantize_uses_division_not_reciprocal_product():
         assert int(r["As"][0, 0]) == 127
         assert int(mxfp4.unpack_nibbles(r["Aq"])[0, 1]) == even_code, t
     assert found >= 3
+
+
+def test_fold_pack_stripes_match_rows_on_uniform_stripes():
+    """When all four 32-blocks of every 128-stripe have the same amax, the
+    128x1 stripe codes equal the 1x32 codes and the nibbles agree; Wst holds
+    one code per row and stripe."""
+    N, K = 8, 256
+    g = np.random.default_rng(17)
+    W = g.uniform(-0.5, 0.5, (N, K)).astype(np.float32)
+    W[:, ::32] = 0.5
+    s = np.ones(K, np.float32)
+    O = np.zeros(0, np.int32)
+    r1 = layer.fold_pack(W, s, O, "1x32")
+    r2 = layer.fold_pack(W, s, O, "128x1")
+    assert np.array_equal(r1["Wq"], r2["Wq"]) and np.array_equal(r1["Ws"], r2["Ws"])
+    assert r2["Wst"].shape == (N, 2) and np.all(r2["Wst"] == r1["Ws"][:, ::4])
+
+
+def test_smoothed_score_ranks_by_product():
+    """With smoothing, a_j / s_j = (a_j w_j)^(1 - alpha) (Eq. (2)), a monotone
+    function of a_j w_j: the smoothed-score top-k is the top-k of a_j w_j
+    (values spread far apart, so f32 rounding cannot reorder them).  With
+    smoothing off the smoothed score is the raw score."""
+    K, k = 40, 7
+    g = np.random.default_rng(5)
+    rank = g.permutation(K)
+    a = (np.exp(g.uniform(-2, 3, K))).astype(np.float32)
+    w = (1.5 ** (rank - 30.0) / a).astype(np.float32)            # products a_j w_j ~ 1.5^rank_j
+    prod = a.astype(np.float64) * w.astype(np.float64)
+    order = np.argsort(-prod)
+    assert np.all(np.diff(prod[order]) < -0.3 * prod[order][1:])      # well separated
+    for alpha in (0.3, 0.5, 0.7):
+        s, _ = layer.smooth_scales(a, w, alpha)
+        O, _ = layer.outlier_set(layer.outlier_score(a, s, "smoothed"), k)
+        assert np.array_equal(O, np.sort(order[:k]))
+    s1, _ = layer.smooth_scales(a, w, 0.5, smooth=False)
+    assert np.array_equal(layer.outlier_score(a, s1, "smoothed"), a)
+    # the score is the largest smoothed activation of the channel
+    X = (g.standard_normal((50, K)) * a[None, :]).astype(np.float32)
+    a_x = layer.act_max(X)
+    s, _ = layer.smooth_scales(a_x, w, 0.6)
+    q = layer.as_f32(X) / s[None, :]
+    assert np.array_equal(layer.outlier_score(a_x, s, "smoothed"), np.abs(q).max(axis=0).astype(np.float32))

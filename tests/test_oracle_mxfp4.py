@@ -128,3 +128,30 @@ def test_tile_scales_cover_32x32():
     # a 1x32 encode of the same matrix differs only where the tile scale is coarser
     p1, s1 = mxfp4.encode_rows(v)
     assert np.all(s1 <= c_rows)
+
+
+def test_stripe_scales_128x1():
+    """128x1 K-major stripes: one E8M0 per 128 consecutive K of a row.  Pins:
+    the stripe code is the E8M0 of the stripe's amax computed independently
+    (frexp), it equals the largest of the stripe's four 1x32 codes (E8M0 is
+    monotone in the amax), the last (short) stripe of a ragged row covers only
+    its own blocks, and decoding loses at most the grid spacing of the
+    stripe's scale."""
+    g = np.random.default_rng(21)
+    v = (g.standard_normal((5, 352)) * 0.2).astype(np.float32)     # K = 352: stripes 128, 128, 96
+    v[2, 200] = 40.0
+    v[4, 340] = -9.0
+    packed, c_blocks, cs = mxfp4.encode_stripes(v, 128)
+    assert cs.shape == (5, 3) and c_blocks.shape == (5, 11)
+    _, s1 = mxfp4.encode_rows(v)
+    for r in range(5):
+        for sidx in range(3):
+            seg = v[r, sidx * 128:min(352, (sidx + 1) * 128)]
+            m, e = math.frexp(float(np.abs(seg).max()))       # amax = m 2^e, 0.5 <= m < 1
+            assert cs[r, sidx] == max(e - 1 - 2 + 127, 0)
+            blocks = range(sidx * 4, min(11, sidx * 4 + 4))
+            assert cs[r, sidx] == max(int(s1[r, b]) for b in blocks)
+            assert all(c_blocks[r, b] == cs[r, sidx] for b in blocks)
+    dec = mxfp4.decode_rows(packed, c_blocks)
+    step = np.repeat(np.exp2(c_blocks.astype(np.float64) - 127), 32, axis=1)   # grid spacing <= 2 x 2^(c-127)
+    assert np.all(np.abs(dec - v) <= np.maximum(step, np.abs(v) / 4) + 1e-30)
