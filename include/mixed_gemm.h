@@ -52,19 +52,29 @@ typedef enum {
 
 typedef enum { MG_F32 = 0, MG_BF16 = 1 } mg_dtype;
 
-/* Weight block-scale layout (the block-packing paragraph after Eq. (5)):
+/* Weight block-scale layout (the block-packing paragraph after Eq. (5) and
+ * its Fig. 8):
  * MG_W_1X32   one E8M0 per (output row n, 32 consecutive K);
- * MG_W_32X32  one E8M0 per aligned tile of 32 output rows x 32 K (requires N % 32 == 0). */
-typedef enum { MG_W_1X32 = 0, MG_W_32X32 = 1 } mg_wlayout;
+ * MG_W_32X32  one E8M0 per aligned tile of 32 output rows x 32 K (requires N % 32 == 0);
+ * MG_W_128X1  one E8M0 per K-major stripe of 128 consecutive K of one output
+ *             row (the last stripe of a row covers the remaining K when
+ *             K % 128 != 0). */
+typedef enum { MG_W_1X32 = 0, MG_W_32X32 = 1, MG_W_128X1 = 2 } mg_wlayout;
+
+/* Score the outlier set of Eq. (4) ranks:
+ * MG_SCORE_MAX       the calibration maximum a_j = max_t |x_tj| (Eq. (4) as written);
+ * MG_SCORE_SMOOTHED  the smoothed maximum max_t |x_tj / s_j| = RN(a_j / s_j). */
+typedef enum { MG_SCORE_MAX = 0, MG_SCORE_SMOOTHED = 1 } mg_score;
 
 /* Plan descriptor.  K, N: input / output widths (multiples of 32, K <= 65536);
  * k: number of outlier columns, 0 <= k <= K; layout: mg_wlayout;
- * smooth: 1 to apply Eq. (2) with alpha in (0, 1), 0 for s = 1. */
+ * smooth: 1 to apply Eq. (2) with alpha in (0, 1), 0 for s = 1;
+ * score: mg_score. */
 typedef struct {
     int32_t K, N, k;
     int32_t layout;
     int32_t smooth;
-    int32_t reserved;   /* must be 0 */
+    int32_t score;
     double alpha;
 } mg_plan_desc;
 
@@ -76,8 +86,11 @@ typedef struct {
  *  Wq  [N][K/2]   u8   MXFP4 payload of the folded bulk weights RN(s_j W[n][j]),
  *                      outlier columns set to +0 before encoding;
  *  Ws  [N][K/32]  u8   E8M0 scale of each (row, 32-block) -- for MG_W_32X32 the
- *                      tile's code repeated on each of its 32 rows;
- *  Wst [N/32][K/32] u8 compact tile codes (MG_W_32X32 only; null allowed otherwise);
+ *                      tile's code repeated on each of its 32 rows, for
+ *                      MG_W_128X1 the stripe's code on each of its 32-blocks;
+ *  Wst                 compact codes: [N/32][K/32] u8 tile codes (MG_W_32X32),
+ *                      [N][ceil(K/128)] u8 stripe codes (MG_W_128X1); null
+ *                      allowed for MG_W_1X32;
  *  WO  [N][k]     bf16 folded outlier columns (null allowed when k == 0). */
 typedef struct {
     mg_plan_desc d;
@@ -134,8 +147,10 @@ int mg_weight_range(const void* W, int32_t dtype, int32_t N, int32_t K, float* w
 int mg_smooth_scales(const mg_plan* p, const float* act_max, const float* w_max,
                      hipStream_t stream);
 
-/* Eq. (4): O = the k channels first in the order (act_max desc, index asc),
- * stored ascending, and pos. */
+/* Eq. (4): O = the k channels first in the order (score desc, index asc),
+ * stored ascending, and pos.  The score is act_max (MG_SCORE_MAX) or
+ * RN(act_max / s) (MG_SCORE_SMOOTHED, which reads p->s: call
+ * mg_smooth_scales first). */
 int mg_outlier_set(const mg_plan* p, const float* act_max, hipStream_t stream);
 
 /* Eq. (1) fold + extraction + block packing of W [N][K] (dtype MG_F32 or

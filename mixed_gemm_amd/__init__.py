@@ -22,8 +22,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmixed_gemm.so")
 
 MG_F32, MG_BF16 = 0, 1
-MG_W_1X32, MG_W_32X32 = 0, 1
-LAYOUTS = {"1x32": MG_W_1X32, "32x32": MG_W_32X32}
+MG_W_1X32, MG_W_32X32, MG_W_128X1 = 0, 1, 2
+LAYOUTS = {"1x32": MG_W_1X32, "32x32": MG_W_32X32, "128x1": MG_W_128X1}
+MG_SCORE_MAX, MG_SCORE_SMOOTHED = 0, 1
+SCORES = {"max": MG_SCORE_MAX, "smoothed": MG_SCORE_SMOOTHED}
 
 STATUS = {0: "MG_OK", -1: "MG_ERR_ARG", -2: "MG_ERR_SHAPE", -3: "MG_ERR_DTYPE", -4: "MG_ERR_ALIGN",
           -5: "MG_ERR_UNSUPPORTED", -6: "MG_ERR_HIP"}
@@ -37,7 +39,7 @@ class MGError(RuntimeError):
 
 class mg_plan_desc(ctypes.Structure):
     _fields_ = [("K", ctypes.c_int32), ("N", ctypes.c_int32), ("k", ctypes.c_int32),
-                ("layout", ctypes.c_int32), ("smooth", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("layout", ctypes.c_int32), ("smooth", ctypes.c_int32), ("score", ctypes.c_int32),
                 ("alpha", ctypes.c_double)]
 
 
@@ -126,9 +128,10 @@ def _dtype(t: torch.Tensor) -> int:
 # ----------------------------------------------------------------------------- plan / workspace
 
 def make_desc(K: int, N: int, k: int, alpha: float = 0.5, layout: str | int = "1x32",
-              smooth: bool = True) -> mg_plan_desc:
+              smooth: bool = True, score: str | int = "max") -> mg_plan_desc:
     lay = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
-    return mg_plan_desc(int(K), int(N), int(k), lay, int(bool(smooth)), 0, float(alpha))
+    sc = SCORES[score] if isinstance(score, str) else int(score)
+    return mg_plan_desc(int(K), int(N), int(k), lay, int(bool(smooth)), sc, float(alpha))
 
 
 def mg_plan_bytes(desc: mg_plan_desc) -> list[int]:
@@ -161,9 +164,9 @@ class Plan:
         b = mg_plan_bytes(desc)
         K, N, k = desc.K, desc.N, desc.k
         e = lambda n, dt: torch.empty(n, dtype=dt, device=device)
+        wst = {MG_W_32X32: (N // 32, K // 32), MG_W_128X1: (N, (K + 127) // 128)}.get(desc.layout, 0)
         return Plan(desc, e(K, torch.float32), e(K, torch.float32), e(k, torch.int32), e(K, torch.int32),
-                    e((N, K // 2), torch.uint8), e((N, K // 32), torch.uint8),
-                    e((N // 32, K // 32), torch.uint8) if b[6] else e(0, torch.uint8),
+                    e((N, K // 2), torch.uint8), e((N, K // 32), torch.uint8), e(wst, torch.uint8),
                     e((N, k), torch.bfloat16))
 
     def c(self) -> mg_plan:
@@ -268,10 +271,10 @@ def calibrate(batches, K: int, device="cuda", stream=None) -> torch.Tensor:
 
 
 def plan(act_max: torch.Tensor, W: torch.Tensor, alpha: float, k: int, layout: str = "1x32",
-         smooth: bool = True, stream=None) -> Plan:
+         smooth: bool = True, stream=None, score: str = "max") -> Plan:
     """calibrated maxima + weights -> a built plan (weight ranges, Eq. (2), Eq. (4), fold + pack)."""
     N, K = W.shape
-    desc = make_desc(K, N, k, alpha, layout, smooth)
+    desc = make_desc(K, N, k, alpha, layout, smooth, score)
     p = Plan.empty(desc, W.device)
     w_max = torch.empty(K, dtype=torch.float32, device=W.device)
     mg_weight_range(W, w_max, stream)

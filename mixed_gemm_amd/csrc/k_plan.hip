@@ -51,19 +51,22 @@ __device__ int block_inclusive_scan(int v, int* buf) {
     return v + add;
 }
 
-// One workgroup.  Scores are non-negative floats, compared through their bit
-// patterns (same order).  T = the k-th largest score is found by an MSB-first
+// One workgroup.  Scores -- a_j, or RN(a_j / s_j) for the smoothed score --
+// are non-negative floats, compared through their bit patterns (same order).  T = the k-th largest score is found by an MSB-first
 // radix select, 8 bits per pass with a 256-bin histogram in LDS; channels above
 // T are in O, and of the channels equal to T the lowest indices fill the
 // remaining places (tie rule: index ascending).  Thread t owns the contiguous
 // index range [t*C, (t+1)*C) so block scans give ascending order directly.
-__global__ void __launch_bounds__(kTopkThreads) topk_kernel(const float* __restrict__ a, int32_t K,
+__global__ void __launch_bounds__(kTopkThreads) topk_kernel(const float* __restrict__ a,
+                                                            const float* __restrict__ s, int32_t K,
                                                             int32_t k, int32_t* __restrict__ O,
                                                             int32_t* __restrict__ pos) {
     __shared__ int buf[kTopkThreads];
     __shared__ int hist[256];
     __shared__ uint32_t sel[2];
-    const uint32_t* ab = reinterpret_cast<const uint32_t*>(a);
+    auto key = [&](int j) -> uint32_t {
+        return __float_as_uint(s ? __fdiv_rn(a[j], s[j]) : a[j]);
+    };
     const int t = threadIdx.x;
     const int C = (K + kTopkThreads - 1) / kTopkThreads;
     const int j0 = t * C;
@@ -78,8 +81,8 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const float* __restr
             if (t < 256) hist[t] = 0;
             __syncthreads();
             for (int j = j0; j < j1; ++j) {
-                const uint32_t key = ab[j];
-                if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+                const uint32_t kj = key(j);
+                if ((kj & pmask) == prefix) atomicAdd(&hist[(kj >> shift) & 255u], 1);
             }
             __syncthreads();
             // the bin holding the remaining-th largest key: counts from the top
@@ -102,15 +105,15 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const float* __restr
     }
     // ties before my range
     int ties = 0;
-    for (int j = j0; j < j1; ++j) ties += ab[j] == T;
+    for (int j = j0; j < j1; ++j) ties += key(j) == T;
     int tie_off = block_inclusive_scan(ties, buf) - ties;
     // membership and ascending positions
     int mine = 0;
     {
         int to = tie_off;
         for (int j = j0; j < j1; ++j) {
-            bool in = k >= K || (k > 0 && (ab[j] > T || (ab[j] == T && to < need)));
-            to += ab[j] == T;
+            bool in = k >= K || (k > 0 && (key(j) > T || (key(j) == T && to < need)));
+            to += key(j) == T;
             mine += in;
         }
     }
@@ -118,8 +121,8 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const float* __restr
     {
         int to = tie_off;
         for (int j = j0; j < j1; ++j) {
-            bool in = k >= K || (k > 0 && (ab[j] > T || (ab[j] == T && to < need)));
-            to += ab[j] == T;
+            bool in = k >= K || (k > 0 && (key(j) > T || (key(j) == T && to < need)));
+            to += key(j) == T;
             if (in) {
                 O[off] = j;
                 pos[j] = off;
@@ -149,8 +152,9 @@ __device__ __forceinline__ float quad_max_f(float v) {
 // W'[n][j] = RN(s_j * W[n][j]); outlier channels go to WO as bf16 and become
 // +0; the block amax gives the E8M0 code (1x32), or, for the 32x32 layout, the
 // amax over the 32 rows of the tile does (a first pass over the tile's rows,
-// the second pass re-reads them from L2); the hardware converter encodes.
-template <bool BF16, bool TILE>
+// the second pass re-reads them from L2), or, for 128x1 stripes, the amax over
+// the 16 lanes (128 channels) of the stripe; the hardware converter encodes.
+template <bool BF16, int LAY>
 __global__ void __launch_bounds__(256) fold_pack_kernel(const void* __restrict__ W, int32_t N, int32_t K,
                                                         int32_t k, const float* __restrict__ s,
                                                         const int32_t* __restrict__ pos,
@@ -241,12 +245,26 @@ __global__ void __launch_bounds__(256) fold_pack_kernel(const void* __restrict__
     };
 
     const int64_t wstride = (int64_t)gridDim.y * kFoldWaves;
-    if constexpr (!TILE) {
+    if constexpr (LAY == MG_W_1X32) {
         for (int64_t n = (int64_t)blockIdx.y * kFoldWaves + wave; n < N; n += wstride) {
             float f[8];
             fold_row(n, f);
             const float amax = quad_max_f(extract(n, f));
             if (valid) encode_store(n, f, e8m0_from_amax_bits(__float_as_uint(amax)));
+        }
+    } else if constexpr (LAY == MG_W_128X1) {
+        const int ns = (K + 127) / 128;
+        for (int64_t n = (int64_t)blockIdx.y * kFoldWaves + wave; n < N; n += wstride) {
+            float f[8];
+            fold_row(n, f);
+            float amax = quad_max_f(extract(n, f));
+            amax = fmaxf(amax, __shfl_xor(amax, 4, 64));      // the stripe's 4 quads (16 lanes)
+            amax = fmaxf(amax, __shfl_xor(amax, 8, 64));
+            const uint32_t c = e8m0_from_amax_bits(__float_as_uint(amax));
+            if (valid) {
+                encode_store(n, f, c);
+                if ((lane & 15) == 0) Wst[n * ns + j0 / 128] = (uint8_t)c;
+            }
         }
     } else {
         const int64_t NG = ((int64_t)N + 31) / 32;
@@ -283,9 +301,9 @@ hipError_t launch_smooth(const float* a, const float* w, int32_t K, double alpha
     return hipGetLastError();
 }
 
-hipError_t launch_topk(const float* a, int32_t K, int32_t k, int32_t* O, int32_t* pos,
+hipError_t launch_topk(const float* a, const float* s, int32_t K, int32_t k, int32_t* O, int32_t* pos,
                        hipStream_t st) {
-    hipLaunchKernelGGL(topk_kernel, dim3(1), dim3(kTopkThreads), 0, st, a, K, k, O, pos);
+    hipLaunchKernelGGL(topk_kernel, dim3(1), dim3(kTopkThreads), 0, st, a, s, K, k, O, pos);
     return hipGetLastError();
 }
 
@@ -295,6 +313,7 @@ hipError_t launch_fold_pack(const void* W, int32_t dtype, int32_t N, int32_t K, 
     if (N <= 0) return hipSuccess;
     const bool bf = dtype == MG_BF16;
     const bool tile = layout == MG_W_32X32;
+    const bool stripe = layout == MG_W_128X1;
     const int64_t gx = ((int64_t)K / 8 + 63) / 64;
     const int64_t units = tile ? ((int64_t)N + 31) / 32 : (int64_t)N;   // rows, or 32-row groups
     int64_t gy = (units + kFoldWaves - 1) / kFoldWaves;
@@ -303,14 +322,18 @@ hipError_t launch_fold_pack(const void* W, int32_t dtype, int32_t N, int32_t K, 
     if (gy > cap) gy = cap;
     if (gy > 65535) gy = 65535;
     dim3 grid((unsigned)gx, (unsigned)gy);
-    if (bf && tile)
-        hipLaunchKernelGGL((fold_pack_kernel<true, true>), grid, dim3(256), 0, st, W, N, K, k, s, pos, Wq, Ws, Wst, WO);
-    else if (bf)
-        hipLaunchKernelGGL((fold_pack_kernel<true, false>), grid, dim3(256), 0, st, W, N, K, k, s, pos, Wq, Ws, Wst, WO);
-    else if (tile)
-        hipLaunchKernelGGL((fold_pack_kernel<false, true>), grid, dim3(256), 0, st, W, N, K, k, s, pos, Wq, Ws, Wst, WO);
-    else
-        hipLaunchKernelGGL((fold_pack_kernel<false, false>), grid, dim3(256), 0, st, W, N, K, k, s, pos, Wq, Ws, Wst, WO);
+#define MG_FOLD_LAUNCH(BFV, LAYV)                                                                          \
+    hipLaunchKernelGGL((fold_pack_kernel<BFV, LAYV>), grid, dim3(256), 0, st, W, N, K, k, s, pos, Wq, Ws, Wst, WO)
+    if (bf) {
+        if (tile) MG_FOLD_LAUNCH(true, MG_W_32X32);
+        else if (stripe) MG_FOLD_LAUNCH(true, MG_W_128X1);
+        else MG_FOLD_LAUNCH(true, MG_W_1X32);
+    } else {
+        if (tile) MG_FOLD_LAUNCH(false, MG_W_32X32);
+        else if (stripe) MG_FOLD_LAUNCH(false, MG_W_128X1);
+        else MG_FOLD_LAUNCH(false, MG_W_1X32);
+    }
+#undef MG_FOLD_LAUNCH
     return hipGetLastError();
 }
 

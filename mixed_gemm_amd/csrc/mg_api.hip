@@ -46,10 +46,11 @@ int check_desc(const mg_plan_desc* d) {
     if (int e = check_K(d->K)) return e;
     if (d->N <= 0 || d->N % 32 != 0) return fail(MG_ERR_SHAPE, "N=%d must be a positive multiple of 32", d->N);
     if (d->k < 0 || d->k > d->K) return fail(MG_ERR_SHAPE, "k=%d must be in [0, K=%d]", d->k, d->K);
-    if (d->layout != MG_W_1X32 && d->layout != MG_W_32X32)
-        return fail(MG_ERR_ARG, "layout %d is not MG_W_1X32/MG_W_32X32", d->layout);
+    if (d->layout != MG_W_1X32 && d->layout != MG_W_32X32 && d->layout != MG_W_128X1)
+        return fail(MG_ERR_ARG, "layout %d is not MG_W_1X32/MG_W_32X32/MG_W_128X1", d->layout);
     if (d->smooth != 0 && d->smooth != 1) return fail(MG_ERR_ARG, "smooth must be 0 or 1");
-    if (d->reserved != 0) return fail(MG_ERR_ARG, "reserved field must be 0");
+    if (d->score != MG_SCORE_MAX && d->score != MG_SCORE_SMOOTHED)
+        return fail(MG_ERR_ARG, "score %d is not MG_SCORE_MAX/MG_SCORE_SMOOTHED", d->score);
     if (d->smooth && !(d->alpha > 0.0 && d->alpha < 1.0))
         return fail(MG_ERR_ARG, "alpha=%g must be in (0, 1)", d->alpha);
     return MG_OK;
@@ -66,7 +67,7 @@ int check_plan(const mg_plan* p, bool need_w) {
         MG_CHECK_PTR(p->Wq, "plan.Wq");
         MG_CHECK_PTR(p->Ws, "plan.Ws");
         if (p->d.k > 0) MG_CHECK_PTR(p->WO, "plan.WO");
-        if (p->d.layout == MG_W_32X32) MG_CHECK_PTR(p->Wst, "plan.Wst");
+        if (p->d.layout != MG_W_1X32) MG_CHECK_PTR(p->Wst, "plan.Wst");
     }
     return MG_OK;
 }
@@ -126,7 +127,8 @@ int mg_plan_bytes(const mg_plan_desc* d, size_t out[8]) {
     out[3] = 4 * K;                                        // pos
     out[4] = N * K / 2;                                    // Wq
     out[5] = N * K / 32;                                   // Ws
-    out[6] = d->layout == MG_W_32X32 ? (N / 32) * (K / 32) : 0;  // Wst
+    out[6] = d->layout == MG_W_32X32 ? (N / 32) * (K / 32)       // Wst
+           : d->layout == MG_W_128X1 ? N * ((K + 127) / 128) : 0;
     out[7] = 2 * N * k;                                    // WO
     return MG_OK;
 }
@@ -184,7 +186,8 @@ int mg_smooth_scales(const mg_plan* p, const float* act_max, const float* w_max,
 int mg_outlier_set(const mg_plan* p, const float* act_max, hipStream_t stream) {
     if (int e = check_plan(p, false)) return e;
     MG_CHECK_PTR(act_max, "act_max");
-    hipError_t h = mg::launch_topk(act_max, p->d.K, p->d.k, p->O, p->pos, stream);
+    hipError_t h = mg::launch_topk(act_max, p->d.score == MG_SCORE_SMOOTHED ? p->s : nullptr, p->d.K, p->d.k,
+                                   p->O, p->pos, stream);
     return h == hipSuccess ? MG_OK : hip_fail(h, "mg_outlier_set");
 }
 

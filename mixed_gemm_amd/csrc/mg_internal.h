@@ -15,7 +15,8 @@ hipError_t launch_colmax(const void* X, int32_t dtype, int64_t R, int32_t K, flo
                          hipStream_t st);
 hipError_t launch_smooth(const float* a, const float* w, int32_t K, double alpha, int32_t smooth,
                          float* s, float* rcp, hipStream_t st);
-hipError_t launch_topk(const float* a, int32_t K, int32_t k, int32_t* O, int32_t* pos,
+// s == nullptr: rank a_j; otherwise rank RN(a_j / s_j)
+hipError_t launch_topk(const float* a, const float* s, int32_t K, int32_t k, int32_t* O, int32_t* pos,
                        hipStream_t st);
 hipError_t launch_fold_pack(const void* W, int32_t dtype, int32_t N, int32_t K, int32_t k,
                             int32_t layout, const float* s, const int32_t* pos, uint8_t* Wq,

@@ -24,7 +24,7 @@ def host(t: torch.Tensor) -> np.ndarray:
 
 
 def run_pipeline(X: np.ndarray, W: np.ndarray, alpha: float, k: int, layout: str = "1x32",
-                 smooth: bool = True, calib_batches: int = 1) -> dict:
+                 smooth: bool = True, calib_batches: int = 1, score: str = "max") -> dict:
     """calibrate (optionally in several batches) -> weight ranges -> plan -> quantize -> GEMM,
     each through its own entry point; returns every artefact on the host."""
     Xd, Wd = dev(X), dev(W)
@@ -37,7 +37,7 @@ def run_pipeline(X: np.ndarray, W: np.ndarray, alpha: float, k: int, layout: str
             mg.mg_calib_act(Xd[part[0]:part[-1] + 1], act_max)
     w_max = torch.empty(K, dtype=torch.float32, device="cuda")
     mg.mg_weight_range(Wd, w_max)
-    desc = mg.make_desc(K, N, k, alpha, layout, smooth)
+    desc = mg.make_desc(K, N, k, alpha, layout, smooth, score)
     p = mg.Plan.empty(desc)
     mg.mg_plan_build(p, act_max, w_max, Wd)
     a = mg.Act.empty(desc, M)

@@ -46,7 +46,7 @@ def test_plan_and_act_sizes():
     (64, 64, -1, 0.5, 0, 1, -2),      # k < 0
     (64, 64, 4, 0.0, 0, 1, -1),       # alpha
     (64, 64, 4, 1.0, 0, 1, -1),       # alpha
-    (64, 64, 4, 0.5, 2, 1, -1),       # layout
+    (64, 64, 4, 0.5, 3, 1, -1),       # layout
     (64, 64, 4, 0.5, 0, 3, -1),       # smooth flag
     (131072, 64, 4, 0.5, 0, 1, -5),   # K beyond the limit
 ])
@@ -55,6 +55,16 @@ def test_desc_validation(K, N, k, alpha, layout, smooth, code):
     out = (ctypes.c_size_t * 8)()
     assert mg.lib().mg_plan_bytes(ctypes.byref(d), out) == code
     assert mg.lib().mg_last_error()
+
+
+def test_score_and_stripe_layout_sizes():
+    out = (ctypes.c_size_t * 8)()
+    d = mg.mg_plan_desc(64, 64, 4, 0, 1, 2, 0.5)                  # score 2 does not exist
+    assert mg.lib().mg_plan_bytes(ctypes.byref(d), out) == -1
+    d = mg.make_desc(352, 64, 4, 0.5, "128x1", score="smoothed")  # stripes 128, 128, 96
+    assert mg.mg_plan_bytes(d)[6] == 64 * 3
+    p = mg.mg_plan(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE)
+    assert mg.lib().mg_fold_pack(ctypes.byref(p), FAKE, 1, None) == -1     # Wst required
 
 
 def test_alpha_ignored_without_smoothing():

@@ -43,8 +43,8 @@ def _bits_equal(a, b, name):
         raise AssertionError(f"{name} differs at {bad[:5].tolist()} ({len(bad)} places)")
 
 
-def _run_full(w: synth.Workload, layout="1x32"):
-    print(f"\n[full-size] {w.name} layout={layout} k={w.k} alpha={w.alpha}", flush=True)
+def _run_full(w: synth.Workload, layout="1x32", score="max"):
+    print(f"\n[full-size] {w.name} layout={layout} score={score} k={w.k} alpha={w.alpha}", flush=True)
     X, W = w.make_x(), w.make_w()
     M, K, N = X.shape[0], X.shape[1], W.shape[0]
     Xd, Wd = dev(X), dev(W)
@@ -53,7 +53,7 @@ def _run_full(w: synth.Workload, layout="1x32"):
     mg.mg_calib_act(Xd, act_max)
     w_max = torch.empty(K, dtype=torch.float32, device="cuda")
     mg.mg_weight_range(Wd, w_max)
-    desc = mg.make_desc(K, N, w.k, w.alpha, layout)
+    desc = mg.make_desc(K, N, w.k, w.alpha, layout, True, score)
     p = mg.Plan.empty(desc)
     mg.mg_plan_build(p, act_max, w_max, Wd)
     a = mg.Act.empty(desc, M)
@@ -74,12 +74,12 @@ def _run_full(w: synth.Workload, layout="1x32"):
     # oracle: plan on the full data, forward on the sampled rows
     o_a = layer.act_max(X)
     o_w = layer.weight_range(W)
-    op = layer.plan(o_a, o_w, W, w.alpha, w.k, layout)
+    op = layer.plan(o_a, o_w, W, w.alpha, w.k, layout, True, score)
     _bits_equal(g["act_max"], o_a, "act_max")
     _bits_equal(g["w_max"], o_w, "w_max")
     for name in ("s", "rcp", "O", "pos", "Wq", "Ws", "WO"):
         _bits_equal(g[name], op[name], name)
-    if layout == "32x32":
+    if layout != "1x32":
         _bits_equal(g["Wst"], op["Wst"], "Wst")
     oq = layer.quantize_act(X[rows], op["s"], op["O"])
     for name in ("Aq", "As", "XO"):
@@ -103,3 +103,11 @@ def test_ffn0_720p_k128_alpha07():
 
 def test_ffn0_480p_tile_scales():
     _run_full(synth.FFN0_480P, layout="32x32")
+
+
+def test_ffn0_480p_stripe_scales():
+    _run_full(synth.FFN0_480P, layout="128x1")
+
+
+def test_ffn2_480p_smoothed_score():
+    _run_full(synth.FFN2_480P, score="smoothed")

@@ -22,10 +22,10 @@ pytestmark = pytest.mark.gpu
 TOL = 2e-3
 
 
-def _oracle(X, W, alpha, k, layout="1x32", smooth=True):
+def _oracle(X, W, alpha, k, layout="1x32", smooth=True, score="max"):
     a = layer.act_max(X)
     w = layer.weight_range(W)
-    p = layer.plan(a, w, W, alpha, k, layout, smooth)
+    p = layer.plan(a, w, W, alpha, k, layout, smooth, score)
     qa = layer.quantize_act(X, p["s"], p["O"])
     Y64 = layer.dual_gemm_f64(qa["Aq"], qa["As"], p["Wq"], p["Ws"], qa["XO"], p["WO"])
     return dict(act_max=a, w_max=w, Y64=Y64, **p, **qa)
@@ -42,7 +42,7 @@ def _compare(g, o, layout="1x32"):
         if not same:
             bad = np.argwhere(gv != ov)
             raise AssertionError(f"{name} differs at {bad[:5].tolist()} ({len(bad)} places)")
-    if layout == "32x32":
+    if layout != "1x32":
         assert np.array_equal(g["Wst"], o["Wst"])
     return check_output(g["Y"], g["Y32"], o["Y64"], TOL)
 
@@ -68,12 +68,32 @@ def test_bf16_shapes(M, K, N, k):
     _compare(g, _oracle(X, W, 0.6, k))
 
 
-@pytest.mark.parametrize("layout", ["1x32", "32x32"])
+@pytest.mark.parametrize("layout", ["1x32", "32x32", "128x1"])
 def test_layouts(layout):
     X, W = _heavy(300, 512, 256, 77)
     W[5, 100] = 0.59                         # a local weight outlier inside one tile
     g = run_pipeline(X, W, 0.5, 12, layout)
     _compare(g, _oracle(X, W, 0.5, 12, layout), layout)
+
+
+@pytest.mark.parametrize("M,K,N,k", [(300, 352, 96, 12), (70, 96, 64, 3)])
+def test_stripes_ragged_K(M, K, N, k):
+    """128x1 stripes when K is not a multiple of 128 (a short last stripe)."""
+    X, W = _heavy(M, K, N, 40 + K)
+    g = run_pipeline(X, W, 0.6, k, "128x1")
+    _compare(g, _oracle(X, W, 0.6, k, "128x1"), "128x1")
+
+
+@pytest.mark.parametrize("layout", ["1x32", "128x1"])
+def test_smoothed_score(layout):
+    """Eq. (4) ranking the smoothed maxima RN(a_j / s_j): a different outlier
+    set than the raw score on this input (checked), bit-exact to the oracle."""
+    X, W = _heavy(400, 512, 128, 91)
+    W[:, 7] = synth.f32_to_bf16_bits(np.full(128, 0.55, np.float32))     # a wide weight column
+    g = run_pipeline(X, W, 0.5, 16, layout, score="smoothed")
+    o = _oracle(X, W, 0.5, 16, layout, score="smoothed")
+    _compare(g, o, layout)
+    assert not np.array_equal(o["O"], _oracle(X, W, 0.5, 16, layout)["O"])
 
 
 def test_smoothing_off():
