@@ -14,11 +14,12 @@ TFLOP/s; the dual-GEMM kernel's own rate is in `roofline`.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
     python bench.py --suite      one JSON line per configuration point: the
-                                 480p up/down-projections, the 720p (k, alpha)
-                                 sweep and the 720p FFN block (both weight-scale
-                                 layouts), each with kernel rates (warm, and the
-                                 GEMM also cold) and the fidelity of the three
-                                 modes against the unquantized float64 layer
+                                 480p up/down-projections (three weight-scale
+                                 layouts, raw and smoothed outlier score), the
+                                 720p (k, alpha) sweep and the 720p FFN block
+                                 (three layouts), each with kernel rates (warm,
+                                 and the GEMM also cold) and the fidelity of the
+                                 three modes against the unquantized float64 layer
 """
 from __future__ import annotations
 
@@ -187,7 +188,7 @@ def suite(args) -> int:
     torch.cuda.set_device(0)
     g = np.random.default_rng(12345)
 
-    def layer_point(w, X_h, W_h, Xd, Wd, points, layout="1x32"):
+    def layer_point(w, X_h, W_h, Xd, Wd, points, layout="1x32", score="max"):
         """Timings + fidelity of one layer for each (k, alpha) in points."""
         M, K, N = X_h.shape[0], w.K, w.N
         bf = w.dtype == "bf16"
@@ -205,14 +206,14 @@ def suite(args) -> int:
         Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
 
         def fidelity(k, alpha, smooth):
-            p = mg.Plan.empty(mg.make_desc(K, N, k, alpha, layout, smooth))
+            p = mg.Plan.empty(mg.make_desc(K, N, k, alpha, layout, smooth, score))
             mg.mg_plan_build(p, act_max, w_max, Wd)
             return rel_fro(y_host(mg.forward(p, Xs)), Yref)
 
         uniform = fidelity(0, 0.5, False)
         smooth_only = {}
         for k, alpha in points:
-            desc = mg.make_desc(K, N, k, alpha, layout, True)
+            desc = mg.make_desc(K, N, k, alpha, layout, True, score)
             p = mg.Plan.empty(desc)
             t_plan = timed(lambda: mg.mg_plan_build(p, act_max, w_max, Wd))
             a = mg.Act.empty(desc, M)
@@ -227,7 +228,7 @@ def suite(args) -> int:
             pack_bytes = N * K * xb + N * K // 2 + N * K // 32 + 2 * N * k
             _emit({"suite": "dual-branch W4A4 layer",
                    "config": {"workload": w.name, "M": M, "K": K, "N": N, "k": k, "alpha": alpha,
-                              "weight_blocks": layout, "output": "bf16"},
+                              "weight_blocks": layout, "outlier_score": score, "output": "bf16"},
                    "gemm_ms": round(t_gemm, 4), "gemm_tflops": round(fl / t_gemm / 1e9, 1),
                    "gemm_pct_mxfp4_peak": round(100 * fl / t_gemm / 1e9 / PEAK_FP4_TFLOPS, 2),
                    "gemm_ms_cold": round(t_gemm_cold, 4),
@@ -244,17 +245,20 @@ def suite(args) -> int:
             del a
         del Y
 
-    def layer_config(w, points, layouts=("1x32",)):
+    def layer_config(w, points, layouts=("1x32",), scores=("max",)):
         X_h, W_h = w.make_x(), w.make_w()
         Xd, Wd = dev(X_h), dev(W_h)
         for lay in layouts:
-            layer_point(w, X_h, W_h, Xd, Wd, points, lay)
+            for sc in scores:
+                layer_point(w, X_h, W_h, Xd, Wd, points, lay, sc)
         del Xd, Wd
         torch.cuda.empty_cache()
 
     layer_config(synth.TINY, [(synth.TINY.k, synth.TINY.alpha)])
-    layer_config(synth.FFN0_480P, [(synth.FFN0_480P.k, synth.FFN0_480P.alpha)], ("1x32", "32x32"))
-    layer_config(synth.FFN2_480P, [(synth.FFN2_480P.k, synth.FFN2_480P.alpha)])
+    layer_config(synth.FFN0_480P, [(synth.FFN0_480P.k, synth.FFN0_480P.alpha)], ("1x32", "32x32", "128x1"),
+                 ("max", "smoothed"))
+    layer_config(synth.FFN2_480P, [(synth.FFN2_480P.k, synth.FFN2_480P.alpha)], ("1x32", "32x32", "128x1"),
+                 ("max", "smoothed"))
     layer_config(synth.FFN0_720P, [(k, a) for a in synth.SWEEP_ALPHA for k in synth.SWEEP_K])
 
     # ---- the 720p FFN block
@@ -273,7 +277,7 @@ def suite(args) -> int:
     c = float(np.sqrt(2.0 / np.pi))
     href = 0.5 * z * (1.0 + np.tanh(c * (z + 0.044715 * z ** 3)))     # float64 GELU-tanh
     Yref = href @ to_f64(W2_h).T
-    for lay in ("1x32", "32x32"):
+    for lay in ("1x32", "32x32", "128x1"):
         def block_fid(k0, a0, k2, a2, smooth):
             p0 = mg.Plan.empty(mg.make_desc(w0.K, w0.N, k0, a0, lay, smooth))
             p2 = mg.Plan.empty(mg.make_desc(w2.K, w2.N, k2, a2, lay, smooth))
