@@ -285,7 +285,7 @@ def suite(args) -> int:
                 wm = torch.empty(p.desc.K, dtype=torch.float32, device="cuda")
                 mg.mg_weight_range(Wd_, wm)
                 mg.mg_plan_build(p, am, wm, Wd_)
-            _, y = mg.ffn_block_forward(mg.FFNBlock(p0, p2), Xs)
+            y = mg.ffn_block_forward(mg.FFNBlock(p0, p2), Xs)
             return rel_fro(y_host(y), Yref)
         blk = mg.ffn_block_plans(act0, act2, W0d, W2d, w0.alpha, w0.k, w2.alpha, w2.k, lay)
         a0 = mg.Act.empty(blk.plan0.desc, M)
@@ -294,11 +294,18 @@ def suite(args) -> int:
         h = torch.empty_like(Y0)
         Y2 = torch.empty((M, w2.N), dtype=torch.bfloat16, device="cuda")
 
-        def run_block():
+        def run_block():              # GELU and ffn.2's quantize fused in one pass
+            mg.mg_forward(blk.plan0, X5, a0, Y0)
+            mg.mg_gelu_quantize_act(blk.plan2, Y0, a2)
+            mg.mg_dual_gemm(blk.plan2, a2, Y2)
+
+        def run_block_unfused():
             mg.mg_forward(blk.plan0, X5, a0, Y0)
             mg.mg_gelu_tanh_bf16(Y0, h)
             mg.mg_forward(blk.plan2, h, a2, Y2)
         t_block = timed(run_block, reps=5)
+        t_block_unfused = timed(run_block_unfused, reps=5)
+        t_gq = timed(lambda: mg.mg_gelu_quantize_act(blk.plan2, Y0, a2))
         t_g0 = timed(lambda: mg.mg_dual_gemm(blk.plan0, a0, Y0))
         t_gelu = timed(lambda: mg.mg_gelu_tanh_bf16(Y0, h))
         t_q2 = timed(lambda: mg.mg_quantize_act(blk.plan2, h, a2))
@@ -308,6 +315,9 @@ def suite(args) -> int:
                "config": {"workload": "ffn_block_720p_75600x5120x13824x5120", "M": M, "k": [w0.k, w2.k],
                           "alpha": [w0.alpha, w2.alpha], "weight_blocks": lay, "output": "bf16"},
                "block_ms": round(t_block, 4), "block_tflops": round((fl0 + fl2) / t_block / 1e9, 1),
+               "block_ms_unfused_gelu": round(t_block_unfused, 4),
+               "gelu_quant_ms": round(t_gq, 4),
+               "gelu_quant_gbs": round((M * w2.K * 2.53125 + 2 * M * w2.k) / t_gq / 1e6, 1),
                "ffn0_gemm_tflops": round(fl0 / t_g0 / 1e9, 1), "ffn2_gemm_tflops": round(fl2 / t_g2 / 1e9, 1),
                "gelu_ms": round(t_gelu, 4), "gelu_gbs": round(4 * M * w0.N / t_gelu / 1e6, 1),
                "ffn2_quant_ms": round(t_q2, 4),

@@ -185,6 +185,14 @@ int mg_forward(const mg_plan* p, const void* X, int32_t dtype, int64_t M, const 
  * computed in f32, for n bf16 values (in == out allowed). */
 int mg_gelu_tanh_bf16(const uint16_t* in, uint16_t* out, int64_t n, hipStream_t stream);
 
+/* The FFN block's second projection fed straight from the first one's bf16
+ * output Y [M][K] (K = p->d.K = the first projection's N): quantizes the
+ * hidden activation h = bf16_RNE(gelu_tanh(Y)) -- bit for bit what
+ * mg_gelu_tanh_bf16 followed by mg_quantize_act computes -- in one pass,
+ * without writing h (GELU-gated FFN inputs: the integration paragraph).
+ * Same arguments and errors as mg_quantize_act with dtype MG_BF16. */
+int mg_gelu_quantize_act(const mg_plan* p, const uint16_t* Y, int64_t M, const mg_act* a, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

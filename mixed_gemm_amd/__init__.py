@@ -55,7 +55,8 @@ class mg_act(ctypes.Structure):
 
 EXPORTS = ("mg_version", "mg_last_error", "mg_plan_bytes", "mg_act_bytes", "mg_calib_reset",
            "mg_calib_act", "mg_weight_range", "mg_smooth_scales", "mg_outlier_set", "mg_fold_pack",
-           "mg_plan_build", "mg_quantize_act", "mg_dual_gemm", "mg_forward", "mg_gelu_tanh_bf16")
+           "mg_plan_build", "mg_quantize_act", "mg_dual_gemm", "mg_forward", "mg_gelu_tanh_bf16",
+           "mg_gelu_quantize_act")
 
 _lib = None
 
@@ -85,7 +86,11 @@ def lib() -> ctypes.CDLL:
             "mg_dual_gemm": ([P(mg_plan), P(mg_act), i64, vp, i32, vp], ctypes.c_int),
             "mg_forward": ([P(mg_plan), vp, i32, i64, P(mg_act), vp, i32, vp], ctypes.c_int),
             "mg_gelu_tanh_bf16": ([vp, vp, i64, vp], ctypes.c_int),
+            "mg_gelu_quantize_act": ([P(mg_plan), vp, i64, P(mg_act), vp], ctypes.c_int),
         }
+        missing = set(EXPORTS) - set(sig)
+        if missing:                       # an undeclared signature would truncate 64-bit pointers
+            raise RuntimeError(f"no ctypes signature for {sorted(missing)}")
         for name, (args, res) in sig.items():
             f = getattr(L, name)
             f.argtypes = args
@@ -259,6 +264,13 @@ def mg_gelu_tanh_bf16(inp: torch.Tensor, out: torch.Tensor, stream=None) -> None
     _check(lib().mg_gelu_tanh_bf16(_ptr(inp), _ptr(out), inp.numel(), _stream(stream)))
 
 
+def mg_gelu_quantize_act(plan: Plan, Y: torch.Tensor, act: Act, stream=None) -> None:
+    if Y.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise ValueError("bf16 input expected")
+    p, a = plan.c(), act.c()
+    _check(lib().mg_gelu_quantize_act(ctypes.byref(p), _ptr(Y), Y.shape[0], ctypes.byref(a), _stream(stream)))
+
+
 # ----------------------------------------------------------------------------- convenience
 
 def calibrate(batches, K: int, device="cuda", stream=None) -> torch.Tensor:
@@ -343,10 +355,14 @@ def ffn_block_plans(act0: torch.Tensor, act2: torch.Tensor, W0: torch.Tensor, W2
                     plan(act2, W2, alpha2, k2, layout, stream=stream))
 
 
-def ffn_block_forward(blk: FFNBlock, X: torch.Tensor, stream=None) -> tuple[torch.Tensor, torch.Tensor]:
-    """Y2 = ffn.2(gelu(ffn.0(X))); returns (h, Y2)."""
+def ffn_block_forward(blk: FFNBlock, X: torch.Tensor, stream=None) -> torch.Tensor:
+    """Y2 = ffn.2(gelu(ffn.0(X))): ffn.0's forward, then GELU and ffn.2's
+    activation quantization in one pass (mg_gelu_quantize_act), then ffn.2's
+    dual GEMM."""
     y0 = forward(blk.plan0, X, stream=stream)
-    h = torch.empty_like(y0)
-    mg_gelu_tanh_bf16(y0, h, stream)
+    a2 = Act.empty(blk.plan2.desc, X.shape[0], X.device)
+    mg_gelu_quantize_act(blk.plan2, y0, a2, stream)
     del y0
-    return h, forward(blk.plan2, h, stream=stream)
+    y2 = torch.empty((X.shape[0], blk.plan2.desc.N), dtype=torch.bfloat16, device=X.device)
+    mg_dual_gemm(blk.plan2, a2, y2, stream)
+    return y2

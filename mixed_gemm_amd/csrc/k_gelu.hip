@@ -10,12 +10,6 @@ namespace mg {
 
 namespace {
 
-__device__ __forceinline__ uint32_t gelu_bf16(uint32_t b) {
-    const float y = bf16_to_f32(b);
-    const float inner = 0.7978845608028654f * (y + 0.044715f * y * y * y);
-    return f32_to_bf16_rne(0.5f * y * (1.0f + tanhf(inner)));
-}
-
 __global__ void __launch_bounds__(256) gelu_kernel(const uint16_t* in,
                                                    uint16_t* out, int64_t n) {
     const int64_t nvec = n / 8;

@@ -17,6 +17,11 @@
 // processed.  The per-channel s, RN(1/s) and outlier masks of a lane's 8
 // channels stay in registers for all of its rows.
 //
+// With GELU, X is the previous projection's bf16 output and the quantized
+// input is h = gelu_bf16(X) (the FFN block's hidden activation), computed
+// in registers with the GELU kernel's own code: one pass instead of a GELU
+// pass that writes h and a quantize pass that reads it back.
+//
 // bf16 input: the quotient comes from Markstein's correction of x * RN(1/s),
 // exact when every x of the lane's row lies in {0} or [2^-100, 2^100]; that
 // range is checked on the raw bf16 bits, two channels per 16-bit-lane
@@ -81,6 +86,7 @@ __device__ __forceinline__ void encode_store(const float (&q)[8], int lane, bool
     }
 }
 
+template <bool GELU>
 __global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restrict__ X, int64_t M, int32_t K,
                                                          int32_t k, const float* __restrict__ s,
                                                          const float* __restrict__ rcp,
@@ -154,7 +160,11 @@ __global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restr
         for (int u = 0; u < RPI; ++u) {
             const int64_t r = r0 + u * rstride;
             if (r >= M) break;                          // uniform across the wave
-            const u32x4 w = cur[u];
+            u32x4 w = cur[u];
+            if constexpr (GELU) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w[i] = gelu_bf16(w[i] & 0xFFFFu) | (gelu_bf16(w[i] >> 16) << 16);
+            }
             const bool fast = s_ok && bf16x8_in_fast_range(w);
             float x[8], q[8];
 #pragma unroll
@@ -228,7 +238,7 @@ __global__ void __launch_bounds__(256) quant_f32_kernel(const float* __restrict_
 
 hipError_t launch_quant(const void* X, int32_t dtype, int64_t M, int32_t K, int32_t k,
                         const float* s, const float* rcp, const int32_t* pos, uint8_t* Aq,
-                        uint8_t* As, uint16_t* XO, hipStream_t st) {
+                        uint8_t* As, uint16_t* XO, hipStream_t st, bool gelu) {
     if (M <= 0) return hipSuccess;
     const int64_t gx = ((int64_t)K / 8 + 63) / 64;
     // about WAVES_PER_CU waves per CU, each wave at least RPI rows
@@ -238,9 +248,12 @@ hipError_t launch_quant(const void* X, int32_t dtype, int64_t M, int32_t K, int3
     if (gy > cap) gy = cap;
     if (gy > 65535) gy = 65535;
     dim3 grid((unsigned)gx, (unsigned)gy);
-    if (dtype == MG_BF16)
-        hipLaunchKernelGGL(quant_bf16_kernel, grid, dim3(256), 0, st, static_cast<const uint16_t*>(X), M, K, k, s,
-                           rcp, pos, Aq, As, XO);
+    if (dtype == MG_BF16 && gelu)
+        hipLaunchKernelGGL(quant_bf16_kernel<true>, grid, dim3(256), 0, st, static_cast<const uint16_t*>(X), M, K, k,
+                           s, rcp, pos, Aq, As, XO);
+    else if (dtype == MG_BF16)
+        hipLaunchKernelGGL(quant_bf16_kernel<false>, grid, dim3(256), 0, st, static_cast<const uint16_t*>(X), M, K,
+                           k, s, rcp, pos, Aq, As, XO);
     else
         hipLaunchKernelGGL(quant_f32_kernel, grid, dim3(256), 0, st, static_cast<const float*>(X), M, K, k, s, pos,
                            Aq, As, XO);

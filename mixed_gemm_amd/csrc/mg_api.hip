@@ -225,6 +225,17 @@ int mg_quantize_act(const mg_plan* p, const void* X, int32_t dtype, int64_t M, c
     return h == hipSuccess ? MG_OK : hip_fail(h, "mg_quantize_act");
 }
 
+int mg_gelu_quantize_act(const mg_plan* p, const uint16_t* Y, int64_t M, const mg_act* a, hipStream_t stream) {
+    if (int e = check_plan(p, false)) return e;
+    if (M < 0) return fail(MG_ERR_SHAPE, "M=%lld must be >= 0", (long long)M);
+    if (M == 0) return MG_OK;
+    MG_CHECK_PTR(Y, "Y");
+    if (int e = check_act(p, a)) return e;
+    hipError_t h = mg::launch_quant(Y, MG_BF16, M, p->d.K, p->d.k, p->s, p->rcp, p->pos, a->Aq, a->As, a->XO,
+                                    stream, true);
+    return h == hipSuccess ? MG_OK : hip_fail(h, "mg_gelu_quantize_act");
+}
+
 int mg_dual_gemm(const mg_plan* p, const mg_act* a, int64_t M, void* Y, int32_t y_dtype, hipStream_t stream) {
     if (int e = check_plan(p, true)) return e;
     if (int e = check_dtype(y_dtype)) return e;

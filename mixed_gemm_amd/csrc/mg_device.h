@@ -66,6 +66,16 @@ __device__ __forceinline__ bool div_fast_ok_x(float x) {
 }
 __device__ __forceinline__ bool div_fast_ok_s(float s) { return s >= 0x1p-20f && s <= 0x1p20f; }
 
+// GELU (tanh form) of one bf16 value, f32 math, rounded to bf16 (nearest
+// even): bf16_RNE(0.5 y (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3)))).  The GELU
+// kernel and the fused GELU + quantize path both use this, so their outputs
+// are the same bits.
+__device__ __forceinline__ uint32_t gelu_bf16(uint32_t b) {
+    const float y = bf16_to_f32(b);
+    const float inner = 0.7978845608028654f * (y + 0.044715f * y * y * y);
+    return f32_to_bf16_rne(0.5f * y * (1.0f + tanhf(inner)));
+}
+
 // E8M0 code c -> the f32 scale 2^(c - 127) (c = 0 gives the subnormal 2^-127).
 __device__ __forceinline__ float e8m0_to_f32(uint32_t c) {
     return __uint_as_float(c ? (c << 23) : 0x00200000u);

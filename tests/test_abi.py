@@ -18,6 +18,15 @@ def _declared():
     return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(mg_\w+)\s*\(", text, re.M)))
 
 
+def test_every_export_has_a_ctypes_signature():
+    """Without argtypes ctypes would pass device pointers as 32-bit ints."""
+    L = mg.lib()
+    for n in mg.EXPORTS:
+        assert getattr(L, n).argtypes is not None, n
+    for n in ("mg_quantize_act", "mg_gelu_quantize_act", "mg_dual_gemm", "mg_forward", "mg_calib_act"):
+        assert ctypes.c_void_p in getattr(L, n).argtypes, n
+
+
 def test_exports_every_declared_symbol():
     names = _declared()
     assert len(names) >= 15

@@ -13,7 +13,9 @@ Stage-wise parity:
 - on sampled rows of the evaluation batch: ffn.0's activation codes bit for
   bit and its output within 2e-3 (fp32) / one RNE (bf16); the GELU within one
   bf16 rounding of the float64 GELU of the GPU's ffn.0 output; ffn.2's codes
-  (from the GPU's h) bit for bit and its output within 2e-3 / one RNE.
+  (from the GPU's h) bit for bit and its output within 2e-3 / one RNE;
+- the fused GELU + quantize pass from ffn.0's output gives ffn.2's codes bit
+  for bit, on every row.
 The block's fidelity against the unquantized float64 block is printed, not
 asserted.
 """
@@ -111,9 +113,13 @@ def test_block_stagewise(block, layout):
     del a0, Y0_32
     h = torch.empty_like(Y0)
     mg.mg_gelu_tanh_bf16(Y0, h)
-    del Y0
     a2 = mg.Act.empty(blk.plan2.desc, M)
     mg.mg_quantize_act(blk.plan2, h, a2)
+    af = mg.Act.empty(blk.plan2.desc, M)          # GELU + quantize in one pass, from ffn.0's output
+    mg.mg_gelu_quantize_act(blk.plan2, Y0, af)
+    for n in ("Aq", "As", "XO"):
+        assert torch.equal(getattr(af, n).view(torch.uint8), getattr(a2, n).view(torch.uint8)), f"fused {n}"
+    del af, Y0
     Y2 = torch.empty((M, w2.N), dtype=torch.bfloat16, device="cuda")
     mg.mg_dual_gemm(blk.plan2, a2, Y2)
     Y2_32 = torch.empty((M, w2.N), dtype=torch.float32, device="cuda")

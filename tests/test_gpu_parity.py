@@ -146,6 +146,34 @@ def test_gelu_tanh():
     assert np.all(np.abs(h - ref) <= 2 ** -8 * np.abs(ref) + 1e-6)
 
 
+@pytest.mark.parametrize("M,K,k", [(300, 512, 12), (77, 96, 5), (1000, 1024, 0)])
+def test_gelu_quantize_fused(M, K, k):
+    """GELU + quantize in one pass equals the GELU kernel followed by the
+    quantizer, bit for bit, and both equal the oracle's quantization of the
+    GPU's h (GELU rounding is the GPU's own: the oracle consumes its h)."""
+    g = np.random.default_rng(M + K)
+    y = (g.standard_normal((M, K)) * 1.5).astype(np.float32)
+    y[:, g.choice(K, max(1, K // 50), replace=False)] *= 12.0
+    Y = synth.f32_to_bf16_bits(y)
+    Yd = dev(Y)
+    h = torch.empty_like(Yd)
+    mg.mg_gelu_tanh_bf16(Yd, h)
+    act_max = torch.empty(K, dtype=torch.float32, device="cuda")
+    mg.mg_calib_reset(act_max)
+    mg.mg_calib_act(h, act_max)
+    W = synth.weights(64, K, sigma=0.01, clip=None, seed=K, bf16=True)
+    p = mg.plan(act_max, dev(W), 0.5, k)
+    a1, a2 = mg.Act.empty(p.desc, M), mg.Act.empty(p.desc, M)
+    mg.mg_quantize_act(p, h, a1)
+    mg.mg_gelu_quantize_act(p, Yd, a2)
+    torch.cuda.synchronize()
+    for n in ("Aq", "As", "XO"):
+        assert torch.equal(getattr(a1, n).view(torch.uint8), getattr(a2, n).view(torch.uint8)), n
+    oq = layer.quantize_act(host(h), host(p.s), host(p.O))
+    for n in ("Aq", "As", "XO"):
+        assert np.array_equal(np.asarray(host(getattr(a2, n))).view(np.uint8), np.asarray(oq[n]).view(np.uint8)), n
+
+
 def test_empty_inputs_are_noops():
     desc = mg.make_desc(64, 32, 4, 0.5)
     p = mg.Plan.empty(desc)
