@@ -181,8 +181,13 @@ int mg_dual_gemm(const mg_plan* p, const mg_act* a, int64_t M, void* Y, int32_t 
 int mg_forward(const mg_plan* p, const void* X, int32_t dtype, int64_t M, const mg_act* a,
                void* Y, int32_t y_dtype, hipStream_t stream);
 
-/* Between the two projections of the FFN block: out[i] = bf16_RNE(gelu_tanh(in[i]))
- * computed in f32, for n bf16 values (in == out allowed). */
+/* Between the two projections of the FFN block: out[i] = gelu_tanh(in[i]) for
+ * n bf16 values (in == out allowed), gelu_tanh(y) = 0.5 y (1 + tanh(sqrt(2/pi)
+ * (y + 0.044715 y^3))).  Evaluated in f32 as the equal y / (1 + exp(-2u))
+ * (u the tanh argument) with the hardware exp2 and reciprocal, then rounded
+ * to bf16: a faithful bf16 rounding (one of the two bf16 neighbours) of the
+ * exact value for every finite input where that is at least 2^-24 in
+ * magnitude; smaller results are at most 2^-24 (very negative y give -0). */
 int mg_gelu_tanh_bf16(const uint16_t* in, uint16_t* out, int64_t n, hipStream_t stream);
 
 /* The FFN block's second projection fed straight from the first one's bf16

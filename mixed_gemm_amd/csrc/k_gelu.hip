@@ -1,8 +1,9 @@
 // GELU (tanh form) between the two projections of the FFN block: the
 // calibrated FFN inputs sit after the SiLU/GELU gates ("W4A4 Quantization for
 // Inference on Wan2.2-I2V-A14B", integration paragraph).
-// out = bf16_RNE(0.5 y (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3)))), f32 math,
-// 8 bf16 per lane (16-byte loads and stores).  HBM-bound: 4 bytes per element.
+// out = gelu_tanh(y) rounded to bf16 (gelu_bf16: the sigmoid form with the
+// hardware exp2 and reciprocal), 8 bf16 per lane (16-byte loads and stores).
+// HBM-bound: 4 bytes per element.
 #include "mg_device.h"
 #include "mg_internal.h"
 

@@ -67,13 +67,21 @@ __device__ __forceinline__ bool div_fast_ok_x(float x) {
 __device__ __forceinline__ bool div_fast_ok_s(float s) { return s >= 0x1p-20f && s <= 0x1p20f; }
 
 // GELU (tanh form) of one bf16 value, f32 math, rounded to bf16 (nearest
-// even): bf16_RNE(0.5 y (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3)))).  The GELU
-// kernel and the fused GELU + quantize path both use this, so their outputs
-// are the same bits.
+// even).  0.5 y (1 + tanh u) with u = sqrt(2/pi) (y + 0.044715 y^3) is
+// evaluated as the equal y / (1 + e^(-2u)) = y * sigmoid(2u): one hardware
+// exp2 (v_exp_f32) of t = -2u log2(e) = y (C2 y^2 + C1) and one hardware
+// reciprocal (v_rcp_f32), with no cancellation in 1 + tanh u for negative y.
+// The result is a faithful bf16 rounding of the exact GELU for every finite
+// bf16 input where that is at least 2^-24 in magnitude (smaller results come
+// out as at most 2^-24; very negative y give -0).  The GELU kernel and the
+// fused GELU + quantize path both use this, so their outputs are the same bits.
 __device__ __forceinline__ uint32_t gelu_bf16(uint32_t b) {
+    constexpr float C1 = -2.302208198144325f;    // -2 sqrt(2/pi) log2(e)
+    constexpr float C2 = -0.1029432395800235f;   // 0.044715 C1
     const float y = bf16_to_f32(b);
-    const float inner = 0.7978845608028654f * (y + 0.044715f * y * y * y);
-    return f32_to_bf16_rne(0.5f * y * (1.0f + tanhf(inner)));
+    const float t = y * __builtin_fmaf(C2, y * y, C1);
+    const float e = __builtin_amdgcn_exp2f(t);
+    return f32_to_bf16_rne(y * __builtin_amdgcn_rcpf(1.0f + e));
 }
 
 // E8M0 code c -> the f32 scale 2^(c - 127) (c = 0 gives the subnormal 2^-127).

@@ -57,6 +57,20 @@ def bf16_to_f64(b: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
+def assert_faithful_bf16(h: np.ndarray, ref: np.ndarray, floor: float = 2.0 ** -24) -> None:
+    """h (float64 values of bf16 results) is a faithful bf16 rounding of the
+    float64 values ref -- less than one bf16 ulp away, so one of the two bf16
+    neighbours -- wherever |ref| >= floor; below it |h| <= floor."""
+    h, ref = np.asarray(h, np.float64), np.asarray(ref, np.float64)
+    big = np.abs(ref) >= floor
+    m = np.maximum(np.abs(ref), np.abs(h))
+    ulp = np.exp2(np.floor(np.log2(np.where(m > 0, m, 1.0))) - 7)
+    bad = big & ~(np.abs(h - ref) < ulp)
+    assert not bad.any(), f"{int(bad.sum())} results not faithful, e.g. {h[bad][:4]} vs {ref[bad][:4]}"
+    small = ~big & (np.abs(h) > floor)
+    assert not small.any(), f"{int(small.sum())} tiny results above {floor}: {h[small][:4]}"
+
+
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
     return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)

@@ -26,7 +26,7 @@ import torch
 import mixed_gemm_amd as mg
 import synth
 from oracle import layer
-from tests.gpu_util import bf16_to_f64, check_output, dev, host
+from tests.gpu_util import assert_faithful_bf16, bf16_to_f64, check_output, dev, host
 
 pytestmark = pytest.mark.gpu
 
@@ -139,7 +139,7 @@ def test_block_stagewise(block, layout):
     e0 = check_output(g0["Y"], g0["Y32"], Y64_0)
     # GELU of the GPU's ffn.0 output
     ref_h = layer.gelu_tanh(bf16_to_f64(g0["Y"]))
-    assert np.all(np.abs(bf16_to_f64(hr) - ref_h) <= 2 ** -8 * np.abs(ref_h) + 1e-6)
+    assert_faithful_bf16(bf16_to_f64(hr), ref_h)
     # ffn.2 from the GPU's h
     oq2 = layer.quantize_act(hr, o_p2["s"], o_p2["O"])
     for name in ("Aq", "As", "XO"):
