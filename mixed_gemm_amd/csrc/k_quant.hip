@@ -99,6 +99,19 @@ __global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restr
     // Whole 32-blocks are either in range or not (K % 32 == 0), so the 4 lanes
     // of a quad agree on `valid` and the quad reduction mixes one block only.
     const bool valid = j0 < K;
+    // s, RN(1/s) and pos of the block's 512 channels in LDS, for the lanes
+    // that hold more than one outlier channel (their further channels are
+    // looked up per row; keeping all 8 positions in registers would cost
+    // occupancy).
+    __shared__ float t_s[512], t_r[512];
+    __shared__ int t_p[512];
+    for (int t = threadIdx.x; t < 512; t += 256) {
+        const int j = blockIdx.x * 512 + t;
+        t_s[t] = j < K ? s[j] : 1.0f;
+        t_r[t] = j < K ? rcp[j] : 1.0f;
+        t_p[t] = j < K ? pos[j] : -1;
+    }
+    __syncthreads();
     // the lane's 8 channels: three pairs of 16-byte loads (j0 is a multiple of 8)
     float sv[8] = {1, 1, 1, 1, 1, 1, 1, 1}, rv[8] = {1, 1, 1, 1, 1, 1, 1, 1};
     int pv[8] = {-1, -1, -1, -1, -1, -1, -1, -1};
@@ -126,7 +139,7 @@ __global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restr
     for (int w = 0; w < 4; ++w)
         keepw[w] = ((omask >> (2 * w)) & 1u ? 0u : 0x0000FFFFu) | ((omask >> (2 * w + 1)) & 1u ? 0u : 0xFFFF0000u);
     // The first outlier channel of the lane (if any) is written with one store
-    // per row; further outlier channels of the same lane (rare) take a loop.
+    // per row; further outlier channels of the same lane take one more store each.
     const int oc0 = omask ? __builtin_ctz(omask) : 0;
     float so = sv[0], ro = rv[0];
     int op0 = pv[0];
@@ -187,11 +200,15 @@ __global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restr
                 const float xo = __uint_as_float((oc0 & 1) ? (wo & 0xFFFF0000u) : (wo << 16));
                 const float qo = fast ? div_fast(xo, so, ro) : __fdiv_rn(xo, so);
                 XO[r * k + op0] = (uint16_t)f32_to_bf16_rne(qo);
+                // further outlier channels of the lane (two or more in its 8)
                 for (uint32_t mm = omask_rest; mm; mm &= mm - 1) {
                     const int i = __builtin_ctz(mm);
+                    const int jl = lane * 8 + i;
                     const uint32_t wi = w[i >> 1];
                     const float xi = __uint_as_float((i & 1) ? (wi & 0xFFFF0000u) : (wi << 16));
-                    XO[r * k + pos[j0 + i]] = (uint16_t)f32_to_bf16_rne(__fdiv_rn(xi, s[j0 + i]));
+                    const float si = t_s[jl];
+                    const float qi = fast ? div_fast(xi, si, t_r[jl]) : __fdiv_rn(xi, si);
+                    XO[r * k + t_p[jl]] = (uint16_t)f32_to_bf16_rne(qi);
                 }
             }
             encode_store(q, lane, valid, Aq + r * (K / 2), As + r * (K / 32), j0);

@@ -122,6 +122,35 @@ def test_k_equals_K_is_bf16_gemm():
     assert np.all(g["Aq"] == 0) and np.all(g["Wq"] == 0)
 
 
+@pytest.mark.parametrize("k", [64, 256])
+def test_division_outside_the_fast_range(k):
+    """Values and scales outside the range where x * RN(1/s) with one FMA
+    correction is exact take the correctly rounded division, bit for bit with
+    the oracle: activation channels 2^100 larger (s > 2^20, outliers) and
+    2^110 smaller, weight columns 2^100 larger (s < 2^-20), scattered entries
+    scaled by 2^-128 (bf16 subnormals) and signed zeros; k = 64 and k = K put
+    several outlier channels in many lanes (their further channels have their
+    own path)."""
+    M, K, N = 300, 256, 64
+    X, W = _heavy(M, K, N, 77)
+    g = np.random.default_rng(5)
+    Xf, Wf = bf16_to_f64(X), bf16_to_f64(W)
+    ch = g.permutation(K)
+    Xf[:, ch[:6]] *= 2.0 ** 100
+    Xf[:, ch[6:12]] *= 2.0 ** -110
+    Wf[:, ch[12:18]] *= 2.0 ** 100
+    Xf[g.random((M, K)) < 0.01] *= 2.0 ** -128
+    zero = g.random((M, K)) < 0.005
+    Xf[zero] = np.where(g.random(int(zero.sum())) < 0.5, 0.0, -0.0)
+    X = synth.f32_to_bf16_bits(Xf.astype(np.float32))
+    W = synth.f32_to_bf16_bits(Wf.astype(np.float32))
+    xa = np.abs(bf16_to_f64(X))
+    assert np.any((xa > 0) & (xa < 2.0 ** -126))
+    o = _oracle(X, W, 0.6, k)
+    assert np.any(o["s"] > 2.0 ** 20) and np.any(o["s"] < 2.0 ** -20)
+    _compare(run_pipeline(X, W, 0.6, k), o)
+
+
 def test_sign_symmetry_and_determinism():
     X, W = _heavy(257, 512, 128, 11)
     g1 = run_pipeline(X, W, 0.6, 16)
