@@ -37,11 +37,15 @@ PEAK_FP4_TFLOPS = 10100.0          # MI355X dense MXFP4 MFMA (published)
 PEAK_HBM_GBS = 8000.0              # MI355X HBM3E (published)
 METRIC = "dual-branch W4A4 FFN GEMM effective TFLOPS, % MXFP4 MFMA peak (480p/720p)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dual_gemm_ffn0_480p_traffic.json")
-GEMM_SRC = os.path.join(ROOT, "mixed_gemm_amd", "csrc", "k_gemm.hip")
+# the dual GEMM's sources: its kernel file and the device header it includes
+GEMM_SRCS = [os.path.join(ROOT, "mixed_gemm_amd", "csrc", f) for f in ("k_gemm.hip", "mg_device.h")]
 
 
 def gemm_source_hash() -> str:
-    return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in GEMM_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic() -> float | None:

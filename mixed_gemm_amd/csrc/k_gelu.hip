@@ -1,7 +1,7 @@
 // GELU (tanh form) between the two projections of the FFN block: the
 // calibrated FFN inputs sit after the SiLU/GELU gates ("W4A4 Quantization for
 // Inference on Wan2.2-I2V-A14B", integration paragraph).
-// out = gelu_tanh(y) rounded to bf16 (gelu_bf16: the sigmoid form with the
+// out = gelu_tanh(y) rounded to bf16 (gelu_bf16x2: the sigmoid form with the
 // hardware exp2 and reciprocal), 8 bf16 per lane (16-byte loads and stores).
 // HBM-bound: 4 bytes per element.
 #include "mg_device.h"
@@ -20,12 +20,12 @@ __global__ void __launch_bounds__(256) gelu_kernel(const uint16_t* in,
         const uint32_t w[4] = {d.x, d.y, d.z, d.w};
         uint32_t o[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) o[k] = gelu_bf16(w[k] & 0xFFFFu) | (gelu_bf16(w[k] >> 16) << 16);
+        for (int k = 0; k < 4; ++k) o[k] = gelu_bf16x2(w[k]);
         reinterpret_cast<uint4*>(out)[i] = make_uint4(o[0], o[1], o[2], o[3]);
     }
     // tail (n % 8 elements)
     const int64_t t = nvec * 8 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t < n && (int64_t)blockIdx.x * blockDim.x + threadIdx.x < 8) out[t] = (uint16_t)gelu_bf16(in[t]);
+    if (t < n && (int64_t)blockIdx.x * blockDim.x + threadIdx.x < 8) out[t] = (uint16_t)gelu_bf16x2(in[t]);
 }
 
 }  // namespace

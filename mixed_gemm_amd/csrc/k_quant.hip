@@ -12,10 +12,11 @@
 //
 // Lane layout: a lane owns 8 consecutive channels (16 B of bf16) of a row, 4
 // lanes form one 32-block (amax combined with two quad DPP moves), a wave
-// covers 512 channels of a row and walks rows with a stride, RPI rows per
-// step, the loads of the next step issued before the current one is
-// processed.  The per-channel s, RN(1/s) and outlier masks of a lane's 8
-// channels stay in registers for all of its rows.
+// covers 512 channels of a row and walks rows with a stride, the next row's
+// load issued before the current one is processed.  The per-channel s,
+// RN(1/s) and outlier masks of a lane's 8 channels stay in registers for all
+// of its rows.  Rows are read and written through buffer resources built per
+// row in scalar registers, so channels past K need no per-lane bounds code.
 //
 // With GELU, X is the previous projection's bf16 output and the quantized
 // input is h = gelu_bf16(X) (the FFN block's hidden activation), computed
@@ -38,16 +39,17 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
-constexpr int RPI = 1;            // rows per step
 constexpr int WAVES_PER_CU = 32;  // launch size: about this many waves per CU
 
 // |x| bit patterns of bf16 2^-100 and 2^100 (biased exponents 27 and 227)
 constexpr unsigned short kBf16Lo = 0x0D80, kBf16Hi = 0x7180;
 
-__device__ __forceinline__ float quad_max(float v) {
-    // max over the 4 lanes of a quad (one 32-block): quad_perm [1,0,3,2] then [2,3,0,1]
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
+// Max over the 4 lanes of a quad (one 32-block: quad_perm [1,0,3,2] then
+// [2,3,0,1]) of the bit patterns of non-negative f32 values, whose unsigned
+// integer order is their numeric order.
+__device__ __forceinline__ uint32_t quad_max_bits(uint32_t v) {
+    v = __builtin_elementwise_max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));
+    v = __builtin_elementwise_max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));
     return v;
 }
 
@@ -65,21 +67,28 @@ __device__ __forceinline__ bool bf16x8_in_fast_range(const u32x4& w) {
     return h <= kBf16Hi && l >= (unsigned short)(kBf16Lo - 1);
 }
 
-// E8M0 scale + E2M1 codes of the lane's 8 (masked) quotients; stores the
-// packed nibbles and, from one lane per quad, the block's scale byte.
-__device__ __forceinline__ void encode_store(const float (&q)[8], int lane, bool valid, uint8_t* aq_row,
-                                             uint8_t* as_row, int j0) {
+// E8M0 scale code c of the lane's 32-block and the packed E2M1 nibbles of its
+// 8 (masked) quotients (first value in the low nibble).
+__device__ __forceinline__ uint32_t encode8(const float (&q)[8], uint32_t& c) {
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, __builtin_fabsf(q[i]));
-    amax = quad_max(amax);
-    const uint32_t c = e8m0_from_amax_bits(__float_as_uint(amax));
+    c = e8m0_from_amax_bits(quad_max_bits(__float_as_uint(amax)));
     const float scale = e8m0_to_f32(c);
     uint32_t word = 0;
     MG_CVT_FP4X2(word, q[0], q[1], scale, 0);
     MG_CVT_FP4X2(word, q[2], q[3], scale, 1);
     MG_CVT_FP4X2(word, q[4], q[5], scale, 2);
     MG_CVT_FP4X2(word, q[6], q[7], scale, 3);
+    return word;
+}
+
+// encode8, then the packed nibbles and, from one lane per quad, the block's
+// scale byte are stored.
+__device__ __forceinline__ void encode_store(const float (&q)[8], int lane, bool valid, uint8_t* aq_row,
+                                             uint8_t* as_row, int j0) {
+    uint32_t c;
+    const uint32_t word = encode8(q, c);
     if (valid) {
         *reinterpret_cast<uint32_t*>(aq_row + j0 / 2) = word;
         if ((lane & 3) == 0) as_row[j0 / 32] = (uint8_t)c;
@@ -151,55 +160,58 @@ __global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restr
     }
     const uint32_t omask_rest = omask & (omask - 1);
 
-    const int64_t rstride = (int64_t)gridDim.y * kWaves;
-    const int64_t rstep = rstride * RPI;
-    auto load_rows = [&](int64_t rb, u32x4 (&d)[RPI]) {
-#pragma unroll
-        for (int u = 0; u < RPI; ++u) {
-            const int64_t r = rb + u * rstride;
-            d[u] = u32x4{0, 0, 0, 0};
-            if (valid && r < M)
-                d[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(X + r * K + j0));
-        }
+    // Per-lane byte offsets inside a row.  Rows are addressed through a buffer
+    // resource per row (scalar registers), so lanes whose channels lie past
+    // K read zeros and drop their stores by the hardware range check, and so
+    // do the lanes that store no scale byte or no outlier value (offset
+    // kNoStore).
+    constexpr uint32_t kNoStore = 0x40000000u;
+    const uint32_t offX = 2u * (uint32_t)j0, offAq = (uint32_t)j0 / 2u;
+    const uint32_t offAs = (lane & 3) == 0 ? (uint32_t)j0 / 32u : kNoStore;
+    const uint32_t offXO = omask ? 2u * (uint32_t)op0 : kNoStore;
+    const bool wave_o = __builtin_amdgcn_ballot_w64(omask != 0) != 0;
+    const bool wave_rest = __builtin_amdgcn_ballot_w64(omask_rest != 0) != 0;
+    const uint32_t rowX = 2u * (uint32_t)K, rowAq = (uint32_t)K / 2u, rowAs = (uint32_t)K / 32u,
+                   rowXO = 2u * (uint32_t)k;
+
+    auto rsrc = [](const void* p, uint32_t bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+    };
+    auto load_row = [&](const uint16_t* px, bool in) -> u32x4 {
+        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc(px, in ? rowX : 0u), offX, 0,
+                                                                                2));   // nt
     };
 
-    int64_t r0 = (int64_t)blockIdx.y * kWaves + wave;
-    u32x4 cur[RPI];
-    load_rows(r0, cur);
-    for (; r0 < M; r0 += rstep) {
-        u32x4 nxt[RPI];
-        load_rows(r0 + rstep, nxt);                     // next step's rows in flight meanwhile
+    // one row: w its 8 bf16 per lane, pq/ps/po its Aq, As and XO rows
+    auto process_row = [&](u32x4 w, uint8_t* pq, uint8_t* ps, uint16_t* po) {
+        if constexpr (GELU) {
 #pragma unroll
-        for (int u = 0; u < RPI; ++u) {
-            const int64_t r = r0 + u * rstride;
-            if (r >= M) break;                          // uniform across the wave
-            u32x4 w = cur[u];
-            if constexpr (GELU) {
+            for (int i = 0; i < 4; ++i) w[i] = gelu_bf16x2(w[i]);
+        }
+        const bool fast = s_ok & bf16x8_in_fast_range(w);
+        float x[8], q[8];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) w[i] = gelu_bf16(w[i] & 0xFFFFu) | (gelu_bf16(w[i] >> 16) << 16);
-            }
-            const bool fast = s_ok && bf16x8_in_fast_range(w);
-            float x[8], q[8];
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t m = w[i] & keepw[i];
+            x[2 * i] = __uint_as_float(m << 16);
+            x[2 * i + 1] = __uint_as_float(m & 0xFFFF0000u);
+        }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t m = w[i] & keepw[i];
-                x[2 * i] = __uint_as_float(m << 16);
-                x[2 * i + 1] = __uint_as_float(m & 0xFFFF0000u);
-            }
+        for (int i = 0; i < 8; ++i) q[i] = div_fast(x[i], sv[i], rv[i]);
+        if (!fast) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) q[i] = div_fast(x[i], sv[i], rv[i]);
-            if (!fast) {
+            for (int i = 0; i < 8; ++i) q[i] = __fdiv_rn(x[i], sv[i]);
+        }
+        if (wave_o) {
+            // the first outlier channel's own (unmasked) value from the raw words
+            uint32_t wo = w[0];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) q[i] = __fdiv_rn(x[i], sv[i]);
-            }
-            if (omask) {
-                // the outlier channel's own (unmasked) value from the raw words
-                uint32_t wo = w[0];
-#pragma unroll
-                for (int i = 1; i < 4; ++i) wo = (oc0 >> 1) == i ? w[i] : wo;
-                const float xo = __uint_as_float((oc0 & 1) ? (wo & 0xFFFF0000u) : (wo << 16));
-                const float qo = fast ? div_fast(xo, so, ro) : __fdiv_rn(xo, so);
-                XO[r * k + op0] = (uint16_t)f32_to_bf16_rne(qo);
+            for (int i = 1; i < 4; ++i) wo = (oc0 >> 1) == i ? w[i] : wo;
+            const float xo = __uint_as_float((oc0 & 1) ? (wo & 0xFFFF0000u) : (wo << 16));
+            const float qo = fast ? div_fast(xo, so, ro) : __fdiv_rn(xo, so);
+            const __amdgpu_buffer_rsrc_t rxo = rsrc(po, rowXO);
+            if (omask) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_rne(qo), rxo, offXO, 0, 0);
+            if (wave_rest) {
                 // further outlier channels of the lane (two or more in its 8)
                 for (uint32_t mm = omask_rest; mm; mm &= mm - 1) {
                     const int i = __builtin_ctz(mm);
@@ -208,13 +220,38 @@ __global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restr
                     const float xi = __uint_as_float((i & 1) ? (wi & 0xFFFF0000u) : (wi << 16));
                     const float si = t_s[jl];
                     const float qi = fast ? div_fast(xi, si, t_r[jl]) : __fdiv_rn(xi, si);
-                    XO[r * k + t_p[jl]] = (uint16_t)f32_to_bf16_rne(qi);
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_rne(qi), rxo, 2u * (uint32_t)t_p[jl],
+                                                          0, 0);
                 }
             }
-            encode_store(q, lane, valid, Aq + r * (K / 2), As + r * (K / 32), j0);
         }
-#pragma unroll
-        for (int u = 0; u < RPI; ++u) cur[u] = nxt[u];
+        uint32_t c;
+        const uint32_t word = encode8(q, c);
+        __builtin_amdgcn_raw_buffer_store_b32(word, rsrc(pq, rowAq), offAq, 0, 0);
+        if ((lane & 3) == 0) __builtin_amdgcn_raw_buffer_store_b8((uint8_t)c, rsrc(ps, rowAs), offAs, 0, 0);
+    };
+
+    // Rows r0, r0 + rstride, ...: the next row's load is in flight while the
+    // current one is processed.  Row addresses advance by a fixed stride
+    // (scalar adds).
+    // The wave's row count n is a 32-bit scalar (64-bit scalar compares do
+    // not exist on this architecture).
+    const int64_t rstride = (int64_t)gridDim.y * kWaves;
+    const int64_t r0 = (int64_t)blockIdx.y * kWaves + wave;
+    const int n = r0 < M ? (int)((M - 1 - r0) / rstride) + 1 : 0;
+    const int64_t dX = rstride * K, dQ = rstride * (K / 2), dS = rstride * (K / 32), dO = rstride * k;
+    const uint16_t* px = X + r0 * K;
+    uint8_t* pq = Aq + r0 * (K / 2);
+    uint8_t* ps = As + r0 * (K / 32);
+    uint16_t* po = XO + r0 * k;
+    u32x4 a = load_row(px, n > 0);
+    px += dX;
+    for (int i = 0; i < n; ++i) {
+        const u32x4 b = load_row(px, i + 1 < n);
+        px += dX;
+        process_row(a, pq, ps, po);
+        pq += dQ; ps += dS; po += dO;
+        a = b;
     }
 }
 
@@ -258,8 +295,8 @@ hipError_t launch_quant(const void* X, int32_t dtype, int64_t M, int32_t K, int3
                         uint8_t* As, uint16_t* XO, hipStream_t st, bool gelu) {
     if (M <= 0) return hipSuccess;
     const int64_t gx = ((int64_t)K / 8 + 63) / 64;
-    // about WAVES_PER_CU waves per CU, each wave at least RPI rows
-    int64_t gy = (M + kWaves * RPI - 1) / (kWaves * RPI);
+    // about WAVES_PER_CU waves per CU, each wave at least one row
+    int64_t gy = (M + kWaves - 1) / kWaves;
     int64_t cap = (int64_t)device_cu_count() * (WAVES_PER_CU / kWaves) / gx;
     if (cap < 1) cap = 1;
     if (gy > cap) gy = cap;

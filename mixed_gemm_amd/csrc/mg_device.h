@@ -7,6 +7,14 @@ namespace mg {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
+// Raw buffer resource over `bytes` bytes from p (clamped to 2^32 - 1): loads
+// past the end return 0 and stores past it are dropped by the hardware range
+// check.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint64_t bytes) {
+    const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
+}
+
 // Round-to-nearest-even f32 -> bf16 bits (finite inputs).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);
@@ -66,22 +74,30 @@ __device__ __forceinline__ bool div_fast_ok_x(float x) {
 }
 __device__ __forceinline__ bool div_fast_ok_s(float s) { return s >= 0x1p-20f && s <= 0x1p20f; }
 
-// GELU (tanh form) of one bf16 value, f32 math, rounded to bf16 (nearest
-// even).  0.5 y (1 + tanh u) with u = sqrt(2/pi) (y + 0.044715 y^3) is
-// evaluated as the equal y / (1 + e^(-2u)) = y * sigmoid(2u): one hardware
-// exp2 (v_exp_f32) of t = -2u log2(e) = y (C2 y^2 + C1) and one hardware
-// reciprocal (v_rcp_f32), with no cancellation in 1 + tanh u for negative y.
-// The result is a faithful bf16 rounding of the exact GELU for every finite
-// bf16 input where that is at least 2^-24 in magnitude (smaller results come
-// out as at most 2^-24; very negative y give -0).  The GELU kernel and the
-// fused GELU + quantize path both use this, so their outputs are the same bits.
-__device__ __forceinline__ uint32_t gelu_bf16(uint32_t b) {
+// GELU (tanh form) in f32 of one value: 0.5 y (1 + tanh u) with
+// u = sqrt(2/pi) (y + 0.044715 y^3), evaluated as the equal
+// y / (1 + e^(-2u)) = y * sigmoid(2u): one hardware exp2 (v_exp_f32) of
+// t = -2u log2(e) = y (C2 y^2 + C1) and one hardware reciprocal (v_rcp_f32),
+// with no cancellation in 1 + tanh u for negative y.
+__device__ __forceinline__ float gelu_f32(float y) {
     constexpr float C1 = -2.302208198144325f;    // -2 sqrt(2/pi) log2(e)
     constexpr float C2 = -0.1029432395800235f;   // 0.044715 C1
-    const float y = bf16_to_f32(b);
     const float t = y * __builtin_fmaf(C2, y * y, C1);
-    const float e = __builtin_amdgcn_exp2f(t);
-    return f32_to_bf16_rne(y * __builtin_amdgcn_rcpf(1.0f + e));
+    return y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
+}
+
+typedef __bf16 mg_bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float mg_f32x2_t __attribute__((ext_vector_type(2)));
+
+// GELU of the two bf16 values packed in w (first in the low half), each
+// rounded to bf16 (nearest even, v_cvt_pk_bf16_f32).  The result is a
+// faithful bf16 rounding of the exact GELU for every finite bf16 input where
+// that is at least 2^-24 in magnitude (smaller results come out as at most
+// 2^-24; very negative y give -0).  The GELU kernel and the fused GELU +
+// quantize path both use this, so their outputs are the same bits.
+__device__ __forceinline__ uint32_t gelu_bf16x2(uint32_t w) {
+    const mg_f32x2_t v = {gelu_f32(__uint_as_float(w << 16)), gelu_f32(__uint_as_float(w & 0xFFFF0000u))};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, mg_bf16x2_t));
 }
 
 // E8M0 code c -> the f32 scale 2^(c - 127) (c = 0 gives the subnormal 2^-127).
