@@ -208,9 +208,12 @@ struct TileOrg {
     int n0;
 };
 
-// K8: k % 8 == 0 (outlier rows are whole 16-byte chunks); NB16: (K/32) % 16
-// == 0 (every scale window of a row is one aligned 16-byte chunk).
-template <typename OutT, bool K8, bool NB16>
+// K8: k % 8 == 0 (outlier rows are whole 16-byte chunks).  SA: alignment of
+// the scale rows (K/32 bytes) -- 16 when every scale window of a row is one
+// aligned 16-byte chunk (one direct-to-LDS copy per row), 4 when it is four
+// aligned 4-byte words (four copies), else 1 (bytes gathered through
+// registers, which waits for the stage's copies in flight).
+template <typename OutT, bool K8, int SA>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 dual_gemm_tiled(GemmArgs g) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -295,7 +298,7 @@ dual_gemm_tiled(GemmArgs g) {
         const int slot = wiss & 1;
         ++wiss;
         uint8_t* dst = lds + SCW_OFF + slot * SCW_BYTES + wave * 64 * SCW_ROWB;
-        if constexpr (NB16) {
+        if constexpr (SA == 16) {
             uint32_t r = lwr;
             asm volatile("" : "+v"(r));
             const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)w * SCW_ROWB);
@@ -304,8 +307,27 @@ dual_gemm_tiled(GemmArgs g) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rAs, (lds_ptr_t)dst, 16, (ra + r) * (uint32_t)nb, so, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rBs, (lds_ptr_t)(dst + TBM * SCW_ROWB), 16,
                                                      (rb + r) * (uint32_t)nb, so, 0, 0);
+        } else if constexpr (SA == 4) {
+            // rows 4-byte aligned: four 4-byte copies per operand; copy i moves
+            // rows 16 i + L/4 of the wave's 64, lane L landing at byte 256 i + 4 L
+            // (row byte 4 (L % 4)).  Bytes past the row's nb read as zero.
+            const uint32_t col = (uint32_t)w * SCW_ROWB + 4u * (uint32_t)(lane & 3);
+            const bool colok = col < (uint32_t)nb;
+            uint32_t r = (uint32_t)(wave * 64) + (uint32_t)(lane >> 2);
+            asm volatile("" : "+v"(r));
+            const uint32_t ra = __builtin_amdgcn_readfirstlane((uint32_t)o.m0);
+            const uint32_t rb = __builtin_amdgcn_readfirstlane((uint32_t)o.n0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t ri = r + 16u * (uint32_t)i;
+                const uint32_t va = colok ? (ra + ri) * (uint32_t)nb + col : OOB;
+                const uint32_t vb = colok ? (rb + ri) * (uint32_t)nb + col : OOB;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rAs, (lds_ptr_t)(dst + 256 * i), 4, va, 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rBs, (lds_ptr_t)(dst + TBM * SCW_ROWB + 256 * i), 4, vb, 0,
+                                                         0, 0);
+            }
         } else {
-            // rows not 16-byte aligned: gather the bytes, store through registers
+            // rows not 4-byte aligned: gather the bytes, store through registers
             const int64_t ra = o.m0 + lwr, rb = (int64_t)o.n0 + lwr;
             uint32_t wa[4], wb[4];
 #pragma unroll
@@ -671,13 +693,13 @@ dual_gemm_tiled(GemmArgs g) {
     }
 }
 
-template <typename OutT, bool K8, bool NB16>
+template <typename OutT, bool K8, int SA>
 static hipError_t launch_tiled(const GemmArgs& a, hipStream_t st) {
     static thread_local int configured_dev = -1;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return hipErrorNoDevice;
     if (configured_dev != dev) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dual_gemm_tiled<OutT, K8, NB16>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dual_gemm_tiled<OutT, K8, SA>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_LDS_BYTES);
         if (e != hipSuccess) return e;
         configured_dev = dev;
@@ -686,7 +708,7 @@ static hipError_t launch_tiled(const GemmArgs& a, hipStream_t st) {
     const int per = (T + NXCD - 1) / NXCD;
     const int cus_per_xcd = device_cu_count() / NXCD;
     const int wg_per_xcd = per < cus_per_xcd ? per : (cus_per_xcd > 0 ? cus_per_xcd : 1);
-    hipLaunchKernelGGL((dual_gemm_tiled<OutT, K8, NB16>), dim3((unsigned)(wg_per_xcd * NXCD)), dim3(256),
+    hipLaunchKernelGGL((dual_gemm_tiled<OutT, K8, SA>), dim3((unsigned)(wg_per_xcd * NXCD)), dim3(256),
                        GEMM_LDS_BYTES, st, a);
     return hipGetLastError();
 }
@@ -694,11 +716,16 @@ static hipError_t launch_tiled(const GemmArgs& a, hipStream_t st) {
 template <typename OutT>
 static hipError_t launch_tiled_t(const GemmArgs& a, hipStream_t st) {
     const bool k8 = a.k % 8 == 0;
-    const bool nb16 = (a.K / 32) % 16 == 0;
-    if (k8 && nb16) return launch_tiled<OutT, true, true>(a, st);
-    if (k8) return launch_tiled<OutT, true, false>(a, st);
-    if (nb16) return launch_tiled<OutT, false, true>(a, st);
-    return launch_tiled<OutT, false, false>(a, st);
+    const int nb = a.K / 32;
+    const int sa = nb % 16 == 0 ? 16 : nb % 4 == 0 ? 4 : 1;
+    if (k8) {
+        if (sa == 16) return launch_tiled<OutT, true, 16>(a, st);
+        if (sa == 4) return launch_tiled<OutT, true, 4>(a, st);
+        return launch_tiled<OutT, true, 1>(a, st);
+    }
+    if (sa == 16) return launch_tiled<OutT, false, 16>(a, st);
+    if (sa == 4) return launch_tiled<OutT, false, 4>(a, st);
+    return launch_tiled<OutT, false, 1>(a, st);
 }
 
 }  // namespace
