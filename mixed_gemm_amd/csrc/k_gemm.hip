@@ -208,12 +208,15 @@ struct TileOrg {
     int n0;
 };
 
-// K8: k % 8 == 0 (outlier rows are whole 16-byte chunks).  SA: alignment of
+// OA: alignment of the outlier rows (2k bytes) -- 16 when k % 8 == 0 (whole
+// 16-byte chunks, one direct-to-LDS copy each), 4 when k is even (four
+// 4-byte copies per chunk), else 2 (values gathered through registers, which
+// waits for the stage's copies in flight).  SA: alignment of
 // the scale rows (K/32 bytes) -- 16 when every scale window of a row is one
 // aligned 16-byte chunk (one direct-to-LDS copy per row), 4 when it is four
 // aligned 4-byte words (four copies), else 1 (bytes gathered through
 // registers, which waits for the stage's copies in flight).
-template <typename OutT, bool K8, int SA>
+template <typename OutT, int OA, int SA>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 dual_gemm_tiled(GemmArgs g) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -263,6 +266,11 @@ dual_gemm_tiled(GemmArgs g) {
     const uint32_t c16o = c16e ^ 64u;                                          // odd groups
     const uint32_t lrA0 = (uint32_t)(wave * 64 + lrow) * rowA;                 // copy row (group 0)
     const uint32_t lrX0 = (uint32_t)(wave * 64 + lrow) * rowX;
+    // 4-byte outlier copies (OA == 4): copy i of an 8-row group moves group
+    // rows 2 i + L/32, lane L landing at byte 4 (L % 32) of its row, i.e.
+    // physical chunk (L % 32) / 4, word L % 4.
+    const uint32_t lrX4 = (uint32_t)(wave * 64 + (lane >> 5)) * rowX + 4u * (uint32_t)(lane & 3);
+    const uint32_t pc4 = (uint32_t)((lane & 31) >> 2);
     const uint32_t lds_w = (uint32_t)(wave * 64 * ROWB);
     // scale windows: lane L of wave w copies window row 64 w + L of A and of
     // B; a lane reads its fragment rows' 8 bytes at these offsets (+ 512 i)
@@ -397,6 +405,21 @@ dual_gemm_tiled(GemmArgs g) {
         const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)(bulk ? nc.st : nc.st - S4) * ROWB);
         const uint32_t r0 = __builtin_amdgcn_readfirstlane((isB ? (uint32_t)nc.o.n0 : (uint32_t)nc.o.m0) * rowb);
         const uint32_t c = (part & 1) ? c16o : c16e;
+        if constexpr (OA == 4) {
+            if (!bulk) {
+                // outlier rows 4-byte aligned: four 4-byte copies (two rows each)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t b16 = (pc4 ^ (uint32_t)(i + 4 * (part & 1))) << 4;   // logical chunk
+                    const uint32_t off = b16 + 4u * (uint32_t)(lane & 3);
+                    const bool ok4 = nc.st >= 0 && so + off < rowb;
+                    const uint32_t v4 = ok4 ? lrX4 + b16 + r0 + (uint32_t)(8 * part + 2 * i) * rowb : OOB;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(isB ? rWO : rXO, (lds_ptr_t)(dst + 256 * i), 4, v4, so,
+                                                             0, 0);
+                }
+                return;
+            }
+        }
         const bool ok = nc.st >= 0 && so + c < rowb;      // chunks past K / k read as zero
         const uint32_t v = ok ? lr + c + r0 + (uint32_t)part * 8 * rowb : OOB;
         if (bulk)
@@ -439,7 +462,7 @@ dual_gemm_tiled(GemmArgs g) {
     // All copies of stage nc at once (the very first stage), with the scale
     // window it opens.
     auto load_stage = [&](const NextCopy& nc, int b) {
-        if (!K8 && nc.st >= S4) {
+        if (OA == 2 && nc.st >= S4) {
             gather_outlier(nc.o, nc.st - S4, b);
         } else {
 #pragma unroll
@@ -496,7 +519,7 @@ dual_gemm_tiled(GemmArgs g) {
         const uint8_t* base = lds + b * STAGE_BYTES;
         const uint8_t* wsc = nullptr;
         if constexpr (cb) wsc = window_of(st);
-        const bool dma_next = K8 || nc.st < S4;
+        const bool dma_next = OA != 2 || nc.st < S4;
         const bool opens_window = nc.st >= 0 && nc.st < S4 && (nc.st & 1) == 0;
         static_for<80>([&](auto QC) {
             constexpr int q = decltype(QC)::value;
@@ -526,7 +549,7 @@ dual_gemm_tiled(GemmArgs g) {
                 if constexpr (q >= 2 && q <= 32 && q % 2 == 0) {
                     if (dma_next) copy_part(nc, b ^ 1, (q - 2) >> 2, ((q - 2) & 2) != 0);
                 }
-                if constexpr (!K8 && q == 2) {
+                if constexpr (OA == 2 && q == 2) {
                     if (!dma_next) gather_outlier(nc.o, nc.st - S4, b ^ 1);
                 }
                 if constexpr (q == 36) {
@@ -693,13 +716,13 @@ dual_gemm_tiled(GemmArgs g) {
     }
 }
 
-template <typename OutT, bool K8, int SA>
+template <typename OutT, int OA, int SA>
 static hipError_t launch_tiled(const GemmArgs& a, hipStream_t st) {
     static thread_local int configured_dev = -1;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return hipErrorNoDevice;
     if (configured_dev != dev) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dual_gemm_tiled<OutT, K8, SA>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dual_gemm_tiled<OutT, OA, SA>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_LDS_BYTES);
         if (e != hipSuccess) return e;
         configured_dev = dev;
@@ -708,24 +731,29 @@ static hipError_t launch_tiled(const GemmArgs& a, hipStream_t st) {
     const int per = (T + NXCD - 1) / NXCD;
     const int cus_per_xcd = device_cu_count() / NXCD;
     const int wg_per_xcd = per < cus_per_xcd ? per : (cus_per_xcd > 0 ? cus_per_xcd : 1);
-    hipLaunchKernelGGL((dual_gemm_tiled<OutT, K8, SA>), dim3((unsigned)(wg_per_xcd * NXCD)), dim3(256),
+    hipLaunchKernelGGL((dual_gemm_tiled<OutT, OA, SA>), dim3((unsigned)(wg_per_xcd * NXCD)), dim3(256),
                        GEMM_LDS_BYTES, st, a);
     return hipGetLastError();
 }
 
 template <typename OutT>
 static hipError_t launch_tiled_t(const GemmArgs& a, hipStream_t st) {
-    const bool k8 = a.k % 8 == 0;
+    const int oa = a.k % 8 == 0 ? 16 : a.k % 2 == 0 ? 4 : 2;
     const int nb = a.K / 32;
     const int sa = nb % 16 == 0 ? 16 : nb % 4 == 0 ? 4 : 1;
-    if (k8) {
-        if (sa == 16) return launch_tiled<OutT, true, 16>(a, st);
-        if (sa == 4) return launch_tiled<OutT, true, 4>(a, st);
-        return launch_tiled<OutT, true, 1>(a, st);
+    if (oa == 16) {
+        if (sa == 16) return launch_tiled<OutT, 16, 16>(a, st);
+        if (sa == 4) return launch_tiled<OutT, 16, 4>(a, st);
+        return launch_tiled<OutT, 16, 1>(a, st);
     }
-    if (sa == 16) return launch_tiled<OutT, false, 16>(a, st);
-    if (sa == 4) return launch_tiled<OutT, false, 4>(a, st);
-    return launch_tiled<OutT, false, 1>(a, st);
+    if (oa == 4) {
+        if (sa == 16) return launch_tiled<OutT, 4, 16>(a, st);
+        if (sa == 4) return launch_tiled<OutT, 4, 4>(a, st);
+        return launch_tiled<OutT, 4, 1>(a, st);
+    }
+    if (sa == 16) return launch_tiled<OutT, 2, 16>(a, st);
+    if (sa == 4) return launch_tiled<OutT, 2, 4>(a, st);
+    return launch_tiled<OutT, 2, 1>(a, st);
 }
 
 }  // namespace
