@@ -52,6 +52,25 @@ def act_max(X: np.ndarray, prev: np.ndarray | None = None) -> np.ndarray:
     return a if prev is None else np.maximum(prev, a)
 
 
+def act_percentile(batches, q: float) -> np.ndarray:
+    """Per-input-channel tail statistic for the channel mask: the q-quantile of
+    |x_tj| over every calibration row t of every batch (the tail-aware
+    percentile calibration page: a percentile of the activation tail builds
+    the channel mask, damping rare calibration outliers; it gives no formula
+    and no level).
+
+    Reading: nearest rank.  With T rows in total, the value of rank
+    r = ceil(q T) (1-based, clamped to [1, T]) in ascending order of |x_tj|,
+    for 0 < q <= 1; q = 1 is the maximum a_j.  bf16 (or f32) inputs, f32 out
+    (exact: the result is one of the inputs' magnitudes)."""
+    assert 0.0 < q <= 1.0
+    xs = np.concatenate([np.abs(as_f32(X)) for X in batches], axis=0)
+    assert np.all(np.isfinite(xs))
+    T = xs.shape[0]
+    r = min(T, max(1, math.ceil(q * T)))
+    return np.sort(xs, axis=0)[r - 1].astype(np.float32)
+
+
 def weight_range(W: np.ndarray) -> np.ndarray:
     """Weight column range of input channel j.  Reading: max_n |W[n][j]| (the
     magnitude counterpart of the activation maximum in Eq. (2))."""
@@ -136,9 +155,13 @@ def fold_pack(W: np.ndarray, s: np.ndarray, O: np.ndarray, layout: str = "1x32")
 
 
 def plan(a: np.ndarray, w: np.ndarray, W: np.ndarray, alpha: float, k: int,
-         layout: str = "1x32", smooth: bool = True, score: str = "max") -> dict:
+         layout: str = "1x32", smooth: bool = True, score: str = "max",
+         rank: np.ndarray | None = None) -> dict:
+    """Eq. (2) scales from the maxima a; Eq. (4) ranks a, or the per-channel
+    statistic ``rank`` when given (e.g. act_percentile), raw or divided by s
+    (``score``); then the fold and packing."""
     s, rcp = smooth_scales(a, w, alpha, smooth)
-    O, pos = outlier_set(outlier_score(a, s, score), k)
+    O, pos = outlier_set(outlier_score(a if rank is None else rank, s, score), k)
     p = dict(s=s, rcp=rcp, O=O, pos=pos)
     p.update(fold_pack(W, s, O, layout))
     return p

@@ -351,3 +351,70 @@ def test_smoothed_score_ranks_by_product():
     s, _ = layer.smooth_scales(a_x, w, 0.6)
     q = layer.as_f32(X) / s[None, :]
     assert np.array_equal(layer.outlier_score(a_x, s, "smoothed"), np.abs(q).max(axis=0).astype(np.float32))
+
+
+# ----------------------------------------------------------------------------- percentile statistic
+
+def _percentile_by_counting(cols, q):
+    """The nearest-rank q-quantile written as a count: the smallest value v
+    among the column's magnitudes with #{t : |x_t| <= v} >= ceil(q T)."""
+    out = []
+    for c in cols:
+        mags = [abs(float(x)) for x in c]
+        T = len(mags)
+        r = min(T, max(1, math.ceil(q * T)))
+        out.append(min(v for v in mags if sum(1 for u in mags if u <= v) >= r))
+    return out
+
+
+@pytest.mark.parametrize("q", [0.5, 0.9, 0.99, 0.999, 1.0, 1e-9])
+def test_act_percentile_bruteforce(q):
+    g = np.random.default_rng(11)
+    X = _bf16((g.standard_normal((53, 9)) * np.exp(g.uniform(-3, 3, 9))[None, :]).astype(np.float32))
+    X[g.random(X.shape) < 0.2] = 0x8000                    # signed zeros and ties at 0
+    X[:7, 4] = X[7, 4]                                     # ties in the middle
+    got = layer.act_percentile([X], q)
+    want = _percentile_by_counting(layer.as_f32(X).T, q)
+    assert got.tolist() == want
+
+
+def test_act_percentile_special_cases_and_batches():
+    g = np.random.default_rng(12)
+    X = _bf16((g.standard_normal((300, 16)) * 3.0).astype(np.float32))
+    parts = [X[:120], X[120:121], X[121:]]
+    # q = 1 is the running maximum over the batches; q <= 1/T the minimum magnitude
+    assert np.array_equal(layer.act_percentile(parts, 1.0),
+                          layer.act_max(parts[2], layer.act_max(parts[1], layer.act_max(parts[0]))))
+    assert np.array_equal(layer.act_percentile(parts, 1.0 / 300), np.abs(layer.as_f32(X)).min(axis=0))
+    # the statistic of the union: independent of how rows are split or ordered
+    perm = g.permutation(300)
+    for q in (0.3, 0.95, 0.999):
+        whole = layer.act_percentile([X], q)
+        assert np.array_equal(layer.act_percentile(parts, q), whole)
+        assert np.array_equal(layer.act_percentile([X[perm[:77]], X[perm[77:]]], q), whole)
+
+
+def test_act_percentile_closed_form():
+    """A column holding c, 2c, ..., Tc (shuffled, signs mixed): the q-quantile
+    of rank ceil(q T) is ceil(q T) c exactly."""
+    T = 200
+    g = np.random.default_rng(13)
+    c = 0.125
+    vals = (np.arange(1, T + 1) * c * np.where(g.random(T) < 0.5, -1.0, 1.0)).astype(np.float32)
+    X = _bf16(g.permutation(vals)[:, None])
+    for q in (0.5, 0.9, 0.955, 0.995, 1.0):
+        assert float(layer.act_percentile([X], q)[0]) == math.ceil(q * T) * c
+
+
+def test_plan_ranks_the_given_statistic():
+    """Eq. (4) over a percentile statistic: O is the top-k of that statistic,
+    while s still comes from the maxima."""
+    X, W, _ = _small_layer(64, 96, 8, 14)
+    a, w = layer.act_max(X), layer.weight_range(W)
+    pct = layer.act_percentile([X], 0.9)
+    p = layer.plan(a, w, W, 0.5, 6, rank=pct)
+    O, _ = layer.outlier_set(pct, 6)
+    s, _ = layer.smooth_scales(a, w, 0.5)
+    assert np.array_equal(p["O"], O) and np.array_equal(p["s"], s)
+    ps = layer.plan(a, w, W, 0.5, 6, score="smoothed", rank=pct)
+    assert np.array_equal(ps["O"], layer.outlier_set(layer.outlier_score(pct, s, "smoothed"), 6)[0])
