@@ -140,6 +140,49 @@ int mg_calib_act(const void* X, int32_t dtype, int64_t M, int32_t K, float* act_
 int mg_weight_range(const void* W, int32_t dtype, int32_t N, int32_t K, float* w_max,
                     hipStream_t stream);
 
+/* ---- percentile calibration statistic: an alternative score for Eq. (4)'s
+ * top-k (the tail-aware percentile calibration page builds its channel mask
+ * from a percentile of the activation tail, to damp rare calibration
+ * outliers; it gives no formula or level -- the reading here is the nearest
+ * rank). ----
+ *
+ * score[j] = the value of rank r = ceil(q T) (1-based, clamped to [1, T]) in
+ * ascending order of |x_tj| over all T calibration rows of all batches, for
+ * 0 < q <= 1 (q = 1 gives act_max; r is computed in double precision).  The
+ * result is exact (one of the inputs' magnitudes), by a two-pass radix
+ * selection on the bf16 bit patterns of |x|:
+ *   mg_pct_reset; mg_pct_count(pass 0) on every batch; mg_pct_select(pass 0);
+ *                 mg_pct_count(pass 1) on every batch; mg_pct_select(pass 1).
+ * Pass 0 counts, per channel, the high byte of each |x|; its select finds the
+ * byte holding rank r and the rank inside it, and clears the counts; pass 1
+ * counts the low bits of the values with that high byte; its select writes
+ * score.  Both passes must see the same rows (in any order and split);
+ * otherwise the result is unspecified (NaN where a rank is not found).  With
+ * no rows counted, score is 0.  bf16 X only.  The score may be passed to
+ * mg_outlier_set in place of act_max (s still comes from act_max).
+ *
+ * State, caller-owned device memory: hist [K][256] u32 (1 KiB per channel),
+ * sel [K][2] i32 (selected high byte, rank inside it).  One state serves one
+ * statistic at a time; calls on one state must be stream-ordered. */
+typedef struct {
+    uint32_t* hist;      /* [K][256] */
+    int32_t* sel;        /* [K][2]   */
+    int32_t K;           /* multiple of 32 */
+    int32_t reserved;    /* 0 */
+} mg_pct;
+
+/* Clears hist: the start of a percentile calibration run. */
+int mg_pct_reset(const mg_pct* st, hipStream_t stream);
+
+/* Adds the M rows of X [M][K] (bf16) to pass `pass` (0 or 1).  M == 0 is a
+ * no-op.  Pass 1 reads sel (written by mg_pct_select pass 0). */
+int mg_pct_count(const mg_pct* st, int32_t pass, const uint16_t* X, int64_t M, hipStream_t stream);
+
+/* Pass 0: from the counts and q, sel := (high byte, rank inside it) per
+ * channel, and hist is cleared (score unused, may be NULL).  Pass 1:
+ * score[0..K) := the statistic (q unused).  q must lie in (0, 1]. */
+int mg_pct_select(const mg_pct* st, int32_t pass, double q, float* score, hipStream_t stream);
+
 /* ---- planning (offline, once per layer) ---- */
 
 /* Eq. (2): s, rcp from act_max and w_max (floor 1e-5 on both before the

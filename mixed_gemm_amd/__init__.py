@@ -53,10 +53,15 @@ class mg_act(ctypes.Structure):
     _fields_ = [("Aq", ctypes.c_void_p), ("As", ctypes.c_void_p), ("XO", ctypes.c_void_p)]
 
 
+class mg_pct(ctypes.Structure):
+    _fields_ = [("hist", ctypes.c_void_p), ("sel", ctypes.c_void_p), ("K", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
 EXPORTS = ("mg_version", "mg_last_error", "mg_plan_bytes", "mg_act_bytes", "mg_calib_reset",
            "mg_calib_act", "mg_weight_range", "mg_smooth_scales", "mg_outlier_set", "mg_fold_pack",
            "mg_plan_build", "mg_quantize_act", "mg_dual_gemm", "mg_forward", "mg_gelu_tanh_bf16",
-           "mg_gelu_quantize_act")
+           "mg_gelu_quantize_act", "mg_pct_reset", "mg_pct_count", "mg_pct_select")
 
 _lib = None
 
@@ -87,6 +92,9 @@ def lib() -> ctypes.CDLL:
             "mg_forward": ([P(mg_plan), vp, i32, i64, P(mg_act), vp, i32, vp], ctypes.c_int),
             "mg_gelu_tanh_bf16": ([vp, vp, i64, vp], ctypes.c_int),
             "mg_gelu_quantize_act": ([P(mg_plan), vp, i64, P(mg_act), vp], ctypes.c_int),
+            "mg_pct_reset": ([P(mg_pct), vp], ctypes.c_int),
+            "mg_pct_count": ([P(mg_pct), i32, vp, i64, vp], ctypes.c_int),
+            "mg_pct_select": ([P(mg_pct), i32, ctypes.c_double, vp, vp], ctypes.c_int),
         }
         missing = set(EXPORTS) - set(sig)
         if missing:                       # an undeclared signature would truncate 64-bit pointers
@@ -271,7 +279,55 @@ def mg_gelu_quantize_act(plan: Plan, Y: torch.Tensor, act: Act, stream=None) -> 
     _check(lib().mg_gelu_quantize_act(ctypes.byref(p), _ptr(Y), Y.shape[0], ctypes.byref(a), _stream(stream)))
 
 
+class PctState:
+    """Device state of one percentile calibration run: hist [K][256] u32
+    counts (stored as int32) and sel [K][2] (selected high byte, rank)."""
+
+    def __init__(self, K: int, device="cuda"):
+        self.K = K
+        self.hist = torch.empty((K, 256), dtype=torch.int32, device=device)
+        self.sel = torch.empty((K, 2), dtype=torch.int32, device=device)
+
+    def c(self) -> mg_pct:
+        return mg_pct(_ptr(self.hist), _ptr(self.sel), self.K, 0)
+
+
+def mg_pct_reset(st: PctState, stream=None) -> None:
+    c = st.c()
+    _check(lib().mg_pct_reset(ctypes.byref(c), _stream(stream)))
+
+
+def mg_pct_count(st: PctState, pass_: int, X: torch.Tensor, stream=None) -> None:
+    if X.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise ValueError("bf16 input expected")
+    if X.dim() != 2 or X.shape[1] != st.K:
+        raise ValueError(f"X must be [M][{st.K}]")
+    c = st.c()
+    _check(lib().mg_pct_count(ctypes.byref(c), pass_, _ptr(X), X.shape[0], _stream(stream)))
+
+
+def mg_pct_select(st: PctState, pass_: int, q: float, score: torch.Tensor | None = None, stream=None) -> None:
+    c = st.c()
+    _check(lib().mg_pct_select(ctypes.byref(c), pass_, float(q), _ptr(score), _stream(stream)))
+
+
 # ----------------------------------------------------------------------------- convenience
+
+def percentile(batches, K: int, q: float, device="cuda", stream=None) -> torch.Tensor:
+    """Per-channel nearest-rank q-quantile of |x| over all rows of the given
+    [M][K] bf16 device tensors (two passes over the batches)."""
+    batches = list(batches)
+    st = PctState(K, device)
+    score = torch.empty(K, dtype=torch.float32, device=device)
+    mg_pct_reset(st, stream)
+    for X in batches:
+        mg_pct_count(st, 0, X, stream)
+    mg_pct_select(st, 0, q, None, stream)
+    for X in batches:
+        mg_pct_count(st, 1, X, stream)
+    mg_pct_select(st, 1, q, score, stream)
+    return score
+
 
 def calibrate(batches, K: int, device="cuda", stream=None) -> torch.Tensor:
     """Running per-channel activation maxima over an iterable of [M][K] device tensors."""
@@ -283,14 +339,20 @@ def calibrate(batches, K: int, device="cuda", stream=None) -> torch.Tensor:
 
 
 def plan(act_max: torch.Tensor, W: torch.Tensor, alpha: float, k: int, layout: str = "1x32",
-         smooth: bool = True, stream=None, score: str = "max") -> Plan:
-    """calibrated maxima + weights -> a built plan (weight ranges, Eq. (2), Eq. (4), fold + pack)."""
+         smooth: bool = True, stream=None, score: str = "max", rank: torch.Tensor | None = None) -> Plan:
+    """calibrated maxima + weights -> a built plan (weight ranges, Eq. (2), Eq. (4), fold + pack).
+    Eq. (4) ranks act_max, or the per-channel statistic ``rank`` when given (e.g. percentile())."""
     N, K = W.shape
     desc = make_desc(K, N, k, alpha, layout, smooth, score)
     p = Plan.empty(desc, W.device)
     w_max = torch.empty(K, dtype=torch.float32, device=W.device)
     mg_weight_range(W, w_max, stream)
-    mg_plan_build(p, act_max, w_max, W, stream)
+    if rank is None:
+        mg_plan_build(p, act_max, w_max, W, stream)
+    else:
+        mg_smooth_scales(p, act_max, w_max, stream)
+        mg_outlier_set(p, rank, stream)
+        mg_fold_pack(p, W, stream)
     return p
 
 

@@ -173,6 +173,45 @@ int mg_weight_range(const void* W, int32_t dtype, int32_t N, int32_t K, float* w
     return h == hipSuccess ? MG_OK : hip_fail(h, "mg_weight_range");
 }
 
+static int check_pct(const mg_pct* st) {
+    if (st == nullptr) return fail(MG_ERR_ARG, "mg_pct: null pointer");
+    if (int e = check_K(st->K)) return e;
+    if (st->reserved != 0) return fail(MG_ERR_ARG, "mg_pct.reserved must be 0");
+    MG_CHECK_PTR(st->hist, "mg_pct.hist");
+    MG_CHECK_PTR(st->sel, "mg_pct.sel");
+    return MG_OK;
+}
+
+static int check_pass(int32_t pass) {
+    if (pass != 0 && pass != 1) return fail(MG_ERR_ARG, "pass=%d must be 0 or 1", pass);
+    return MG_OK;
+}
+
+int mg_pct_reset(const mg_pct* st, hipStream_t stream) {
+    if (int e = check_pct(st)) return e;
+    hipError_t h = mg::launch_pct_reset(st->hist, st->K, stream);
+    return h == hipSuccess ? MG_OK : hip_fail(h, "mg_pct_reset");
+}
+
+int mg_pct_count(const mg_pct* st, int32_t pass, const uint16_t* X, int64_t M, hipStream_t stream) {
+    if (int e = check_pct(st)) return e;
+    if (int e = check_pass(pass)) return e;
+    if (M < 0) return fail(MG_ERR_SHAPE, "M=%lld must be >= 0", (long long)M);
+    if (M == 0) return MG_OK;
+    MG_CHECK_PTR(X, "X");
+    hipError_t h = mg::launch_pct_count(X, M, st->K, pass, st->sel, st->hist, stream);
+    return h == hipSuccess ? MG_OK : hip_fail(h, "mg_pct_count");
+}
+
+int mg_pct_select(const mg_pct* st, int32_t pass, double q, float* score, hipStream_t stream) {
+    if (int e = check_pct(st)) return e;
+    if (int e = check_pass(pass)) return e;
+    if (!(q > 0.0 && q <= 1.0)) return fail(MG_ERR_ARG, "q=%g must lie in (0, 1]", q);
+    if (pass == 1) MG_CHECK_PTR(score, "score");
+    hipError_t h = mg::launch_pct_select(st->K, pass, q, st->hist, st->sel, pass == 1 ? score : nullptr, stream);
+    return h == hipSuccess ? MG_OK : hip_fail(h, "mg_pct_select");
+}
+
 int mg_smooth_scales(const mg_plan* p, const float* act_max, const float* w_max, hipStream_t stream) {
     if (int e = check_plan(p, false)) return e;
     if (p->d.smooth) {

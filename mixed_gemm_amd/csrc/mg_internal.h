@@ -29,6 +29,11 @@ hipError_t launch_dual_gemm(const uint8_t* Aq, const uint8_t* As, const uint16_t
                             int32_t N, int32_t K, int32_t k, void* Y, int32_t y_dtype,
                             hipStream_t st);
 hipError_t launch_gelu(const uint16_t* in, uint16_t* out, int64_t n, hipStream_t st);
+hipError_t launch_pct_reset(uint32_t* hist, int32_t K, hipStream_t st);
+hipError_t launch_pct_count(const uint16_t* X, int64_t M, int32_t K, int pass, const int32_t* sel, uint32_t* hist,
+                            hipStream_t st);
+hipError_t launch_pct_select(int32_t K, int pass, double q, uint32_t* hist, int32_t* sel, float* score,
+                             hipStream_t st);
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();

@@ -127,3 +127,22 @@ def test_tile_layout_needs_wst():
     d = mg.make_desc(64, 64, 4, 0.5, "32x32")
     p = mg.mg_plan(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE)
     assert L.mg_fold_pack(ctypes.byref(p), FAKE, 1, None) == -1
+
+
+def test_percentile_state_validation():
+    L = mg.lib()
+    st = mg.mg_pct(FAKE, FAKE, 64, 0)
+    assert L.mg_pct_select(ctypes.byref(st), 0, 0.0, None, None) == -1        # q must lie in (0, 1]
+    assert L.mg_pct_select(ctypes.byref(st), 0, 1.5, None, None) == -1
+    assert L.mg_pct_select(ctypes.byref(st), 0, float("nan"), None, None) == -1
+    assert L.mg_pct_select(ctypes.byref(st), 1, 0.5, None, None) == -1        # pass 1 writes score
+    assert L.mg_pct_select(ctypes.byref(st), 2, 0.5, FAKE, None) == -1        # pass 0 or 1
+    assert L.mg_pct_count(ctypes.byref(st), 3, FAKE, 8, None) == -1
+    assert L.mg_pct_count(ctypes.byref(st), 0, FAKE, -1, None) == -2
+    assert L.mg_pct_count(ctypes.byref(st), 0, None, 8, None) == -1
+    assert L.mg_pct_count(ctypes.byref(st), 0, FAKE + 4, 8, None) == -4
+    assert L.mg_pct_count(ctypes.byref(st), 0, None, 0, None) == 0            # M == 0: no-op
+    assert L.mg_pct_reset(ctypes.byref(mg.mg_pct(FAKE, FAKE, 60, 0)), None) == -2
+    assert L.mg_pct_reset(ctypes.byref(mg.mg_pct(None, FAKE, 64, 0)), None) == -1
+    assert L.mg_pct_reset(ctypes.byref(mg.mg_pct(FAKE, FAKE, 64, 1)), None) == -1
+    assert L.mg_pct_reset(None, None) == -1
