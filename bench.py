@@ -15,8 +15,9 @@ TFLOP/s; the dual-GEMM kernel's own rate is in `roofline`.
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
     python bench.py --suite      one JSON line per configuration point: the
                                  480p up/down-projections (three weight-scale
-                                 layouts, raw and smoothed outlier score), the
-                                 720p (k, alpha) sweep and the 720p FFN block
+                                 layouts, raw, smoothed and percentile outlier
+                                 scores), the 720p (k, alpha) sweep and the
+                                 720p FFN block
                                  (three layouts), each with kernel rates (warm,
                                  and the GEMM also cold) and the fidelity of the
                                  three modes against the unquantized float64 layer
@@ -204,22 +205,45 @@ def suite(args) -> int:
             mg.mg_calib_act(Xd, act_max)
         t_calib = timed(calib)
         t_wr = timed(lambda: mg.mg_weight_range(Wd, w_max))
+        # score "pNN.N": Eq. (4) ranks the nearest-rank NN.N% quantile of |x| per channel
+        pct_q = float(score[1:]) / 100.0 if score.startswith("p") else None
+        desc_score = "max" if pct_q is not None else score
+        rank_stat, t_pct = None, None
+        if pct_q is not None:
+            rank_stat = torch.empty(K, dtype=torch.float32, device="cuda")
+            st = mg.PctState(K)
+
+            def pct():
+                mg.mg_pct_reset(st)
+                mg.mg_pct_count(st, 0, Xd)
+                mg.mg_pct_select(st, 0, pct_q)
+                mg.mg_pct_count(st, 1, Xd)
+                mg.mg_pct_select(st, 1, pct_q, rank_stat)
+            t_pct = timed(pct)
+
+        def build(p):
+            if rank_stat is None:
+                mg.mg_plan_build(p, act_max, w_max, Wd)
+            else:
+                mg.mg_smooth_scales(p, act_max, w_max)
+                mg.mg_outlier_set(p, rank_stat)
+                mg.mg_fold_pack(p, Wd)
         rows = np.arange(M) if M <= FID_ROWS else np.sort(g.choice(M, FID_ROWS, replace=False))
         Xs = Xd[torch.from_numpy(rows).cuda()].contiguous()
         Yref = to_f64(X_h[rows]) @ to_f64(W_h).T
         Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
 
         def fidelity(k, alpha, smooth):
-            p = mg.Plan.empty(mg.make_desc(K, N, k, alpha, layout, smooth, score))
-            mg.mg_plan_build(p, act_max, w_max, Wd)
+            p = mg.Plan.empty(mg.make_desc(K, N, k, alpha, layout, smooth, desc_score))
+            build(p)
             return rel_fro(y_host(mg.forward(p, Xs)), Yref)
 
         uniform = fidelity(0, 0.5, False)
         smooth_only = {}
         for k, alpha in points:
-            desc = mg.make_desc(K, N, k, alpha, layout, True, score)
+            desc = mg.make_desc(K, N, k, alpha, layout, True, desc_score)
             p = mg.Plan.empty(desc)
-            t_plan = timed(lambda: mg.mg_plan_build(p, act_max, w_max, Wd))
+            t_plan = timed(lambda: build(p))
             a = mg.Act.empty(desc, M)
             t_quant = timed(lambda: mg.mg_quantize_act(p, Xd, a))
             t_gemm = timed(lambda: mg.mg_dual_gemm(p, a, Y))
@@ -245,7 +269,9 @@ def suite(args) -> int:
                    "fidelity_rel_fro": {"uniform": round(uniform, 5),
                                         "smooth_only": round(smooth_only[alpha], 5),
                                         "smooth_split": round(fidelity(k, alpha, True), 5)},
-                   "fidelity_rows": int(rows.size)})
+                   "fidelity_rows": int(rows.size),
+                   **({"pct_ms": round(t_pct, 4), "pct_gbs": round(2 * M * K * xb / t_pct / 1e6, 1)}
+                      if t_pct is not None else {})})
             del a
         del Y
 
@@ -260,9 +286,9 @@ def suite(args) -> int:
 
     layer_config(synth.TINY, [(synth.TINY.k, synth.TINY.alpha)])
     layer_config(synth.FFN0_480P, [(synth.FFN0_480P.k, synth.FFN0_480P.alpha)], ("1x32", "32x32", "128x1"),
-                 ("max", "smoothed"))
+                 ("max", "smoothed", "p99.9"))
     layer_config(synth.FFN2_480P, [(synth.FFN2_480P.k, synth.FFN2_480P.alpha)], ("1x32", "32x32", "128x1"),
-                 ("max", "smoothed"))
+                 ("max", "smoothed", "p99.9"))
     layer_config(synth.FFN0_720P, [(k, a) for a in synth.SWEEP_ALPHA for k in synth.SWEEP_K])
 
     # ---- the 720p FFN block

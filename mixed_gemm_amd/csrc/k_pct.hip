@@ -13,10 +13,10 @@
 //   pass 1: per channel, a histogram of the low 7 bits of the values whose
 //           high byte is h;
 //   select 1: the low bits l holding rank r'; the value is (h << 7) | l.
-// Counting: a workgroup takes 64 channels (128 B of each row: a lane loads
-// two channels, 32 lanes a row piece, 8 rows per step) over a chunk of rows
-// and counts into 64 x 256 LDS bins with LDS atomics, then adds its non-zero
-// bins into the global [K][256] histogram.
+// Counting: a workgroup takes 32 channels (64 B of each row: a lane loads 8
+// channels, 4 lanes a row piece, 64 rows per step, 4 rows in flight per
+// lane) over a chunk of rows and counts into 32 x 256 LDS bins with LDS
+// atomics, then adds its non-zero bins into the global [K][256] histogram.
 #include "mg_device.h"
 #include "mg_internal.h"
 
@@ -24,47 +24,72 @@ namespace mg {
 
 namespace {
 
-constexpr int kPctCh = 64;        // channels per workgroup
+constexpr int kPctCh = 32;        // channels per workgroup
 constexpr int kPctBins = 256;
+constexpr int kPctStride = 257;   // LDS words per channel: equal bins of different channels in different banks
+constexpr int kPctUnroll = 4;     // rows in flight per thread
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Halfword e (0..7) of a 16-byte word.
+__device__ __forceinline__ uint32_t half_of(const u32x4& w, int e) {
+    const uint32_t d = (e & 4) ? ((e & 2) ? w[3] : w[2]) : ((e & 2) ? w[1] : w[0]);
+    return (e & 1) ? (d >> 16) : (d & 0xFFFFu);
+}
 
 __global__ void __launch_bounds__(256) pct_count_kernel(const uint16_t* __restrict__ X, int64_t M, int32_t K,
                                                         int64_t rows_per_chunk, int pass,
                                                         const int32_t* __restrict__ sel,
                                                         uint32_t* __restrict__ hist) {
-    __shared__ uint32_t bins[kPctCh * kPctBins];
+    __shared__ uint32_t bins[kPctCh * kPctStride];
     const int t = threadIdx.x;
-    for (int i = t; i < kPctCh * kPctBins; i += 256) bins[i] = 0;
-    const int cp = t & 31, ri = t >> 5;
-    const int c0 = blockIdx.x * kPctCh + 2 * cp;      // this lane's first channel (K even)
+    for (int i = t; i < kPctCh * kPctStride; i += 256) bins[i] = 0;
+    // a thread owns 8 consecutive channels (16 bytes of a row) and rows
+    // rho, rho + 64, ...; it visits its channels starting at rho % 8, so the
+    // lanes of a wave that share channels mostly update different channels
+    const int g = t & 3, rho = t >> 2;
+    const int c0 = blockIdx.x * kPctCh + 8 * g;        // K % 32 == 0: all 8 in range or none
     const bool valid = c0 < K;
-    int h0 = -1, h1 = -1;                              // pass 1: the selected high bytes
-    if (pass == 1 && valid) {
-        h0 = sel[2 * c0];
-        h1 = sel[2 * (c0 + 1)];
-    }
+    int hsel[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) hsel[e] = (pass == 1 && valid) ? sel[2 * (c0 + e)] : -1;
     __syncthreads();
     const int64_t r_begin = (int64_t)blockIdx.y * rows_per_chunk;
     const int64_t r_end = r_begin + rows_per_chunk < M ? r_begin + rows_per_chunk : M;
-    uint32_t* b0 = bins + (2 * cp) * kPctBins;
-    uint32_t* b1 = b0 + kPctBins;
+    uint32_t* bg = bins + 8 * g * kPctStride;
     if (valid) {
-        for (int64_t r = r_begin + ri; r < r_end; r += 8) {
-            const uint32_t w = *reinterpret_cast<const uint32_t*>(X + r * K + c0);
-            const uint32_t a0 = w & 0x7FFFu, a1 = (w >> 16) & 0x7FFFu;
-            if (pass == 0) {
-                atomicAdd(b0 + (a0 >> 7), 1u);
-                atomicAdd(b1 + (a1 >> 7), 1u);
-            } else {
-                if ((int)(a0 >> 7) == h0) atomicAdd(b0 + (a0 & 0x7Fu), 1u);
-                if ((int)(a1 >> 7) == h1) atomicAdd(b1 + (a1 & 0x7Fu), 1u);
+        for (int64_t r0 = r_begin + rho; r0 < r_end; r0 += 64 * kPctUnroll) {
+            u32x4 w[kPctUnroll];
+#pragma unroll
+            for (int u = 0; u < kPctUnroll; ++u) {
+                const int64_t r = r0 + 64 * u;
+                w[u] = r < r_end ? *reinterpret_cast<const u32x4*>(X + r * K + c0) : u32x4{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int u = 0; u < kPctUnroll; ++u) {
+                if (r0 + 64 * u >= r_end) break;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int e = (i + rho) & 7;
+                    const uint32_t a = half_of(w[u], e) & 0x7FFFu;
+                    const uint32_t hi = a >> 7;
+                    int h_e = hsel[0];
+#pragma unroll
+                    for (int f = 1; f < 8; ++f) h_e = e == f ? hsel[f] : h_e;
+                    if (pass == 0)
+                        atomicAdd(bg + e * kPctStride + hi, 1u);
+                    else if ((int)hi == h_e)
+                        atomicAdd(bg + e * kPctStride + (a & 0x7Fu), 1u);
+                }
             }
         }
     }
     __syncthreads();
     for (int i = t; i < kPctCh * kPctBins; i += 256) {
-        const int c = blockIdx.x * kPctCh + i / kPctBins;
-        const uint32_t v = bins[i];
-        if (v && c < K) atomicAdd(hist + (int64_t)c * kPctBins + (i % kPctBins), v);
+        const int ch = i / kPctBins, b = i % kPctBins;
+        const int c = blockIdx.x * kPctCh + ch;
+        const uint32_t v = bins[ch * kPctStride + b];
+        if (v && c < K) atomicAdd(hist + (int64_t)c * kPctBins + b, v);
     }
 }
 
@@ -129,9 +154,9 @@ hipError_t launch_pct_count(const uint16_t* X, int64_t M, int32_t K, int pass, c
                             hipStream_t st) {
     if (M <= 0) return hipSuccess;
     const int gx = (K + kPctCh - 1) / kPctCh;
-    // about 4 workgroups per CU (64 KB of LDS each), row chunks of at least 64 rows
-    int64_t gy = ((int64_t)device_cu_count() * 4 + gx - 1) / gx;
-    int64_t max_gy = (M + 63) / 64;
+    // about 8 workgroups per CU (33 KB of LDS each), row chunks of at least 256 rows
+    int64_t gy = ((int64_t)device_cu_count() * 8 + gx - 1) / gx;
+    int64_t max_gy = (M + 255) / 256;
     if (gy > max_gy) gy = max_gy;
     if (gy < 1) gy = 1;
     if (gy > 65535) gy = 65535;
