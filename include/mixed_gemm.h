@@ -220,6 +220,18 @@ int mg_quantize_act(const mg_plan* p, const void* X, int32_t dtype, int64_t M,
 int mg_dual_gemm(const mg_plan* p, const mg_act* a, int64_t M, void* Y, int32_t y_dtype,
                  hipStream_t stream);
 
+/* mg_quantize_act and mg_calib_act on the same X in one pass: the quantized
+ * operands as mg_quantize_act writes them, and act_max[j] = max(act_max[j],
+ * max_t |X[t][j]|) over every channel (outlier channels included) as
+ * mg_calib_act computes it.  For routing that detects the outlier channels of
+ * one step while it runs on the set chosen from the previous step (outlier
+ * channels persist across steps; MixQ's quantization ahead of detection,
+ * whose port to diffusion steps the pages name as future work).  Same
+ * arguments and errors as mg_quantize_act, plus act_max [K] f32 (running;
+ * reset it with mg_calib_reset). */
+int mg_quantize_act_stats(const mg_plan* p, const void* X, int32_t dtype, int64_t M, const mg_act* a,
+                          float* act_max, hipStream_t stream);
+
 /* mg_quantize_act followed by mg_dual_gemm. */
 int mg_forward(const mg_plan* p, const void* X, int32_t dtype, int64_t M, const mg_act* a,
                void* Y, int32_t y_dtype, hipStream_t stream);

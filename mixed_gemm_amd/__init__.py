@@ -61,7 +61,7 @@ class mg_pct(ctypes.Structure):
 EXPORTS = ("mg_version", "mg_last_error", "mg_plan_bytes", "mg_act_bytes", "mg_calib_reset",
            "mg_calib_act", "mg_weight_range", "mg_smooth_scales", "mg_outlier_set", "mg_fold_pack",
            "mg_plan_build", "mg_quantize_act", "mg_dual_gemm", "mg_forward", "mg_gelu_tanh_bf16",
-           "mg_gelu_quantize_act", "mg_pct_reset", "mg_pct_count", "mg_pct_select")
+           "mg_gelu_quantize_act", "mg_pct_reset", "mg_pct_count", "mg_pct_select", "mg_quantize_act_stats")
 
 _lib = None
 
@@ -92,6 +92,7 @@ def lib() -> ctypes.CDLL:
             "mg_forward": ([P(mg_plan), vp, i32, i64, P(mg_act), vp, i32, vp], ctypes.c_int),
             "mg_gelu_tanh_bf16": ([vp, vp, i64, vp], ctypes.c_int),
             "mg_gelu_quantize_act": ([P(mg_plan), vp, i64, P(mg_act), vp], ctypes.c_int),
+            "mg_quantize_act_stats": ([P(mg_plan), vp, i32, i64, P(mg_act), vp, vp], ctypes.c_int),
             "mg_pct_reset": ([P(mg_pct), vp], ctypes.c_int),
             "mg_pct_count": ([P(mg_pct), i32, vp, i64, vp], ctypes.c_int),
             "mg_pct_select": ([P(mg_pct), i32, ctypes.c_double, vp, vp], ctypes.c_int),
@@ -272,6 +273,12 @@ def mg_gelu_tanh_bf16(inp: torch.Tensor, out: torch.Tensor, stream=None) -> None
     _check(lib().mg_gelu_tanh_bf16(_ptr(inp), _ptr(out), inp.numel(), _stream(stream)))
 
 
+def mg_quantize_act_stats(plan: Plan, X: torch.Tensor, act: Act, act_max: torch.Tensor, stream=None) -> None:
+    p, a = plan.c(), act.c()
+    _check(lib().mg_quantize_act_stats(ctypes.byref(p), _ptr(X), _dtype(X), X.shape[0], ctypes.byref(a),
+                                       _ptr(act_max), _stream(stream)))
+
+
 def mg_gelu_quantize_act(plan: Plan, Y: torch.Tensor, act: Act, stream=None) -> None:
     if Y.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
         raise ValueError("bf16 input expected")
@@ -374,6 +381,60 @@ def reference_plan(W: torch.Tensor, stream=None) -> Plan:
     N, K = W.shape
     act_max = torch.ones(K, dtype=torch.float32, device=W.device)
     return plan(act_max, W, 0.5, K, "1x32", smooth=False, stream=stream)
+
+
+class DynamicRouter:
+    """Per-step outlier routing by prediction (MixQ's quantization ahead of
+    detection; the pages name its port to diffusion steps as future work).
+
+    The smoothing scales s are fixed from the offline calibration maxima, and
+    the first step routes the calibrated top-k set.  Each step quantizes its
+    batch with the current plan while recording the batch's per-channel
+    maxima (mg_quantize_act_stats, one pass), runs the dual GEMM, and -- on a
+    side stream, overlapping the GEMM -- builds the next step's plan from
+    those maxima (Eq. (4) top-k, then fold and pack) into the other of two
+    plan buffers.  Step t's outlier set is therefore Eq. (4) applied to the
+    maxima of step t-1's batch."""
+
+    def __init__(self, W: torch.Tensor, act_max_calib: torch.Tensor, alpha: float, k: int,
+                 layout: str = "1x32", smooth: bool = True, score: str = "max"):
+        N, K = W.shape
+        self.W = W
+        self.desc = make_desc(K, N, k, alpha, layout, smooth, score)
+        self.plans = [Plan.empty(self.desc, W.device), Plan.empty(self.desc, W.device)]
+        w_max = torch.empty(K, dtype=torch.float32, device=W.device)
+        mg_weight_range(W, w_max)
+        for p in self.plans:
+            mg_smooth_scales(p, act_max_calib, w_max)
+        mg_outlier_set(self.plans[0], act_max_calib)
+        mg_fold_pack(self.plans[0], W)
+        self.cur = 0
+        self.stats = torch.empty(K, dtype=torch.float32, device=W.device)
+        self.side = torch.cuda.Stream(device=W.device)
+        self.ready = None                      # event: the current plan is built
+
+    def step(self, X: torch.Tensor, act: Act | None = None, Y: torch.Tensor | None = None) -> torch.Tensor:
+        main = torch.cuda.current_stream()
+        M = X.shape[0]
+        act = act if act is not None else Act.empty(self.desc, M, X.device)
+        if Y is None:
+            Y = torch.empty((M, self.desc.N), dtype=torch.bfloat16, device=X.device)
+        if self.ready is not None:
+            main.wait_event(self.ready)       # this step's plan, and the last read of stats
+        p = self.plans[self.cur]
+        mg_calib_reset(self.stats, main)
+        mg_quantize_act_stats(p, X, act, self.stats, main)
+        detected = torch.cuda.Event()
+        detected.record(main)                  # also orders after the previous GEMM (which read the other plan)
+        mg_dual_gemm(p, act, Y, main)
+        nxt = self.plans[self.cur ^ 1]
+        self.side.wait_event(detected)
+        mg_outlier_set(nxt, self.stats, self.side)
+        mg_fold_pack(nxt, self.W, self.side)
+        self.ready = torch.cuda.Event()
+        self.ready.record(self.side)
+        self.cur ^= 1
+        return Y
 
 
 @dataclass

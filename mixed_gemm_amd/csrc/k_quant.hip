@@ -95,13 +95,13 @@ __device__ __forceinline__ void encode_store(const float (&q)[8], int lane, bool
     }
 }
 
-template <bool GELU>
+template <bool GELU, bool STATS>
 __global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restrict__ X, int64_t M, int32_t K,
                                                          int32_t k, const float* __restrict__ s,
                                                          const float* __restrict__ rcp,
                                                          const int32_t* __restrict__ pos,
                                                          uint8_t* __restrict__ Aq, uint8_t* __restrict__ As,
-                                                         uint16_t* __restrict__ XO) {
+                                                         uint16_t* __restrict__ XO, uint32_t* __restrict__ amax) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int j0 = (blockIdx.x * 64 + lane) * 8;
@@ -114,13 +114,16 @@ __global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restr
     // occupancy).
     __shared__ float t_s[512], t_r[512];
     __shared__ int t_p[512];
+    __shared__ uint32_t t_m[512];    // STATS: the workgroup's per-channel max |x| (bf16 bits)
     for (int t = threadIdx.x; t < 512; t += 256) {
         const int j = blockIdx.x * 512 + t;
         t_s[t] = j < K ? s[j] : 1.0f;
         t_r[t] = j < K ? rcp[j] : 1.0f;
         t_p[t] = j < K ? pos[j] : -1;
+        t_m[t] = 0;
     }
     __syncthreads();
+    u16x2 mx[4] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};   // STATS: running max of the lane's |x| bit patterns
     // the lane's 8 channels: three pairs of 16-byte loads (j0 is a multiple of 8)
     float sv[8] = {1, 1, 1, 1, 1, 1, 1, 1}, rv[8] = {1, 1, 1, 1, 1, 1, 1, 1};
     int pv[8] = {-1, -1, -1, -1, -1, -1, -1, -1};
@@ -188,6 +191,11 @@ __global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restr
 #pragma unroll
             for (int i = 0; i < 4; ++i) w[i] = gelu_bf16x2(w[i]);
         }
+        if constexpr (STATS) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                mx[i] = __builtin_elementwise_max(mx[i], __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
+        }
         const bool fast = s_ok & bf16x8_in_fast_range(w);
         float x[8], q[8];
 #pragma unroll
@@ -253,6 +261,20 @@ __global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restr
         pq += dQ; ps += dS; po += dO;
         a = b;
     }
+    if constexpr (STATS) {
+        // the magnitudes' bit patterns order like the magnitudes: integer max, in LDS across the
+        // workgroup's waves, then one global max per channel and workgroup (f32 bits = bf16 << 16)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            atomicMax(&t_m[lane * 8 + 2 * i], (uint32_t)mx[i][0]);
+            atomicMax(&t_m[lane * 8 + 2 * i + 1], (uint32_t)mx[i][1]);
+        }
+        __syncthreads();
+        for (int t = threadIdx.x; t < 512; t += 256) {
+            const int j = blockIdx.x * 512 + t;
+            if (j < K && t_m[t]) atomicMax(amax + j, t_m[t] << 16);
+        }
+    }
 }
 
 // f32 input (the small f32 layer): correctly rounded division throughout.
@@ -260,9 +282,10 @@ __global__ void __launch_bounds__(256) quant_f32_kernel(const float* __restrict_
                                                         int32_t k, const float* __restrict__ s,
                                                         const int32_t* __restrict__ pos,
                                                         uint8_t* __restrict__ Aq, uint8_t* __restrict__ As,
-                                                        uint16_t* __restrict__ XO) {
+                                                        uint16_t* __restrict__ XO, uint32_t* __restrict__ amax) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
+    float mx[8] = {0, 0, 0, 0, 0, 0, 0, 0};       // amax != nullptr: running max |x| per channel
     const int j0 = (blockIdx.x * 64 + lane) * 8;
     const bool valid = j0 < K;
     float sv[8];
@@ -278,6 +301,7 @@ __global__ void __launch_bounds__(256) quant_f32_kernel(const float* __restrict_
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const float x = valid ? X[r * K + j0 + i] : 0.0f;
+            mx[i] = fmaxf(mx[i], __builtin_fabsf(x));
             q[i] = __fdiv_rn(x, sv[i]);
             if (pv[i] >= 0) {
                 XO[r * k + pv[i]] = (uint16_t)f32_to_bf16_rne(q[i]);
@@ -286,31 +310,47 @@ __global__ void __launch_bounds__(256) quant_f32_kernel(const float* __restrict_
         }
         encode_store(q, lane, valid, Aq + r * (K / 2), As + r * (K / 32), j0);
     }
+    if (amax != nullptr && valid) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) atomicMax(amax + j0 + i, __float_as_uint(mx[i]));
+    }
 }
 
 }  // namespace
 
 hipError_t launch_quant(const void* X, int32_t dtype, int64_t M, int32_t K, int32_t k,
                         const float* s, const float* rcp, const int32_t* pos, uint8_t* Aq,
-                        uint8_t* As, uint16_t* XO, hipStream_t st, bool gelu) {
+                        uint8_t* As, uint16_t* XO, hipStream_t st, bool gelu, float* amax) {
     if (M <= 0) return hipSuccess;
     const int64_t gx = ((int64_t)K / 8 + 63) / 64;
     // about WAVES_PER_CU waves per CU, each wave at least one row
     int64_t gy = (M + kWaves - 1) / kWaves;
-    int64_t cap = (int64_t)device_cu_count() * (WAVES_PER_CU / kWaves) / gx;
+    // the statistics variant holds 7 waves per SIMD (more registers), the others 8
+    const int waves_per_cu = amax ? 28 : WAVES_PER_CU;
+    int64_t cap = (int64_t)device_cu_count() * (waves_per_cu / kWaves) / gx;
     if (cap < 1) cap = 1;
     if (gy > cap) gy = cap;
     if (gy > 65535) gy = 65535;
     dim3 grid((unsigned)gx, (unsigned)gy);
-    if (dtype == MG_BF16 && gelu)
-        hipLaunchKernelGGL(quant_bf16_kernel<true>, grid, dim3(256), 0, st, static_cast<const uint16_t*>(X), M, K, k,
-                           s, rcp, pos, Aq, As, XO);
-    else if (dtype == MG_BF16)
-        hipLaunchKernelGGL(quant_bf16_kernel<false>, grid, dim3(256), 0, st, static_cast<const uint16_t*>(X), M, K,
-                           k, s, rcp, pos, Aq, As, XO);
-    else
+    uint32_t* am = reinterpret_cast<uint32_t*>(amax);   // non-negative f32 maxima: integer max of the bits
+    const uint16_t* Xb = static_cast<const uint16_t*>(X);
+    if (dtype == MG_BF16) {
+        if (gelu && am)
+            hipLaunchKernelGGL((quant_bf16_kernel<true, true>), grid, dim3(256), 0, st, Xb, M, K, k, s, rcp, pos, Aq, As,
+                               XO, am);
+        else if (gelu)
+            hipLaunchKernelGGL((quant_bf16_kernel<true, false>), grid, dim3(256), 0, st, Xb, M, K, k, s, rcp, pos, Aq,
+                               As, XO, am);
+        else if (am)
+            hipLaunchKernelGGL((quant_bf16_kernel<false, true>), grid, dim3(256), 0, st, Xb, M, K, k, s, rcp, pos, Aq,
+                               As, XO, am);
+        else
+            hipLaunchKernelGGL((quant_bf16_kernel<false, false>), grid, dim3(256), 0, st, Xb, M, K, k, s, rcp, pos, Aq,
+                               As, XO, am);
+    } else {
         hipLaunchKernelGGL(quant_f32_kernel, grid, dim3(256), 0, st, static_cast<const float*>(X), M, K, k, s, pos,
-                           Aq, As, XO);
+                           Aq, As, XO, am);
+    }
     return hipGetLastError();
 }
 

@@ -264,6 +264,20 @@ int mg_quantize_act(const mg_plan* p, const void* X, int32_t dtype, int64_t M, c
     return h == hipSuccess ? MG_OK : hip_fail(h, "mg_quantize_act");
 }
 
+int mg_quantize_act_stats(const mg_plan* p, const void* X, int32_t dtype, int64_t M, const mg_act* a,
+                          float* act_max, hipStream_t stream) {
+    if (int e = check_plan(p, false)) return e;
+    if (int e = check_dtype(dtype)) return e;
+    if (M < 0) return fail(MG_ERR_SHAPE, "M=%lld must be >= 0", (long long)M);
+    MG_CHECK_PTR(act_max, "act_max");
+    if (M == 0) return MG_OK;
+    MG_CHECK_PTR(X, "X");
+    if (int e = check_act(p, a)) return e;
+    hipError_t h = mg::launch_quant(X, dtype, M, p->d.K, p->d.k, p->s, p->rcp, p->pos, a->Aq, a->As, a->XO,
+                                    stream, false, act_max);
+    return h == hipSuccess ? MG_OK : hip_fail(h, "mg_quantize_act_stats");
+}
+
 int mg_gelu_quantize_act(const mg_plan* p, const uint16_t* Y, int64_t M, const mg_act* a, hipStream_t stream) {
     if (int e = check_plan(p, false)) return e;
     if (M < 0) return fail(MG_ERR_SHAPE, "M=%lld must be >= 0", (long long)M);

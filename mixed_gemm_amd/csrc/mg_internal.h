@@ -23,7 +23,8 @@ hipError_t launch_fold_pack(const void* W, int32_t dtype, int32_t N, int32_t K, 
                             uint8_t* Ws, uint8_t* Wst, uint16_t* WO, hipStream_t st);
 hipError_t launch_quant(const void* X, int32_t dtype, int64_t M, int32_t K, int32_t k,
                         const float* s, const float* rcp, const int32_t* pos, uint8_t* Aq,
-                        uint8_t* As, uint16_t* XO, hipStream_t st, bool gelu = false);
+                        uint8_t* As, uint16_t* XO, hipStream_t st, bool gelu = false,
+                        float* amax = nullptr);
 hipError_t launch_dual_gemm(const uint8_t* Aq, const uint8_t* As, const uint16_t* XO,
                             const uint8_t* Wq, const uint8_t* Ws, const uint16_t* WO, int64_t M,
                             int32_t N, int32_t K, int32_t k, void* Y, int32_t y_dtype,

@@ -78,6 +78,40 @@ def heavy_tail_act(M: int, K: int, *, sigma: float, frac: float, mult: float,
     return out
 
 
+def drifting_channels(K: int, steps: int, *, frac: float, drift: float, seed: int) -> list[np.ndarray]:
+    """Heavy-channel sets for a sequence of batches: round(frac*K) channels at
+    the first step; from one step to the next, round(drift * n) of them are
+    replaced by channels outside the set (the rest persist)."""
+    g = rng(seed)
+    n = int(round(frac * K))
+    cur = g.choice(K, size=n, replace=False)
+    sets = [np.sort(cur).astype(np.int64)]
+    for _ in range(1, steps):
+        m = int(round(drift * n))
+        keep = g.choice(n, size=n - m, replace=False)
+        outside = np.setdiff1d(np.arange(K), cur)
+        cur = np.concatenate([cur[keep], g.choice(outside, size=m, replace=False)])
+        sets.append(np.sort(cur).astype(np.int64))
+    return sets
+
+
+def drifting_act(M: int, K: int, steps: int, *, sigma: float, frac: float, mult: float, drift: float,
+                 ch_seed: int, x_seed: int) -> list[np.ndarray]:
+    """bf16 batches like heavy_tail_act whose heavy channels follow
+    drifting_channels (a denoising-step sequence with persistent, slowly
+    moving outlier channels)."""
+    out = []
+    for t, ch in enumerate(drifting_channels(K, steps, frac=frac, drift=drift, seed=ch_seed)):
+        g = rng(x_seed + t)
+        X = np.empty((M, K), dtype=np.uint16)
+        for r0, z in _normal_rows(g, M, K):
+            z *= np.float32(sigma)
+            z[:, ch] *= np.float32(mult)
+            X[r0:r0 + z.shape[0]] = f32_to_bf16_bits(z)
+        out.append(X)
+    return out
+
+
 def gelu_act(M: int, K: int, *, frac: float, mult: float, ch_seed: int, x_seed: int) -> np.ndarray:
     """bf16 GELU-tanh of an N(0,1) pre-activation with round(frac*K) channels x mult."""
     ch = pick_channels(K, frac, ch_seed)
