@@ -3,7 +3,9 @@
     python -m mixed_gemm_amd.build
 
 Compiles every ``csrc/*.hip`` with hipcc for gfx950 (one object per file, in
-parallel) and links them into ``mixed_gemm_amd/libmixed_gemm.so``.
+parallel) and links them into ``mixed_gemm_amd/libmixed_gemm.so``; then builds
+``tests/c/abi_demo`` (plain C against ``include/mixed_gemm.h``, the library and
+the HIP runtime), which a GPU test runs to exercise the C ABI without Python.
 """
 from __future__ import annotations
 
@@ -59,7 +61,32 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    demo = build_c_demo()
+    if verbose:
+        print(f"built {demo}")
     return LIB
+
+
+def build_c_demo() -> str:
+    """tests/c/abi_demo (executable) and tests/c/libabi_demo.so (the same
+    program's abi_demo_run() for in-process use): C99, host code only (no
+    kernels), linked against the in-tree library (found next to it at run time
+    through an $ORIGIN rpath)."""
+    src = os.path.join(ROOT, "tests", "c", "abi_demo.c")
+    exe = os.path.join(ROOT, "tests", "c", "abi_demo")
+    so = os.path.join(ROOT, "tests", "c", "libabi_demo.so")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cc = os.environ.get("CC", "gcc")
+    common = ["-std=c99", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+              "-I", os.path.join(rocm, "include"), src,
+              "-L", HERE, "-lmixed_gemm", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+              "-Wl,-rpath,$ORIGIN/../../mixed_gemm_amd", "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    for target, extra in ((exe, []), (so, ["-DABI_DEMO_LIB", "-shared", "-fPIC"])):
+        r = subprocess.run([cc, *extra, *common, "-o", target + ".tmp"], capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"C demo build failed:\n{r.stdout}\n{r.stderr}")
+        os.replace(target + ".tmp", target)
+    return exe
 
 
 if __name__ == "__main__":
