@@ -19,7 +19,7 @@
 // row in scalar registers, so channels past K need no per-lane bounds code.
 //
 // With GELU, X is the previous projection's bf16 output and the quantized
-// input is h = gelu_bf16(X) (the FFN block's hidden activation), computed
+// input is h = gelu_bf16x2 of X (the FFN block's hidden activation), computed
 // in registers with the GELU kernel's own code: one pass instead of a GELU
 // pass that writes h and a quantize pass that reads it back.
 //
