@@ -62,23 +62,24 @@ def measured_traffic() -> float | None:
 
 
 def cpu_baseline(w, X, W, rows: int) -> dict:
-    """The oracle as it stands, on a bounded sample: the plan on the full W and
-    the per-row work (calibration, quantize, float64 dual GEMM) on `rows` rows;
-    the per-row cost is scaled to the workload's M."""
+    """The oracle as it stands, on a bounded sample: the weight ranges and plan
+    on the full W, and the per-row work (calibration, quantize, float64 dual
+    GEMM) on `rows` rows, whose cost is scaled to the workload's M."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
     from oracle import layer
     t0 = time.perf_counter()
-    a = layer.act_max(X[:rows])
-    wr = layer.weight_range(W)
-    p = layer.plan(a, wr, W, w.alpha, w.k)
+    a = layer.act_max(X[:rows])                                   # per-row work
     t1 = time.perf_counter()
-    qa = layer.quantize_act(X[:rows], p["s"], p["O"])
-    Y = layer.dual_gemm_f64(qa["Aq"], qa["As"], p["Wq"], p["Ws"], qa["XO"], p["WO"])
+    wr = layer.weight_range(W)                                    # per-weight work
+    p = layer.plan(a, wr, W, w.alpha, w.k)
     t2 = time.perf_counter()
+    qa = layer.quantize_act(X[:rows], p["s"], p["O"])             # per-row work
+    Y = layer.dual_gemm_f64(qa["Aq"], qa["As"], p["Wq"], p["Ws"], qa["XO"], p["WO"])
+    t3 = time.perf_counter()
     assert Y.shape == (rows, w.N)
-    t_plan, t_rows = t1 - t0, t2 - t1
+    t_plan, t_rows = t2 - t1, (t1 - t0) + (t3 - t2)
     t_full = t_plan + t_rows * w.M / rows
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": round(w.flops() / t_full / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
@@ -415,7 +416,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ffn0_480p_32760x5120x13824")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--cpu-rows", type=int, default=3072,
+                    help="rows of the workload the oracle runs for cpu_baseline (about 10 s of CPU work at 480p)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run a plain device copy of 256 MiB (HBM counter calibration)")
     ap.add_argument("--suite", action="store_true",
