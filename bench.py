@@ -416,7 +416,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ffn0_480p_32760x5120x13824")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=3072,
+    ap.add_argument("--cpu-rows", type=int, default=12288,
                     help="rows of the workload the oracle runs for cpu_baseline (about 10 s of CPU work at 480p)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run a plain device copy of 256 MiB (HBM counter calibration)")
