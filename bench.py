@@ -84,8 +84,10 @@ def cpu_baseline(w, X, W, rows: int) -> dict:
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": round(w.flops() / t_full / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"oracle step on {rows} of {w.M} rows (plan on the full W: {t_plan:.1f} s; "
-                      f"per-row work {t_rows:.1f} s scaled x{w.M / rows:.0f}); est. full step {t_full:.0f} s"}
+            "sample": (f"the whole oracle step, all {w.M} rows: weight ranges and plan {t_plan:.1f} s, "
+                       f"per-row work {t_rows:.1f} s" if rows == w.M else
+                       f"oracle step on {rows} of {w.M} rows (weight ranges and plan {t_plan:.1f} s; "
+                       f"per-row work {t_rows:.1f} s scaled x{w.M / rows:.1f}); est. full step {t_full:.0f} s")}
 
 
 COPY_BYTES = 256 << 20            # plain copy used to calibrate the HBM byte counters
@@ -416,8 +418,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ffn0_480p_32760x5120x13824")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=12288,
-                    help="rows of the workload the oracle runs for cpu_baseline (about 10 s of CPU work at 480p)")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="rows of the workload the oracle runs for cpu_baseline (0: all of them; at 480p about "
+                         "10-20 s of CPU work)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run a plain device copy of 256 MiB (HBM counter calibration)")
     ap.add_argument("--suite", action="store_true",
@@ -536,7 +539,7 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, X_h, W_h, args.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline(w, X_h, W_h, args.cpu_rows if 0 < args.cpu_rows < M else M)
     print(json.dumps(out), flush=True)
     return 0
 
