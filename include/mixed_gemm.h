@@ -85,13 +85,25 @@ typedef struct {
  *  pos [K]        i32  index of channel j in O, or -1;
  *  Wq  [N][K/2]   u8   MXFP4 payload of the folded bulk weights RN(s_j W[n][j]),
  *                      outlier columns set to +0 before encoding;
- *  Ws  [N][K/32]  u8   E8M0 scale of each (row, 32-block) -- for MG_W_32X32 the
- *                      tile's code repeated on each of its 32 rows, for
- *                      MG_W_128X1 the stripe's code on each of its 32-blocks;
+ *  Ws             u8   E8M0 scale of each (row, 32-block), in scale windows
+ *                      (below) -- for MG_W_32X32 the tile's code repeated on
+ *                      each of its 32 rows, for MG_W_128X1 the stripe's code
+ *                      on each of its 32-blocks;
  *  Wst                 compact codes: [N/32][K/32] u8 tile codes (MG_W_32X32),
  *                      [N][ceil(K/128)] u8 stripe codes (MG_W_128X1); null
  *                      allowed for MG_W_1X32;
- *  WO  [N][k]     bf16 folded outlier columns (null allowed when k == 0). */
+ *  WO  [N][k]     bf16 folded outlier columns (null allowed when k == 0).
+ *
+ * Scale windows (Ws, As).  The E8M0 codes of a [rows][K/32] scale matrix are
+ * stored in windows of 256 rows x 16 blocks (512 channels), 16 bytes per row,
+ * 4096 contiguous bytes per window, windows of a 256-row group consecutive:
+ * the code of (row r, block b) is at byte
+ *     ((r / 256) * nwin + b / 16) * 4096 + (r % 256) * 16 + b % 16,
+ * nwin = ceil(K / 512), for ceil(rows / 256) * nwin * 4096 bytes in all.  The
+ * layout depends on K only (a buffer sized for more rows serves fewer).  The
+ * writers fill the whole last 256-row group: blocks past K/32 and rows past
+ * the matrix hold code 0, the code of an all-zero block.  The dual GEMM copies
+ * one window of its 256x256 output tile's rows as 4 KB of contiguous memory. */
 typedef struct {
     mg_plan_desc d;
     float* s;
@@ -105,8 +117,9 @@ typedef struct {
 } mg_plan;
 
 /* Per-forward activation workspace (sizes from mg_act_bytes):
- *  Aq [M][K/2] u8 MXFP4 payload of the bulk quotients, As [M][K/32] u8 E8M0,
- *  XO [M][k] bf16 outlier quotients (null allowed when k == 0). */
+ *  Aq [M][K/2] u8 MXFP4 payload of the bulk quotients, As the E8M0 code of
+ *  each (row, 32-block) in scale windows (see mg_plan), XO [M][k] bf16
+ *  outlier quotients (null allowed when k == 0). */
 typedef struct {
     uint8_t* Aq;
     uint8_t* As;

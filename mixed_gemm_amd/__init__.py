@@ -160,6 +160,13 @@ def mg_act_bytes(desc: mg_plan_desc, M: int) -> list[int]:
     return list(out)
 
 
+def scale_shape(rows: int, K: int) -> tuple:
+    """Shape of a scale array (As, Ws) for `rows` rows in its stored order:
+    [ceil(rows/256)][ceil(K/512)][256 rows][16 blocks] (the C header's scale
+    windows)."""
+    return (-(-rows // 256), -(-K // 512), 256, 16)
+
+
 @dataclass
 class Plan:
     """Device buffers of one layer's plan (allocated with torch from mg_plan_bytes)."""
@@ -179,9 +186,13 @@ class Plan:
         K, N, k = desc.K, desc.N, desc.k
         e = lambda n, dt: torch.empty(n, dtype=dt, device=device)
         wst = {MG_W_32X32: (N // 32, K // 32), MG_W_128X1: (N, (K + 127) // 128)}.get(desc.layout, 0)
-        return Plan(desc, e(K, torch.float32), e(K, torch.float32), e(k, torch.int32), e(K, torch.int32),
-                    e((N, K // 2), torch.uint8), e((N, K // 32), torch.uint8), e(wst, torch.uint8),
-                    e((N, k), torch.bfloat16))
+        p = Plan(desc, e(K, torch.float32), e(K, torch.float32), e(k, torch.int32), e(K, torch.int32),
+                 e((N, K // 2), torch.uint8), e(scale_shape(N, K), torch.uint8), e(wst, torch.uint8),
+                 e((N, k), torch.bfloat16))
+        got = [t.numel() * t.element_size() for t in p.tensors().values()]
+        if got != b:
+            raise RuntimeError(f"plan buffer sizes {got} differ from mg_plan_bytes {b}")
+        return p
 
     def c(self) -> mg_plan:
         return mg_plan(self.desc, _ptr(self.s), _ptr(self.rcp), _ptr(self.O), _ptr(self.pos), _ptr(self.Wq),
@@ -203,9 +214,13 @@ class Act:
     @staticmethod
     def empty(desc: mg_plan_desc, M: int, device="cuda") -> "Act":
         K, k = desc.K, desc.k
-        return Act(M, torch.empty((M, K // 2), dtype=torch.uint8, device=device),
-                   torch.empty((M, K // 32), dtype=torch.uint8, device=device),
-                   torch.empty((M, k), dtype=torch.bfloat16, device=device))
+        a = Act(M, torch.empty((M, K // 2), dtype=torch.uint8, device=device),
+                torch.empty(scale_shape(M, K), dtype=torch.uint8, device=device),
+                torch.empty((M, k), dtype=torch.bfloat16, device=device))
+        got = [t.numel() * t.element_size() for t in (a.Aq, a.As, a.XO)]
+        if got != mg_act_bytes(desc, M):
+            raise RuntimeError(f"activation buffer sizes {got} differ from mg_act_bytes")
+        return a
 
     def c(self) -> mg_act:
         return mg_act(_ptr(self.Aq), _ptr(self.As), _ptr(self.XO))

@@ -79,6 +79,7 @@ __global__ void __launch_bounds__(256) dual_gemm_simple(const uint8_t* __restric
     const int64_t row = min(m0 + (lane & 31), M - 1);
     const int64_t col = n0 + (lane & 31);
     const int nb = K / 32;
+    const int64_t nwin = sc_nwin(K);
     v16f acc = {};
     for (int kk = 0; kk < K; kk += 64) {
         const int kb = kk / 32 + half;          // this lane's 32-block
@@ -87,8 +88,8 @@ __global__ void __launch_bounds__(256) dual_gemm_simple(const uint8_t* __restric
         if (kb < nb) {
             a = *reinterpret_cast<const uint4*>(Aq + row * (K / 2) + kb * 16);
             b = *reinterpret_cast<const uint4*>(Wq + col * (K / 2) + kb * 16);
-            sa = As[row * nb + kb];
-            sb = Ws[col * nb + kb];
+            sa = As[sc_offset(row, kb, nwin)];
+            sb = Ws[sc_offset(col, kb, nwin)];
         }
         acc = mfma_fp4(a, b, sa, sb, acc);
     }
@@ -121,9 +122,11 @@ __global__ void __launch_bounds__(256) dual_gemm_simple(const uint8_t* __restric
 // E8M0 scales.  A bulk stage needs 8 scale bytes per tile row.  They are not
 // fetched per lane (one cache line per row, per wave, per stage): the 16 bytes
 // of two consecutive bulk stages ("a window") of all 512 tile rows are copied
-// into LDS with one 16-byte load per row, next to the operand copies, and
-// each wave reads its rows' 8 bytes from there.  Windows alternate between two
-// LDS slots.
+// into LDS, next to the operand copies, and each wave reads its rows' 8 bytes
+// from there.  The scale arrays are stored window by window (256 rows x 16
+// bytes contiguous, the tile's rows), so a window of the A (B) tile is 4 KB
+// of contiguous memory: one 16-byte load per lane and row, 8 cache lines per
+// load instruction.  Windows alternate between two LDS slots.
 //
 // Pipeline.  The stages of all of a workgroup's tiles form one sequence over
 // two LDS buffers (2 x 64 KB).  While stage g is multiplied out of one buffer,
@@ -159,6 +162,7 @@ constexpr int GEMM_LDS_BYTES = 2 * STAGE_BYTES + 2 * SCW_BYTES;
 constexpr uint32_t OOB = 0xC0000000u;             // offset that reads as zero
 constexpr int NXCD = 8;
 constexpr int GROUP_M = 8;
+static_assert(TBM == kScRows && TBN == kScRows && SCW_ROWB == kScBlocks, "a tile's scale window is one stored window");
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -211,12 +215,8 @@ struct TileOrg {
 // OA: alignment of the outlier rows (2k bytes) -- 16 when k % 8 == 0 (whole
 // 16-byte chunks, one direct-to-LDS copy each), 4 when k is even (four
 // 4-byte copies per chunk), else 2 (values gathered through registers, which
-// waits for the stage's copies in flight).  SA: alignment of
-// the scale rows (K/32 bytes) -- 16 when every scale window of a row is one
-// aligned 16-byte chunk (one direct-to-LDS copy per row), 4 when it is four
-// aligned 4-byte words (four copies), else 1 (bytes gathered through
-// registers, which waits for the stage's copies in flight).
-template <typename OutT, int OA, int SA>
+// waits for the stage's copies in flight).
+template <typename OutT, int OA>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 dual_gemm_tiled(GemmArgs g) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -231,7 +231,6 @@ dual_gemm_tiled(GemmArgs g) {
     const int64_t M = g.M;
     const uint32_t rowA = (uint32_t)(K / 2);       // bytes per Aq / Wq row
     const uint32_t rowX = (uint32_t)(2 * k);       // bytes per XO / WO row
-    const int nb = K / 32;
     const int S4 = (K / 2 + ROWB - 1) / ROWB;      // bulk stages
     const int S16 = (2 * k + ROWB - 1) / ROWB;     // outlier stages
     const int S = S4 + S16;
@@ -248,8 +247,9 @@ dual_gemm_tiled(GemmArgs g) {
 
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.Aq, (uint64_t)M * rowA);
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(g.Wq, (uint64_t)N * rowA);
-    const __amdgpu_buffer_rsrc_t rAs = make_rsrc(g.As, (uint64_t)M * nb);
-    const __amdgpu_buffer_rsrc_t rBs = make_rsrc(g.Ws, (uint64_t)N * nb);
+    const __amdgpu_buffer_rsrc_t rAs = make_rsrc(g.As, (uint64_t)sc_bytes(M, K));
+    const __amdgpu_buffer_rsrc_t rBs = make_rsrc(g.Ws, (uint64_t)sc_bytes(N, K));
+    const uint32_t nwin = (uint32_t)sc_nwin(K);
     const __amdgpu_buffer_rsrc_t rXO = make_rsrc(g.XO, (uint64_t)M * rowX);
     const __amdgpu_buffer_rsrc_t rWO = make_rsrc(g.WO, (uint64_t)N * rowX);
 
@@ -274,7 +274,7 @@ dual_gemm_tiled(GemmArgs g) {
     const uint32_t lds_w = (uint32_t)(wave * 64 * ROWB);
     // scale windows: lane L of wave w copies window row 64 w + L of A and of
     // B; a lane reads its fragment rows' 8 bytes at these offsets (+ 512 i)
-    const uint32_t lwr = (uint32_t)(wave * 64 + lane);
+    const uint32_t lwr = (uint32_t)(wave * 64 + lane) * SCW_ROWB;
     const uint32_t scw_a = (uint32_t)((wm * 128 + l32) * SCW_ROWB);
     const uint32_t scw_b = (uint32_t)(TBM * SCW_ROWB + (wn * 128 + l32) * SCW_ROWB);
     uint32_t fa[4], fb[4];                        // fragment rows within a stage buffer
@@ -301,61 +301,18 @@ dual_gemm_tiled(GemmArgs g) {
     int wuse = 0;      // scale windows taken into use so far
     int wcur = 0;      // slot of the window of the current bulk stage
 
-    // ---- scale window w (bulk stages 2w, 2w+1) of a tile into the next slot
+    // ---- scale window w (bulk stages 2w, 2w+1) of a tile into the next slot:
+    // the stored windows of the tile's 256 A rows and 256 B rows (4 KB each)
     auto load_window = [&](const TileOrg& o, int w) {
         const int slot = wiss & 1;
         ++wiss;
         uint8_t* dst = lds + SCW_OFF + slot * SCW_BYTES + wave * 64 * SCW_ROWB;
-        if constexpr (SA == 16) {
-            uint32_t r = lwr;
-            asm volatile("" : "+v"(r));
-            const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)w * SCW_ROWB);
-            const uint32_t ra = __builtin_amdgcn_readfirstlane((uint32_t)o.m0);
-            const uint32_t rb = __builtin_amdgcn_readfirstlane((uint32_t)o.n0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rAs, (lds_ptr_t)dst, 16, (ra + r) * (uint32_t)nb, so, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rBs, (lds_ptr_t)(dst + TBM * SCW_ROWB), 16,
-                                                     (rb + r) * (uint32_t)nb, so, 0, 0);
-        } else if constexpr (SA == 4) {
-            // rows 4-byte aligned: four 4-byte copies per operand; copy i moves
-            // rows 16 i + L/4 of the wave's 64, lane L landing at byte 256 i + 4 L
-            // (row byte 4 (L % 4)).  Bytes past the row's nb read as zero.
-            const uint32_t col = (uint32_t)w * SCW_ROWB + 4u * (uint32_t)(lane & 3);
-            const bool colok = col < (uint32_t)nb;
-            uint32_t r = (uint32_t)(wave * 64) + (uint32_t)(lane >> 2);
-            asm volatile("" : "+v"(r));
-            const uint32_t ra = __builtin_amdgcn_readfirstlane((uint32_t)o.m0);
-            const uint32_t rb = __builtin_amdgcn_readfirstlane((uint32_t)o.n0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t ri = r + 16u * (uint32_t)i;
-                const uint32_t va = colok ? (ra + ri) * (uint32_t)nb + col : OOB;
-                const uint32_t vb = colok ? (rb + ri) * (uint32_t)nb + col : OOB;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rAs, (lds_ptr_t)(dst + 256 * i), 4, va, 0, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rBs, (lds_ptr_t)(dst + TBM * SCW_ROWB + 256 * i), 4, vb, 0,
-                                                         0, 0);
-            }
-        } else {
-            // rows not 4-byte aligned: gather the bytes, store through registers
-            const int64_t ra = o.m0 + lwr, rb = (int64_t)o.n0 + lwr;
-            uint32_t wa[4], wb[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                uint32_t xa = 0, xb = 0;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int col = w * SCW_ROWB + 4 * e + q;
-                    const uint32_t ba = (col < nb && ra < M)
-                        ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rAs, (uint32_t)(ra * nb + col), 0, 0) : 0u;
-                    const uint32_t bb = (col < nb && rb < N)
-                        ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rBs, (uint32_t)(rb * nb + col), 0, 0) : 0u;
-                    xa |= (ba & 0xFFu) << (8 * q);
-                    xb |= (bb & 0xFFu) << (8 * q);
-                }
-                wa[e] = xa; wb[e] = xb;
-            }
-            *reinterpret_cast<u32x4*>(dst + lane * 16) = u32x4{wa[0], wa[1], wa[2], wa[3]};
-            *reinterpret_cast<u32x4*>(dst + TBM * SCW_ROWB + lane * 16) = u32x4{wb[0], wb[1], wb[2], wb[3]};
-        }
+        uint32_t r = lwr;
+        asm volatile("" : "+v"(r));
+        const uint32_t wa = __builtin_amdgcn_readfirstlane(((uint32_t)(o.m0 / TBM) * nwin + (uint32_t)w) * kScWinBytes);
+        const uint32_t wb = __builtin_amdgcn_readfirstlane(((uint32_t)(o.n0 / TBN) * nwin + (uint32_t)w) * kScWinBytes);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rAs, (lds_ptr_t)dst, 16, wa + r, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rBs, (lds_ptr_t)(dst + TBM * SCW_ROWB), 16, wb + r, 0, 0, 0);
     };
 
     // ---- this lane's scale words of bulk stage st (from its window)
@@ -716,13 +673,13 @@ dual_gemm_tiled(GemmArgs g) {
     }
 }
 
-template <typename OutT, int OA, int SA>
+template <typename OutT, int OA>
 static hipError_t launch_tiled(const GemmArgs& a, hipStream_t st) {
     static thread_local int configured_dev = -1;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return hipErrorNoDevice;
     if (configured_dev != dev) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dual_gemm_tiled<OutT, OA, SA>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dual_gemm_tiled<OutT, OA>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_LDS_BYTES);
         if (e != hipSuccess) return e;
         configured_dev = dev;
@@ -731,29 +688,16 @@ static hipError_t launch_tiled(const GemmArgs& a, hipStream_t st) {
     const int per = (T + NXCD - 1) / NXCD;
     const int cus_per_xcd = device_cu_count() / NXCD;
     const int wg_per_xcd = per < cus_per_xcd ? per : (cus_per_xcd > 0 ? cus_per_xcd : 1);
-    hipLaunchKernelGGL((dual_gemm_tiled<OutT, OA, SA>), dim3((unsigned)(wg_per_xcd * NXCD)), dim3(256),
+    hipLaunchKernelGGL((dual_gemm_tiled<OutT, OA>), dim3((unsigned)(wg_per_xcd * NXCD)), dim3(256),
                        GEMM_LDS_BYTES, st, a);
     return hipGetLastError();
 }
 
 template <typename OutT>
 static hipError_t launch_tiled_t(const GemmArgs& a, hipStream_t st) {
-    const int oa = a.k % 8 == 0 ? 16 : a.k % 2 == 0 ? 4 : 2;
-    const int nb = a.K / 32;
-    const int sa = nb % 16 == 0 ? 16 : nb % 4 == 0 ? 4 : 1;
-    if (oa == 16) {
-        if (sa == 16) return launch_tiled<OutT, 16, 16>(a, st);
-        if (sa == 4) return launch_tiled<OutT, 16, 4>(a, st);
-        return launch_tiled<OutT, 16, 1>(a, st);
-    }
-    if (oa == 4) {
-        if (sa == 16) return launch_tiled<OutT, 4, 16>(a, st);
-        if (sa == 4) return launch_tiled<OutT, 4, 4>(a, st);
-        return launch_tiled<OutT, 4, 1>(a, st);
-    }
-    if (sa == 16) return launch_tiled<OutT, 2, 16>(a, st);
-    if (sa == 4) return launch_tiled<OutT, 2, 4>(a, st);
-    return launch_tiled<OutT, 2, 1>(a, st);
+    if (a.k % 8 == 0) return launch_tiled<OutT, 16>(a, st);
+    if (a.k % 2 == 0) return launch_tiled<OutT, 4>(a, st);
+    return launch_tiled<OutT, 2>(a, st);
 }
 
 }  // namespace

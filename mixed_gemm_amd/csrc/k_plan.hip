@@ -166,6 +166,9 @@ __global__ void __launch_bounds__(256) fold_pack_kernel(const void* __restrict__
     const int j0 = (blockIdx.x * 64 + lane) * 8;
     const bool valid = j0 < K;                       // whole quads agree (K % 32 == 0)
     const int nb = K / 32;
+    const int64_t nwin = sc_nwin(K);
+    // Ws covers whole 256-row scale groups: rows past N get the zero code
+    const int64_t Np = ((int64_t)N + kScRows - 1) / kScRows * kScRows;
     float sv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     int pv[8] = {-1, -1, -1, -1, -1, -1, -1, -1};
     if (valid) {                                     // j0 is a multiple of 8: 16-byte loads
@@ -213,7 +216,7 @@ __global__ void __launch_bounds__(256) fold_pack_kernel(const void* __restrict__
     // outlier channels of row n to WO, then masked to +0 in f; returns the
     // lane's amax of the masked values
     auto extract = [&](int64_t n, float (&f)[8]) {
-        if (omask) {
+        if (omask && n < N) {
             for (uint32_t m = omask; m; m &= m - 1) {
                 const int i = __builtin_ctz(m);
                 float fi = f[0];
@@ -233,6 +236,9 @@ __global__ void __launch_bounds__(256) fold_pack_kernel(const void* __restrict__
         }
         return amax;
     };
+    // the nibbles of row n (lanes inside K, rows inside N) and, from one lane
+    // per quad, the block's scale code (every lane of rows < Np: past K or N
+    // the code 0 of an all-zero block)
     auto encode_store = [&](int64_t n, const float (&f)[8], uint32_t c) {
         const float scale = e8m0_to_f32(c);
         uint32_t word = 0;
@@ -240,35 +246,35 @@ __global__ void __launch_bounds__(256) fold_pack_kernel(const void* __restrict__
         MG_CVT_FP4X2(word, f[2], f[3], scale, 1);
         MG_CVT_FP4X2(word, f[4], f[5], scale, 2);
         MG_CVT_FP4X2(word, f[6], f[7], scale, 3);
-        *reinterpret_cast<uint32_t*>(Wq + n * (K / 2) + j0 / 2) = word;
-        if ((lane & 3) == 0) Ws[n * nb + j0 / 32] = (uint8_t)c;
+        if (valid && n < N) *reinterpret_cast<uint32_t*>(Wq + n * (K / 2) + j0 / 2) = word;
+        if ((lane & 3) == 0) Ws[sc_offset(n, j0 / 32, nwin)] = (uint8_t)(valid ? c : 0u);   // a short stripe's pads: 0
     };
 
     const int64_t wstride = (int64_t)gridDim.y * kFoldWaves;
     if constexpr (LAY == MG_W_1X32) {
-        for (int64_t n = (int64_t)blockIdx.y * kFoldWaves + wave; n < N; n += wstride) {
+        for (int64_t n = (int64_t)blockIdx.y * kFoldWaves + wave; n < Np; n += wstride) {
             float f[8];
             fold_row(n, f);
             const float amax = quad_max_f(extract(n, f));
-            if (valid) encode_store(n, f, e8m0_from_amax_bits(__float_as_uint(amax)));
+            encode_store(n, f, e8m0_from_amax_bits(__float_as_uint(amax)));
         }
     } else if constexpr (LAY == MG_W_128X1) {
         const int ns = (K + 127) / 128;
-        for (int64_t n = (int64_t)blockIdx.y * kFoldWaves + wave; n < N; n += wstride) {
+        for (int64_t n = (int64_t)blockIdx.y * kFoldWaves + wave; n < Np; n += wstride) {
             float f[8];
             fold_row(n, f);
             float amax = quad_max_f(extract(n, f));
             amax = fmaxf(amax, __shfl_xor(amax, 4, 64));      // the stripe's 4 quads (16 lanes)
             amax = fmaxf(amax, __shfl_xor(amax, 8, 64));
             const uint32_t c = e8m0_from_amax_bits(__float_as_uint(amax));
-            if (valid) {
-                encode_store(n, f, c);
-                if ((lane & 15) == 0) Wst[n * ns + j0 / 128] = (uint8_t)c;
-            }
+            encode_store(n, f, c);
+            if (valid && n < N && (lane & 15) == 0) Wst[n * ns + j0 / 128] = (uint8_t)c;
         }
     } else {
-        const int64_t NG = ((int64_t)N + 31) / 32;
-        for (int64_t gi = (int64_t)blockIdx.y * kFoldWaves + wave; gi < NG; gi += wstride) {
+        // 32-row groups through the last scale group (N % 32 == 0: the groups
+        // past N are all pad rows)
+        const int64_t NG = (int64_t)N / 32, NGp = Np / 32;
+        for (int64_t gi = (int64_t)blockIdx.y * kFoldWaves + wave; gi < NGp; gi += wstride) {
             const int64_t n0 = gi * 32;
             float tmax = 0.0f;
             for (int r = 0; r < 32; ++r) {
@@ -281,13 +287,12 @@ __global__ void __launch_bounds__(256) fold_pack_kernel(const void* __restrict__
             const uint32_t c = e8m0_from_amax_bits(__float_as_uint(quad_max_f(tmax)));
             for (int r = 0; r < 32; ++r) {
                 const int64_t n = n0 + r;
-                if (n >= N) break;                       // uniform
                 float f[8];
                 fold_row(n, f);
                 (void)extract(n, f);
-                if (valid) encode_store(n, f, c);
+                encode_store(n, f, c);
             }
-            if (valid && (lane & 3) == 0) Wst[gi * nb + j0 / 32] = (uint8_t)c;
+            if (valid && gi < NG && (lane & 3) == 0) Wst[gi * nb + j0 / 32] = (uint8_t)c;
         }
     }
 }

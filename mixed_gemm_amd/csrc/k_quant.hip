@@ -83,16 +83,15 @@ __device__ __forceinline__ uint32_t encode8(const float (&q)[8], uint32_t& c) {
     return word;
 }
 
-// encode8, then the packed nibbles and, from one lane per quad, the block's
-// scale byte are stored.
-__device__ __forceinline__ void encode_store(const float (&q)[8], int lane, bool valid, uint8_t* aq_row,
-                                             uint8_t* as_row, int j0) {
+// encode8, then the packed nibbles (lanes inside K, rows inside M) and, from
+// one lane per quad, the block's scale byte into the row's 16 bytes of its
+// scale window (every lane: past K or M the code of a zero block).
+__device__ __forceinline__ void encode_store(const float (&q)[8], int lane, bool store_q, uint8_t* aq_row,
+                                             uint8_t* as_win_row, int j0) {
     uint32_t c;
     const uint32_t word = encode8(q, c);
-    if (valid) {
-        *reinterpret_cast<uint32_t*>(aq_row + j0 / 2) = word;
-        if ((lane & 3) == 0) as_row[j0 / 32] = (uint8_t)c;
-    }
+    if (store_q) *reinterpret_cast<uint32_t*>(aq_row + j0 / 2) = word;
+    if ((lane & 3) == 0) as_win_row[lane >> 2] = (uint8_t)c;
 }
 
 template <bool GELU, bool STATS>
@@ -167,15 +166,16 @@ __global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restr
     // resource per row (scalar registers), so lanes whose channels lie past
     // K read zeros and drop their stores by the hardware range check, and so
     // do the lanes that store no scale byte or no outlier value (offset
-    // kNoStore).
+    // kNoStore).  The workgroup's 512 channels are one scale window: a row's
+    // 16 scale bytes are contiguous, lane 4 i storing byte i (past K: the
+    // code 0 of its all-zero block).
     constexpr uint32_t kNoStore = 0x40000000u;
     const uint32_t offX = 2u * (uint32_t)j0, offAq = (uint32_t)j0 / 2u;
-    const uint32_t offAs = (lane & 3) == 0 ? (uint32_t)j0 / 32u : kNoStore;
+    const uint32_t offAs = (lane & 3) == 0 ? (uint32_t)(lane >> 2) : kNoStore;
     const uint32_t offXO = omask ? 2u * (uint32_t)op0 : kNoStore;
     const bool wave_o = __builtin_amdgcn_ballot_w64(omask != 0) != 0;
     const bool wave_rest = __builtin_amdgcn_ballot_w64(omask_rest != 0) != 0;
-    const uint32_t rowX = 2u * (uint32_t)K, rowAq = (uint32_t)K / 2u, rowAs = (uint32_t)K / 32u,
-                   rowXO = 2u * (uint32_t)k;
+    const uint32_t rowX = 2u * (uint32_t)K, rowAq = (uint32_t)K / 2u, rowXO = 2u * (uint32_t)k;
 
     auto rsrc = [](const void* p, uint32_t bytes) {
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
@@ -185,8 +185,10 @@ __global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restr
                                                                                 2));   // nt
     };
 
-    // one row: w its 8 bf16 per lane, pq/ps/po its Aq, As and XO rows
-    auto process_row = [&](u32x4 w, uint8_t* pq, uint8_t* ps, uint16_t* po) {
+    // one row: w its 8 bf16 per lane, pq/ps/po its Aq row, its 16 bytes of
+    // the As window and its XO row; live: a row of X (else a pad row of the
+    // last 256-row scale group, whose Aq and XO stores are dropped)
+    auto process_row = [&](u32x4 w, uint8_t* pq, uint8_t* ps, uint16_t* po, bool live) {
         if constexpr (GELU) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) w[i] = gelu_bf16x2(w[i]);
@@ -217,7 +219,7 @@ __global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restr
             for (int i = 1; i < 4; ++i) wo = (oc0 >> 1) == i ? w[i] : wo;
             const float xo = __uint_as_float((oc0 & 1) ? (wo & 0xFFFF0000u) : (wo << 16));
             const float qo = fast ? div_fast(xo, so, ro) : __fdiv_rn(xo, so);
-            const __amdgpu_buffer_rsrc_t rxo = rsrc(po, rowXO);
+            const __amdgpu_buffer_rsrc_t rxo = rsrc(po, live ? rowXO : 0u);
             if (omask) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_rne(qo), rxo, offXO, 0, 0);
             if (wave_rest) {
                 // further outlier channels of the lane (two or more in its 8)
@@ -235,30 +237,37 @@ __global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restr
         }
         uint32_t c;
         const uint32_t word = encode8(q, c);
-        __builtin_amdgcn_raw_buffer_store_b32(word, rsrc(pq, rowAq), offAq, 0, 0);
-        if ((lane & 3) == 0) __builtin_amdgcn_raw_buffer_store_b8((uint8_t)c, rsrc(ps, rowAs), offAs, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(word, rsrc(pq, live ? rowAq : 0u), offAq, 0, 0);
+        if ((lane & 3) == 0)
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)c, rsrc(ps, (uint32_t)kScBlocks), offAs, 0, 0);
     };
 
     // Rows r0, r0 + rstride, ...: the next row's load is in flight while the
     // current one is processed.  Row addresses advance by a fixed stride
-    // (scalar adds).
-    // The wave's row count n is a 32-bit scalar (64-bit scalar compares do
-    // not exist on this architecture).
+    // (scalar adds).  The rows run on to the end of the last 256-row scale
+    // group, so its pad rows get their zero codes.
+    // The wave's row counts n (with pad rows) and nv (rows of X) are 32-bit
+    // scalars (64-bit scalar compares do not exist on this architecture).
     const int64_t rstride = (int64_t)gridDim.y * kWaves;
     const int64_t r0 = (int64_t)blockIdx.y * kWaves + wave;
-    const int n = r0 < M ? (int)((M - 1 - r0) / rstride) + 1 : 0;
-    const int64_t dX = rstride * K, dQ = rstride * (K / 2), dS = rstride * (K / 32), dO = rstride * k;
+    const int64_t Mp = (M + kScRows - 1) / kScRows * kScRows;
+    const int n = r0 < Mp ? (int)((Mp - 1 - r0) / rstride) + 1 : 0;
+    const int nv = r0 < M ? (int)((M - 1 - r0) / rstride) + 1 : 0;
+    const int64_t dX = rstride * K, dQ = rstride * (K / 2), dO = rstride * k;
+    const int64_t win_stride = sc_nwin(K) * kScWinBytes;     // bytes between 256-row groups of As
+    static_assert(kScRows == 256, "row group = m >> 8");
     const uint16_t* px = X + r0 * K;
     uint8_t* pq = Aq + r0 * (K / 2);
-    uint8_t* ps = As + r0 * (K / 32);
+    uint8_t* const asw = As + (int64_t)blockIdx.x * kScWinBytes;
     uint16_t* po = XO + r0 * k;
-    u32x4 a = load_row(px, n > 0);
+    int64_t m = r0;
+    u32x4 a = load_row(px, nv > 0);
     px += dX;
     for (int i = 0; i < n; ++i) {
-        const u32x4 b = load_row(px, i + 1 < n);
+        const u32x4 b = load_row(px, i + 1 < nv);
         px += dX;
-        process_row(a, pq, ps, po);
-        pq += dQ; ps += dS; po += dO;
+        process_row(a, pq, asw + (m >> 8) * win_stride + (m & 255) * kScBlocks, po, i < nv);   // 256-row groups
+        pq += dQ; po += dO; m += rstride;
         a = b;
     }
     if constexpr (STATS) {
@@ -296,19 +305,23 @@ __global__ void __launch_bounds__(256) quant_f32_kernel(const float* __restrict_
         pv[i] = valid ? pos[j0 + i] : -1;
     }
     const int64_t rstride = (int64_t)gridDim.y * kWaves;
-    for (int64_t r = (int64_t)blockIdx.y * kWaves + wave; r < M; r += rstride) {
+    const int64_t Mp = (M + kScRows - 1) / kScRows * kScRows;   // through the last scale group's pad rows
+    const int64_t nwin = sc_nwin(K);
+    for (int64_t r = (int64_t)blockIdx.y * kWaves + wave; r < Mp; r += rstride) {
+        const bool live = r < M;
         float q[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const float x = valid ? X[r * K + j0 + i] : 0.0f;
+            const float x = valid && live ? X[r * K + j0 + i] : 0.0f;
             mx[i] = fmaxf(mx[i], __builtin_fabsf(x));
             q[i] = __fdiv_rn(x, sv[i]);
             if (pv[i] >= 0) {
-                XO[r * k + pv[i]] = (uint16_t)f32_to_bf16_rne(q[i]);
+                if (live) XO[r * k + pv[i]] = (uint16_t)f32_to_bf16_rne(q[i]);
                 q[i] = 0.0f;
             }
         }
-        encode_store(q, lane, valid, Aq + r * (K / 2), As + r * (K / 32), j0);
+        encode_store(q, lane, valid && live, Aq + r * (K / 2),
+                     As + sc_offset(r, (int32_t)blockIdx.x * kScBlocks, nwin), j0);
     }
     if (amax != nullptr && valid) {
 #pragma unroll

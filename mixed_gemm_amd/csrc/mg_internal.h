@@ -10,6 +10,24 @@ namespace mg {
 // Largest supported input width (LDS-resident per-channel tables in the plan kernels).
 constexpr int32_t kMaxK = 65536;
 
+// Storage order of the E8M0 scale codes of Aq (As) and Wq (Ws): windows of
+// 256 rows x 16 blocks (512 channels), 16 bytes per row, so that one window
+// is 4 KB of contiguous memory -- the unit the GEMM copies into LDS.  Byte
+// (row, block) sits at ((row / 256) * nwin + block / 16) * 4096 +
+// (row % 256) * 16 + block % 16 with nwin = ceil(K / 512); the layout depends
+// on K only.  Blocks past K / 32 and rows past the last row of the final
+// 256-row group hold code 0, the code of an all-zero block.
+constexpr int kScRows = 256;      // rows per window
+constexpr int kScBlocks = 16;     // 32-blocks per window row
+constexpr int kScWinBytes = kScRows * kScBlocks;
+__host__ __device__ constexpr int64_t sc_nwin(int32_t K) { return ((int64_t)K + 511) / 512; }
+__host__ __device__ constexpr int64_t sc_bytes(int64_t rows, int32_t K) {
+    return (rows + kScRows - 1) / kScRows * sc_nwin(K) * kScWinBytes;
+}
+__host__ __device__ constexpr int64_t sc_offset(int64_t row, int32_t blk, int64_t nwin) {
+    return ((row / kScRows) * nwin + blk / kScBlocks) * kScWinBytes + (row % kScRows) * kScBlocks + blk % kScBlocks;
+}
+
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t st);
 hipError_t launch_colmax(const void* X, int32_t dtype, int64_t R, int32_t K, float* out,
                          hipStream_t st);

@@ -23,6 +23,24 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy()
 
 
+def scale_rows(x, rows: int, K: int) -> np.ndarray:
+    """[rows][K/32] E8M0 codes of a scale array (As, Ws) stored in scale
+    windows: the code of (row r, block b) at byte ((r // 256) * nwin + b // 16)
+    * 4096 + (r % 256) * 16 + b % 16, nwin = ceil(K / 512).  Asserts that the
+    bytes the writers fill around the matrix (blocks past K/32, rows up to the
+    end of the last 256-row group) hold code 0."""
+    a = np.ascontiguousarray(host(x) if isinstance(x, torch.Tensor) else np.asarray(x)).reshape(-1)
+    nwin, nb = -(-K // 512), K // 32
+    assert a.dtype == np.uint8 and a.size % (nwin * 4096) == 0, (a.dtype, a.size)
+    groups = a.size // (nwin * 4096)
+    assert groups * 256 >= rows, (groups, rows)
+    full = a.reshape(groups, nwin, 256, 16).transpose(0, 2, 1, 3).reshape(groups * 256, nwin * 16)
+    written = full[: -(-rows // 256) * 256].copy()
+    written[:rows, :nb] = 0
+    assert not written.any(), "scale pad bytes must hold code 0"
+    return np.ascontiguousarray(full[:rows, :nb])
+
+
 def run_pipeline(X: np.ndarray, W: np.ndarray, alpha: float, k: int, layout: str = "1x32",
                  smooth: bool = True, calib_batches: int = 1, score: str = "max") -> dict:
     """calibrate (optionally in several batches) -> weight ranges -> plan -> quantize -> GEMM,
@@ -49,7 +67,8 @@ def run_pipeline(X: np.ndarray, W: np.ndarray, alpha: float, k: int, layout: str
     torch.cuda.synchronize()
     out = dict(act_max=host(act_max), w_max=host(w_max), Y=host(Y), Y32=host(Y32))
     out.update({n: host(t) for n, t in p.tensors().items()})
-    out.update(Aq=host(a.Aq), As=host(a.As), XO=host(a.XO))
+    out["Ws"] = scale_rows(p.Ws, N, K)
+    out.update(Aq=host(a.Aq), As=scale_rows(a.As, M, K), XO=host(a.XO))
     return out
 
 

@@ -5,9 +5,11 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import mixed_gemm_amd as mg
+from tests.gpu_util import scale_rows
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "mixed_gemm.h")
 FAKE = 1 << 20          # aligned, never dereferenced: every call below fails validation first
@@ -43,8 +45,33 @@ def test_plan_and_act_sizes():
     assert b == [4 * 5120, 4 * 5120, 4 * 64, 4 * 5120, 13824 * 2560, 13824 * 160, 0, 2 * 13824 * 64]
     d2 = mg.make_desc(512, 1024, 8, 0.5, "32x32")
     assert mg.mg_plan_bytes(d2)[6] == 32 * 16
-    assert mg.mg_act_bytes(d, 32760) == [32760 * 2560, 32760 * 160, 2 * 32760 * 64]
+    # scales in 256-row x 16-block windows of 4 KB: 128 row groups x 10 windows
+    assert mg.mg_act_bytes(d, 32760) == [32760 * 2560, 128 * 10 * 4096, 2 * 32760 * 64]
     assert mg.mg_act_bytes(d, 0) == [0, 0, 0]
+    d3 = mg.make_desc(352, 96, 3, 0.5, "1x32")               # K % 512 != 0: one window per group
+    assert mg.mg_plan_bytes(d3)[5] == 1 * 1 * 4096
+    assert mg.mg_act_bytes(d3, 300)[1] == 2 * 1 * 4096
+
+
+@pytest.mark.parametrize("rows,K", [(300, 352), (256, 512), (1, 32), (513, 1568)])
+def test_scale_window_layout(rows, K):
+    """The tests' reader of the stored scale order against the header's byte
+    formula applied code by code, and the buffer size against mg_act_bytes."""
+    rng = np.random.default_rng(rows + K)
+    nb, nwin = K // 32, -(-K // 512)
+    codes = rng.integers(1, 255, size=(rows, nb), dtype=np.uint8)
+    buf = np.zeros(-(-rows // 256) * nwin * 4096, dtype=np.uint8)
+    for r in range(rows):
+        for b in range(nb):
+            buf[((r // 256) * nwin + b // 16) * 4096 + (r % 256) * 16 + b % 16] = codes[r, b]
+    assert buf.size == mg.mg_act_bytes(mg.make_desc(K, 32, 0, 0.5, "1x32"), rows)[1]
+    assert buf.size == int(np.prod(mg.scale_shape(rows, K)))
+    assert np.array_equal(scale_rows(buf, rows, K), codes)
+    if buf.size > rows * nb:                                  # a non-zero pad byte is caught
+        pad = np.flatnonzero(buf == 0)[0]
+        buf[pad] = 7
+        with pytest.raises(AssertionError):
+            scale_rows(buf, rows, K)
 
 
 @pytest.mark.parametrize("K,N,k,alpha,layout,smooth,code", [
