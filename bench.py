@@ -38,8 +38,8 @@ PEAK_FP4_TFLOPS = 10100.0          # MI355X dense MXFP4 MFMA (published)
 PEAK_HBM_GBS = 8000.0              # MI355X HBM3E (published)
 METRIC = "dual-branch W4A4 FFN GEMM effective TFLOPS, % MXFP4 MFMA peak (480p/720p)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dual_gemm_ffn0_480p_traffic.json")
-# the dual GEMM's sources: its kernel file and the device header it includes
-GEMM_SRCS = [os.path.join(ROOT, "mixed_gemm_amd", "csrc", f) for f in ("k_gemm.hip", "mg_device.h")]
+# the dual GEMM's sources: its kernel file and the headers it includes
+GEMM_SRCS = [os.path.join(ROOT, "mixed_gemm_amd", "csrc", f) for f in ("k_gemm.hip", "mg_device.h", "mg_internal.h")]
 
 
 def gemm_source_hash() -> str:

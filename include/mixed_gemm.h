@@ -230,10 +230,11 @@ int mg_quantize_act(const mg_plan* p, const void* X, int32_t dtype, int64_t M,
  * the fp32 sum rounded once to nearest-even.  y_dtype MG_F32: Y [M][N] f32
  * holds the fp32 sums unrounded (for callers that keep fp32 activations and
  * for checking the accumulation itself).  M == 0 is a no-op.  Each operand
- * (Aq, Wq, XO, WO) must stay below 3 GiB (32-bit buffer offsets), else
- * MG_ERR_UNSUPPORTED; Y has no limit (it is addressed per output tile).
- * Fastest when K % 512 == 0 and k % 8 == 0; K % 128 == 0 and even k keep
- * most of the speed; other K and odd k are correct but several times slower. */
+ * (Aq, As, Wq, Ws, XO, WO) must stay below 3 GiB (32-bit buffer offsets),
+ * else MG_ERR_UNSUPPORTED; Y has no limit (it is addressed per output tile).
+ * Any K (a multiple of 32) runs at full speed; fastest when k % 8 == 0, an
+ * even k keeps most of the speed, an odd k is correct but several times
+ * slower. */
 int mg_dual_gemm(const mg_plan* p, const mg_act* a, int64_t M, void* Y, int32_t y_dtype,
                  hipStream_t stream);
 
