@@ -46,17 +46,22 @@ __device__ int block_inclusive_scan(int v, int* buf) {
     if (lane == 63) buf[w] = v;
     __syncthreads();
     int add = 0;
-    for (int i = 0; i < w; ++i) add += buf[i];
+#pragma unroll
+    for (int i = 0; i < kTopkThreads / 64; ++i) add += i < w ? buf[i] : 0;   // independent loads
     __syncthreads();                  // buf is free again for the next scan
     return v + add;
 }
 
 // One workgroup.  Scores -- a_j, or RN(a_j / s_j) for the smoothed score --
-// are non-negative floats, compared through their bit patterns (same order).  T = the k-th largest score is found by an MSB-first
-// radix select, 8 bits per pass with a 256-bin histogram in LDS; channels above
-// T are in O, and of the channels equal to T the lowest indices fill the
-// remaining places (tie rule: index ascending).  Thread t owns the contiguous
-// index range [t*C, (t+1)*C) so block scans give ascending order directly.
+// are non-negative floats, compared through their bit patterns (same order).
+// T = the k-th largest score is found by an MSB-first radix select, 8 bits
+// per pass with a 256-bin histogram in LDS; channels above T are in O, and of
+// the channels equal to T the lowest indices fill the remaining places (tie
+// rule: index ascending).  Thread t owns the contiguous index range
+// [t*C, (t+1)*C) so block scans give ascending order directly.  Its C <= CMAX
+// scores are loaded once, all loads in flight together, and every pass runs
+// on the registers.
+template <int CMAX>
 __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const float* __restrict__ a,
                                                             const float* __restrict__ s, int32_t K,
                                                             int32_t k, int32_t* __restrict__ O,
@@ -64,13 +69,18 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const float* __restr
     __shared__ int buf[kTopkThreads];
     __shared__ int hist[256];
     __shared__ uint32_t sel[2];
-    auto key = [&](int j) -> uint32_t {
-        return __float_as_uint(s ? __fdiv_rn(a[j], s[j]) : a[j]);
-    };
     const int t = threadIdx.x;
-    const int C = (K + kTopkThreads - 1) / kTopkThreads;
+    const int C = (K + kTopkThreads - 1) / kTopkThreads;     // <= CMAX (checked by the launcher)
     const int j0 = t * C;
-    const int j1 = min(K, j0 + C);
+    const int n = max(0, min(K, j0 + C) - j0);               // this thread's channels
+    uint32_t kv[CMAX];
+    if (s) {
+#pragma unroll
+        for (int i = 0; i < CMAX; ++i) kv[i] = i < n ? __float_as_uint(__fdiv_rn(a[j0 + i], s[j0 + i])) : 0u;
+    } else {
+#pragma unroll
+        for (int i = 0; i < CMAX; ++i) kv[i] = i < n ? __float_as_uint(a[j0 + i]) : 0u;
+    }
 
     uint32_t T = 0;
     int need = 0;
@@ -80,9 +90,28 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const float* __restr
         for (int shift = 24; shift >= 0; shift -= 8) {
             if (t < 256) hist[t] = 0;
             __syncthreads();
-            for (int j = j0; j < j1; ++j) {
-                const uint32_t kj = key(j);
-                if ((kj & pmask) == prefix) atomicAdd(&hist[(kj >> shift) & 255u], 1);
+            // Counting.  The high bytes of channel maxima take few values (similar
+            // exponents), so one bin can receive most of the 1024 threads' adds:
+            // lanes of a wave with the same bin as a leader lane are counted with
+            // one atomic (two such rounds per key), the rest add one by one.
+#pragma unroll
+            for (int i = 0; i < CMAX; ++i) {
+                if (i < C) {                                              // uniform
+                    bool act = i < n && (kv[i] & pmask) == prefix;
+                    const uint32_t bin = (kv[i] >> shift) & 255u;
+#pragma unroll
+                    for (int r = 0; r < 2; ++r) {
+                        const uint64_t m = __builtin_amdgcn_ballot_w64(act);
+                        if (m != 0) {                                     // uniform
+                            const int leader = __builtin_ctzll(m);
+                            const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)bin, leader);
+                            const uint64_t same = __builtin_amdgcn_ballot_w64(act && bin == b);
+                            if ((t & 63) == leader) atomicAdd(&hist[b], (int)__builtin_popcountll(same));
+                            act = act && bin != b;
+                        }
+                    }
+                    if (act) atomicAdd(&hist[bin], 1);
+                }
             }
             __syncthreads();
             // the bin holding the remaining-th largest key: counts from the top
@@ -95,40 +124,44 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const float* __restr
                 sel[1] = (uint32_t)(remaining - (incl - hv));
             }
             __syncthreads();
+            // sel is written again only after the next pass's scan barriers,
+            // and hist was read before this pass's: no barrier needed here
             prefix |= sel[0] << shift;
             pmask |= 255u << shift;
             remaining = (int)sel[1];
-            __syncthreads();
         }
         T = prefix;
         need = remaining;                         // keys equal to T that are taken
     }
     // ties before my range
     int ties = 0;
-    for (int j = j0; j < j1; ++j) ties += key(j) == T;
-    int tie_off = block_inclusive_scan(ties, buf) - ties;
-    // membership and ascending positions
-    int mine = 0;
+#pragma unroll
+    for (int i = 0; i < CMAX; ++i) ties += i < n && kv[i] == T;
+    const int tie_off = block_inclusive_scan(ties, buf) - ties;
+    // membership (bit i of `in`) and ascending positions
+    uint64_t in = 0;
     {
         int to = tie_off;
-        for (int j = j0; j < j1; ++j) {
-            bool in = k >= K || (k > 0 && (key(j) > T || (key(j) == T && to < need)));
-            to += key(j) == T;
-            mine += in;
+#pragma unroll
+        for (int i = 0; i < CMAX; ++i) {
+            if (i < n) {
+                const bool m = k >= K || (k > 0 && (kv[i] > T || (kv[i] == T && to < need)));
+                to += kv[i] == T;
+                in |= (uint64_t)m << i;
+            }
         }
     }
+    const int mine = __builtin_popcountll(in);
     int off = block_inclusive_scan(mine, buf) - mine;
-    {
-        int to = tie_off;
-        for (int j = j0; j < j1; ++j) {
-            bool in = k >= K || (k > 0 && (key(j) > T || (key(j) == T && to < need)));
-            to += key(j) == T;
-            if (in) {
-                O[off] = j;
-                pos[j] = off;
+#pragma unroll
+    for (int i = 0; i < CMAX; ++i) {
+        if (i < n) {
+            if ((in >> i) & 1u) {
+                O[off] = j0 + i;
+                pos[j0 + i] = off;
                 ++off;
             } else {
-                pos[j] = -1;
+                pos[j0 + i] = -1;
             }
         }
     }
@@ -308,7 +341,16 @@ hipError_t launch_smooth(const float* a, const float* w, int32_t K, double alpha
 
 hipError_t launch_topk(const float* a, const float* s, int32_t K, int32_t k, int32_t* O, int32_t* pos,
                        hipStream_t st) {
-    hipLaunchKernelGGL(topk_kernel, dim3(1), dim3(kTopkThreads), 0, st, a, s, K, k, O, pos);
+    const int C = (K + kTopkThreads - 1) / kTopkThreads;    // scores per thread (K <= kMaxK: C <= 64)
+    static_assert(kMaxK <= 64 * kTopkThreads, "top-k holds at most 64 scores per thread");
+    if (C <= 8)
+        hipLaunchKernelGGL(topk_kernel<8>, dim3(1), dim3(kTopkThreads), 0, st, a, s, K, k, O, pos);
+    else if (C <= 16)
+        hipLaunchKernelGGL(topk_kernel<16>, dim3(1), dim3(kTopkThreads), 0, st, a, s, K, k, O, pos);
+    else if (C <= 32)
+        hipLaunchKernelGGL(topk_kernel<32>, dim3(1), dim3(kTopkThreads), 0, st, a, s, K, k, O, pos);
+    else
+        hipLaunchKernelGGL(topk_kernel<64>, dim3(1), dim3(kTopkThreads), 0, st, a, s, K, k, O, pos);
     return hipGetLastError();
 }
 
