@@ -17,6 +17,10 @@
 // RN(1/s) and outlier masks of a lane's 8 channels stay in registers for all
 // of its rows.  Rows are read and written through buffer resources built per
 // row in scalar registers, so channels past K need no per-lane bounds code.
+// The codes As[m][b] are stored in scale windows of 256 rows x 16 blocks
+// (sc_offset): a workgroup's 512 channels are one window, so a row's 16
+// codes are 16 contiguous bytes; the rows run on to the end of the last
+// 256-row group, whose pad rows (and the blocks past K) get code 0.
 //
 // With GELU, X is the previous projection's bf16 output and the quantized
 // input is h = gelu_bf16x2 of X (the FFN block's hidden activation), computed
