@@ -173,3 +173,23 @@ def test_percentile_state_validation():
     assert L.mg_pct_reset(ctypes.byref(mg.mg_pct(None, FAKE, 64, 0)), None) == -1
     assert L.mg_pct_reset(ctypes.byref(mg.mg_pct(FAKE, FAKE, 64, 1)), None) == -1
     assert L.mg_pct_reset(None, None) == -1
+
+
+def test_missing_library_and_host_tensors_fail_loudly(tmp_path):
+    """No fallback: without the built library every entry point raises, and a
+    host tensor is refused before any library call."""
+    import torch
+    saved_lib, saved_path = mg._lib, mg.LIB_PATH
+    try:
+        mg._lib = None
+        mg.LIB_PATH = str(tmp_path / "libmissing.so")
+        with pytest.raises(RuntimeError, match="not built"):
+            mg.lib()
+        with pytest.raises(RuntimeError, match="not built"):
+            mg.mg_version()
+        with pytest.raises(RuntimeError, match="not built"):
+            mg.mg_calib_reset(torch.zeros(32))
+    finally:
+        mg._lib, mg.LIB_PATH = saved_lib, saved_path
+    with pytest.raises(ValueError, match="device tensor"):
+        mg.mg_calib_reset(torch.zeros(32))
