@@ -102,6 +102,37 @@ def test_smoothed_score(layout):
     assert not np.array_equal(o["O"], _oracle(X, W, 0.5, 16, layout)["O"])
 
 
+@pytest.mark.parametrize("layout", ["1x32", "32x32", "128x1"])
+@pytest.mark.parametrize("M,K,N,k,bf16", [(300, 352, 96, 6, True), (600, 800, 288, 12, False)])
+def test_scale_pads_written_over_garbage(M, K, N, k, bf16, layout):
+    """Ragged M, N and K (not multiples of 256, 256 and 512): over scale
+    buffers pre-filled with 0xFF (the E8M0 NaN code), the writers fill every
+    pad row and pad block of the scale windows with code 0 (checked by
+    scale_rows), the codes equal the oracle's, and the output is exact."""
+    X, W = _heavy(M, K, N, 70 + K, bf16=bf16)
+    Xd, Wd = dev(X), dev(W)
+    act_max = mg.calibrate([Xd], K)
+    w_max = torch.empty(K, dtype=torch.float32, device="cuda")
+    mg.mg_weight_range(Wd, w_max)
+    desc = mg.make_desc(K, N, k, 0.6, layout)
+    p = mg.Plan.empty(desc)
+    p.Ws.fill_(0xFF)
+    mg.mg_plan_build(p, act_max, w_max, Wd)
+    a = mg.Act.empty(desc, M)
+    a.As.fill_(0xFF)
+    mg.mg_quantize_act(p, Xd, a)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    Y32 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    mg.mg_dual_gemm(p, a, Y)
+    mg.mg_dual_gemm(p, a, Y32)
+    torch.cuda.synchronize()
+    o = _oracle(X, W, 0.6, k, layout)
+    assert np.array_equal(scale_rows(p.Ws, N, K), o["Ws"])
+    assert np.array_equal(scale_rows(a.As, M, K), o["As"])
+    assert np.array_equal(host(a.Aq), o["Aq"]) and np.array_equal(host(p.Wq), o["Wq"])
+    check_output(host(Y), host(Y32), o["Y64"])
+
+
 def test_smoothing_off():
     X, W = _heavy(200, 256, 128, 88)
     g = run_pipeline(X, W, 0.5, 8, smooth=False)
