@@ -62,13 +62,17 @@ def test_tiny_workload_all_stages():
 
 @pytest.mark.parametrize("M,K,N,k", [(257, 512, 192, 16), (1000, 1024, 320, 64), (64, 96, 64, 5),
                                      (33, 256, 96, 0), (130, 128, 64, 128), (4095, 640, 256, 40),
-                                     (300, 768, 256, 24), (200, 384, 128, 6), (300, 512, 192, 70)])
+                                     (300, 768, 256, 24), (200, 384, 128, 6), (300, 512, 192, 70),
+                                     (1, 32, 32, 0), (5, 32, 32, 1), (513, 1056, 288, 16),
+                                     (100, 1568, 64, 31), (64, 4128, 96, 130)])
 def test_bf16_shapes(M, K, N, k):
-    """Shapes across the GEMM's code paths: scale rows 16-byte aligned (K % 512
-    == 0), 4-byte aligned (K % 128 == 0; K = 768 has an odd number of 256-deep
-    stages, so its last scale window is half past the row) or unaligned, and
-    outlier rows of whole 16-byte chunks (k % 8 == 0), of 4-byte words (even k;
-    k = 70 spans two outlier stages, the second partial) or neither."""
+    """Shapes across the GEMM's code paths: scale windows whole (K % 512 == 0)
+    or with a partial last window (K = 768 also has an odd number of 256-deep
+    stages, so the last window's second half is all pad; K = 4128 ends in a
+    window of one block; K = 32 is one block in one stage), M and N not
+    multiples of the 256x256 tile (M = 1 included), and outlier rows of whole
+    16-byte chunks (k % 8 == 0), of 4-byte words (even k; k = 70 and 130 span
+    two and three outlier stages, the last partial) or neither (odd k)."""
     X, W = _heavy(M, K, N, 1000 + M)
     g = run_pipeline(X, W, 0.6, k)
     _compare(g, _oracle(X, W, 0.6, k))
