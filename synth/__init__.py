@@ -57,12 +57,15 @@ def _normal_rows(g: np.random.Generator, M: int, K: int) -> Iterator[tuple[int, 
         yield r0, g.standard_normal((r1 - r0, K), dtype=np.float32)
 
 
-def gelu_tanh_f32(x: np.ndarray) -> np.ndarray:
-    """Input recipe only (shapes the ffn.2 input distribution), float32."""
-    x = x.astype(np.float32)
-    c = np.float32(0.7978845608)
-    inner = c * (x + np.float32(0.044715) * x * x * x)
-    return (np.float32(0.5) * x * (np.float32(1.0) + np.tanh(inner))).astype(np.float32)
+def rectified_lobe_f32(z: np.ndarray) -> np.ndarray:
+    """Input shaping for the hidden activations that feed a down-projection:
+    z itself where z >= 0, a small bounded negative lobe below (0.17 z on
+    (-1, 0), -0.17 from -1 down).  It has the shape of an activation-function
+    output -- a heavy positive tail, negatives no lower than about -0.17 --
+    without evaluating the layer's own activation function, which belongs to
+    the path under test.  float32."""
+    z = z.astype(np.float32)
+    return np.where(z >= 0, z, np.float32(0.17) * np.maximum(z, np.float32(-1.0))).astype(np.float32)
 
 
 def heavy_tail_act(M: int, K: int, *, sigma: float, frac: float, mult: float,
@@ -113,13 +116,14 @@ def drifting_act(M: int, K: int, steps: int, *, sigma: float, frac: float, mult:
 
 
 def gelu_act(M: int, K: int, *, frac: float, mult: float, ch_seed: int, x_seed: int) -> np.ndarray:
-    """bf16 GELU-tanh of an N(0,1) pre-activation with round(frac*K) channels x mult."""
+    """bf16 hidden activations of a GELU-gated FFN: rectified_lobe_f32 of an
+    N(0,1) pre-activation with round(frac*K) channels x mult."""
     ch = pick_channels(K, frac, ch_seed)
     g = rng(x_seed)
     out = np.empty((M, K), dtype=np.uint16)
     for r0, z in _normal_rows(g, M, K):
         z[:, ch] *= np.float32(mult)
-        out[r0:r0 + z.shape[0]] = f32_to_bf16_bits(gelu_tanh_f32(z))
+        out[r0:r0 + z.shape[0]] = f32_to_bf16_bits(rectified_lobe_f32(z))
     return out
 
 
@@ -178,7 +182,7 @@ TINY = Workload("tiny_256x512x1024", 256, 512, 1024, 8, 0.5, "f32", "heavy",
 # Wan2.2-A14B FFN up-projection at 480p (21x30x52 tokens), 5120 -> 13824.
 FFN0_480P = Workload("ffn0_480p_32760x5120x13824", 32760, 5120, 13824, 64, 0.6, "bf16", "heavy",
                      0.25, 0.02, 25.0, 0.02, 0.6, 201, 202, 203)
-# FFN down-projection at 480p, 13824 -> 5120, GELU-tanh input with 1% channels x20.
+# FFN down-projection at 480p, 13824 -> 5120: hidden activations (rectified_lobe_f32) with 1% channels x20.
 FFN2_480P = Workload("ffn2_480p_32760x13824x5120", 32760, 13824, 5120, 128, 0.5, "bf16", "gelu",
                      1.0, 0.01, 20.0, 0.01, None, 301, 302, 303)
 # FFN up-projection at 720p (21x45x80 tokens).

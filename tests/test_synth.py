@@ -55,3 +55,7 @@ def test_large_workload_small_slice():
     g = synth.FFN2_480P.make_x(M=8)
     assert g.shape == (8, 13824)
     assert synth.pick_channels(13824, 0.01, 301).size == 138
+    h = synth.bf16_bits_to_f32(g)
+    # the shape of an activation output: negatives bounded near -0.17, a heavy positive tail
+    assert h.min() >= -0.171 and (h < 0).mean() > 0.3
+    assert h[:, synth.pick_channels(13824, 0.01, 301)].max() > 20.0
