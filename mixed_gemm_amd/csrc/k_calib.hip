@@ -5,7 +5,8 @@
 //
 // HBM-bound column reduction.  Each lane owns 16 bytes of one row (8 bf16 or
 // 4 f32 channels) so a wave reads 1 KiB contiguous per row; the 4 waves of a
-// workgroup walk interleaved rows, keep running maxima of |x| as integer bit
+// workgroup walk interleaved rows (four rows' streaming loads in flight per
+// lane), keep running maxima of |x| as integer bit
 // patterns in registers, combine through LDS, and fold into the output with
 // one integer atomicMax per channel (non-negative floats order like their
 // bit patterns, so the result is exact and independent of order).
@@ -38,7 +39,32 @@ __global__ void __launch_bounds__(256) colmax_kernel(const void* __restrict__ X,
     for (int v = 0; v < VEC; ++v) m[v] = 0;
     if (valid) {
         const int64_t rstride = (int64_t)gridDim.y * kWaves;
-        for (int64_t r = (int64_t)blockIdx.y * kWaves + wave; r < R; r += rstride) {
+        typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+        auto at = [&](int64_t r) {
+            return reinterpret_cast<const v4u*>(reinterpret_cast<const uint8_t*>(X) +
+                                                (r * K + chunk * VEC) * (BF16 ? 2 : 4));
+        };
+        int64_t r = (int64_t)blockIdx.y * kWaves + wave;
+        // four rows' streaming loads in flight together, then their maxima
+        for (; r + 3 * rstride < R; r += 4 * rstride) {
+            v4u d[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) d[u] = __builtin_nontemporal_load(at(r + u * rstride));
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if constexpr (BF16) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        m[2 * i] = max(m[2 * i], (d[u][i] & 0x7FFFu) << 16);
+                        m[2 * i + 1] = max(m[2 * i + 1], d[u][i] & 0x7FFF0000u);
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) m[i] = max(m[i], d[u][i] & 0x7FFFFFFFu);
+                }
+            }
+        }
+        for (; r < R; r += rstride) {
             const uint4 d = *reinterpret_cast<const uint4*>(
                 reinterpret_cast<const uint8_t*>(X) + (r * K + chunk * VEC) * (BF16 ? 2 : 4));
             const uint32_t w[4] = {d.x, d.y, d.z, d.w};
