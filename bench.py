@@ -163,9 +163,11 @@ def _suite_tools():
     def y_host(t):
         return t.view(torch.int16).cpu().numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.cpu().numpy()
 
-    def timed(fn, reps=10, warmup=2, cold=False):
-        """mean ms of fn() over reps launches, HIP events on the current stream;
-        cold: a 1 GiB write before each launch, outside the timed interval."""
+    def timed(fn, reps=10, warmup=20, cold=False):
+        """mean ms of fn() over reps launches after `warmup` untimed ones (the
+        first ~10-20 launches after a pause run up to ~10% slower), HIP events on
+        the current stream; cold: a 1 GiB write before each launch, outside the
+        timed interval."""
         for _ in range(warmup):
             fn()
         ts = []
@@ -415,7 +417,8 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=30,
+                    help="untimed steps first: the GEMM needs ~20 launches to reach its steady rate")
     ap.add_argument("--workload", default="ffn0_480p_32760x5120x13824")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0,
