@@ -13,6 +13,8 @@ bf16 data travels in ``torch.bfloat16`` (or 16-bit integer) tensors.
 from __future__ import annotations
 
 import ctypes
+import functools
+import inspect
 import os
 from dataclasses import dataclass
 
@@ -119,6 +121,26 @@ def _stream(stream) -> int:
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream
     return int(stream)
+
+
+def _on_stream(fn):
+    """Run a helper that allocates temporaries with torch's current stream set
+    to its `stream` argument (a torch stream or a raw hipStream_t handle), so
+    the caching allocator ties them to the stream whose kernels use them: a
+    block freed on another stream could be handed out again while those
+    kernels still read it."""
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def wrap(*args, **kwargs):
+        stream = sig.bind(*args, **kwargs).arguments.get("stream")
+        if stream is None:
+            return fn(*args, **kwargs)
+        if not isinstance(stream, torch.cuda.Stream):
+            stream = torch.cuda.ExternalStream(int(stream))
+        with torch.cuda.stream(stream):
+            return fn(*args, **kwargs)
+    return wrap
 
 
 def _ptr(t: torch.Tensor | None) -> int | None:
@@ -335,6 +357,7 @@ def mg_pct_select(st: PctState, pass_: int, q: float, score: torch.Tensor | None
 
 # ----------------------------------------------------------------------------- convenience
 
+@_on_stream
 def percentile(batches, K: int, q: float, device="cuda", stream=None) -> torch.Tensor:
     """Per-channel nearest-rank q-quantile of |x| over all rows of the given
     [M][K] bf16 device tensors (two passes over the batches)."""
@@ -351,6 +374,7 @@ def percentile(batches, K: int, q: float, device="cuda", stream=None) -> torch.T
     return score
 
 
+@_on_stream
 def calibrate(batches, K: int, device="cuda", stream=None) -> torch.Tensor:
     """Running per-channel activation maxima over an iterable of [M][K] device tensors."""
     act_max = torch.empty(K, dtype=torch.float32, device=device)
@@ -360,6 +384,7 @@ def calibrate(batches, K: int, device="cuda", stream=None) -> torch.Tensor:
     return act_max
 
 
+@_on_stream
 def plan(act_max: torch.Tensor, W: torch.Tensor, alpha: float, k: int, layout: str = "1x32",
          smooth: bool = True, stream=None, score: str = "max", rank: torch.Tensor | None = None) -> Plan:
     """calibrated maxima + weights -> a built plan (weight ranges, Eq. (2), Eq. (4), fold + pack).
@@ -378,6 +403,7 @@ def plan(act_max: torch.Tensor, W: torch.Tensor, alpha: float, k: int, layout: s
     return p
 
 
+@_on_stream
 def forward(p: Plan, X: torch.Tensor, act: Act | None = None, Y: torch.Tensor | None = None,
             stream=None) -> torch.Tensor:
     M = X.shape[0]
@@ -389,6 +415,7 @@ def forward(p: Plan, X: torch.Tensor, act: Act | None = None, Y: torch.Tensor | 
     return Y
 
 
+@_on_stream
 def reference_plan(W: torch.Tensor, stream=None) -> Plan:
     """A plan that routes every channel through the bf16 branch with no
     smoothing (k = K, s = 1): forward() then computes the plain bf16 GEMM
@@ -459,6 +486,7 @@ class FFNBlock:
     plan2: Plan
 
 
+@_on_stream
 def ffn_block_stats(calib_batches, W0: torch.Tensor, on_hidden=None, stream=None):
     """Calibration statistics of both projections of an FFN block from the
     same batches: ffn.0's from the batches themselves, ffn.2's from the
@@ -486,6 +514,7 @@ def ffn_block_stats(calib_batches, W0: torch.Tensor, on_hidden=None, stream=None
     return act0, act2
 
 
+@_on_stream
 def ffn_block_plans(act0: torch.Tensor, act2: torch.Tensor, W0: torch.Tensor, W2: torch.Tensor,
                     alpha0: float, k0: int, alpha2: float, k2: int, layout: str = "1x32",
                     stream=None) -> FFNBlock:
@@ -493,6 +522,7 @@ def ffn_block_plans(act0: torch.Tensor, act2: torch.Tensor, W0: torch.Tensor, W2
                     plan(act2, W2, alpha2, k2, layout, stream=stream))
 
 
+@_on_stream
 def ffn_block_forward(blk: FFNBlock, X: torch.Tensor, stream=None) -> torch.Tensor:
     """Y2 = ffn.2(gelu(ffn.0(X))): ffn.0's forward, then GELU and ffn.2's
     activation quantization in one pass (mg_gelu_quantize_act), then ffn.2's

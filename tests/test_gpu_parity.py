@@ -261,3 +261,31 @@ def test_empty_inputs_are_noops():
     mg.mg_quantize_act(p, X, a)
     torch.cuda.synchronize()
     assert torch.all(act_max == 0)
+
+
+def test_helpers_on_a_side_stream():
+    """The binding's allocating helpers run on an explicit stream (a torch
+    stream, or a raw hipStream_t handle) with their temporaries allocated on
+    that stream, bit for bit the default stream's results."""
+    M, K, N, k = 600, 512, 256, 12
+    X, W = _heavy(M, K, N, 505)
+    Xd, Wd = dev(X), dev(W)
+    act = mg.calibrate([Xd], K)
+    ref_p = mg.plan(act, Wd, 0.6, k)
+    ref_y = mg.forward(ref_p, Xd)
+    W2d = dev(synth.weights(K, N, sigma=0.02, clip=0.6, seed=506, bf16=True))       # [512][256]: 256 -> 512
+    act2 = mg.calibrate([torch.relu(ref_y.float()).to(torch.bfloat16)], N)
+    blk = mg.ffn_block_plans(act, act2, Wd, W2d, 0.6, k, 0.5, 8)
+    ref_b = mg.ffn_block_forward(blk, Xd)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    for st in (side, side.cuda_stream):
+        a = mg.calibrate([Xd], K, stream=st)
+        p = mg.plan(a, Wd, 0.6, k, stream=st)
+        y = mg.forward(p, Xd, stream=st)
+        b = mg.ffn_block_forward(blk, Xd, stream=st)
+        side.synchronize()
+        assert torch.equal(a, act)
+        assert torch.equal(p.Wq, ref_p.Wq) and torch.equal(p.Ws, ref_p.Ws) and torch.equal(p.O, ref_p.O)
+        assert torch.equal(y.view(torch.int16), ref_y.view(torch.int16))
+        assert torch.equal(b.view(torch.int16), ref_b.view(torch.int16))
