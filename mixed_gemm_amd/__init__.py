@@ -224,6 +224,23 @@ class Plan:
         return dict(s=self.s, rcp=self.rcp, O=self.O, pos=self.pos, Wq=self.Wq, Ws=self.Ws, Wst=self.Wst,
                     WO=self.WO)
 
+    def state(self) -> dict:
+        """The plan as plain data (descriptor fields and tensors) for torch.save;
+        a plan holds no other state."""
+        d = {f: getattr(self.desc, f) for f, _ in mg_plan_desc._fields_}
+        return {"desc": d, "tensors": self.tensors()}
+
+    @staticmethod
+    def from_state(state: dict, device="cuda") -> "Plan":
+        """A plan from state() (e.g. after torch.load(..., weights_only=True)),
+        its buffers checked against mg_plan_bytes."""
+        desc = mg_plan_desc(**state["desc"])
+        p = Plan(desc, **{n: t.to(device) for n, t in state["tensors"].items()})
+        got = [t.numel() * t.element_size() for t in p.tensors().values()]
+        if got != mg_plan_bytes(desc):
+            raise ValueError(f"plan buffer sizes {got} differ from mg_plan_bytes")
+        return p
+
 
 @dataclass
 class Act:

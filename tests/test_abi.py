@@ -193,3 +193,24 @@ def test_missing_library_and_host_tensors_fail_loudly(tmp_path):
         mg._lib, mg.LIB_PATH = saved_lib, saved_path
     with pytest.raises(ValueError, match="device tensor"):
         mg.mg_calib_reset(torch.zeros(32))
+
+
+def test_plan_state_round_trip(tmp_path):
+    """Plan.state() survives torch.save / torch.load(weights_only=True), and
+    from_state() rejects buffers of the wrong size (host tensors: no GPU)."""
+    import torch
+    for layout in ("1x32", "32x32", "128x1"):
+        d = mg.make_desc(544, 96, 10, 0.6, layout, True, "smoothed")
+        p = mg.Plan.empty(d, device="cpu")
+        for i, t in enumerate(p.tensors().values()):
+            t.view(torch.uint8).view(-1).copy_(torch.arange(t.numel() * t.element_size()) % 251)
+        torch.save(p.state(), tmp_path / "p.pt")
+        q = mg.Plan.from_state(torch.load(tmp_path / "p.pt", weights_only=True), device="cpu")
+        assert [getattr(q.desc, f) for f, _ in mg.mg_plan_desc._fields_] == \
+               [getattr(d, f) for f, _ in mg.mg_plan_desc._fields_]
+        for n, t in p.tensors().items():
+            assert torch.equal(t, getattr(q, n)), n
+        bad = p.state()
+        bad["tensors"]["Ws"] = bad["tensors"]["Ws"].reshape(-1)[:16]
+        with pytest.raises(ValueError):
+            mg.Plan.from_state(bad, device="cpu")

@@ -289,3 +289,18 @@ def test_helpers_on_a_side_stream():
         assert torch.equal(p.Wq, ref_p.Wq) and torch.equal(p.Ws, ref_p.Ws) and torch.equal(p.O, ref_p.O)
         assert torch.equal(y.view(torch.int16), ref_y.view(torch.int16))
         assert torch.equal(b.view(torch.int16), ref_b.view(torch.int16))
+
+
+def test_plan_saved_and_loaded(tmp_path):
+    """A plan is plain data: torch.save of Plan.state(), torch.load with
+    weights_only=True and Plan.from_state() give the same forward, bit for bit."""
+    M, K, N, k = 300, 544, 96, 10
+    X, W = _heavy(M, K, N, 611)
+    Xd, Wd = dev(X), dev(W)
+    for layout in ("1x32", "32x32", "128x1"):
+        p = mg.plan(mg.calibrate([Xd], K), Wd, 0.6, k, layout)
+        y = mg.forward(p, Xd)
+        path = tmp_path / f"plan_{layout}.pt"
+        torch.save(p.state(), path)
+        q = mg.Plan.from_state(torch.load(path, weights_only=True))
+        assert torch.equal(mg.forward(q, Xd).view(torch.int16), y.view(torch.int16)), layout
