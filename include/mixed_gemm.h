@@ -188,7 +188,8 @@ typedef struct {
 int mg_pct_reset(const mg_pct* st, hipStream_t stream);
 
 /* Adds the M rows of X [M][K] (bf16) to pass `pass` (0 or 1).  M == 0 is a
- * no-op.  Pass 1 reads sel (written by mg_pct_select pass 0). */
+ * no-op; M above 65535^2 (4.29e9) rows in one call is MG_ERR_UNSUPPORTED
+ * (split the batch).  Pass 1 reads sel (written by mg_pct_select pass 0). */
 int mg_pct_count(const mg_pct* st, int32_t pass, const uint16_t* X, int64_t M, hipStream_t stream);
 
 /* Pass 0: from the counts and q, sel := (high byte, rank inside it) per

@@ -13,9 +13,10 @@
 //   pass 1: per channel, a histogram of the low 7 bits of the values whose
 //           high byte is h;
 //   select 1: the low bits l holding rank r'; the value is (h << 7) | l.
-// Counting: a workgroup takes 32 channels (64 B of each row: a lane loads 8
-// channels, 4 lanes a row piece, 64 rows per step, 4 rows in flight per
-// lane) over a chunk of rows and counts into 32 x 256 LDS bins with LDS
+// Counting: a workgroup takes 64 channels (128 B of each row, a whole cache
+// line: a lane loads 8 channels, 8 lanes a row piece, 32 rows per step, 4
+// rows in flight per lane) over a chunk of at most 65535 rows and counts into
+// 64 x 256 16-bit LDS counters (two channels per 32-bit word) with LDS
 // atomics, then adds its non-zero bins into the global [K][256] histogram.
 #include "mg_device.h"
 #include "mg_internal.h"
@@ -24,10 +25,11 @@ namespace mg {
 
 namespace {
 
-constexpr int kPctCh = 32;        // channels per workgroup
+constexpr int kPctCh = 64;        // channels per workgroup: 128 bytes of a bf16 row, one cache line
 constexpr int kPctBins = 256;
-constexpr int kPctStride = 257;   // LDS words per channel: equal bins of different channels in different banks
+constexpr int kPctStride = 257;   // LDS words per channel pair: equal bins of different pairs in different banks
 constexpr int kPctUnroll = 4;     // rows in flight per thread
+constexpr int64_t kPctMaxRows = 65535;   // rows per workgroup chunk: a 16-bit counter cannot overflow
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -41,45 +43,49 @@ __global__ void __launch_bounds__(256) pct_count_kernel(const uint16_t* __restri
                                                         int64_t rows_per_chunk, int pass,
                                                         const int32_t* __restrict__ sel,
                                                         uint32_t* __restrict__ hist) {
-    __shared__ uint32_t bins[kPctCh * kPctStride];
+    // bins of channel c (of the workgroup's 64) are the 16-bit half c / 32 of
+    // words (c % 32) * 257 + bin: two channels share a word, which keeps the
+    // histograms of 64 channels in 33 KB
+    __shared__ uint32_t bins[(kPctCh / 2) * kPctStride];
     const int t = threadIdx.x;
-    for (int i = t; i < kPctCh * kPctStride; i += 256) bins[i] = 0;
+    for (int i = t; i < (kPctCh / 2) * kPctStride; i += 256) bins[i] = 0;
     // a thread owns 8 consecutive channels (16 bytes of a row) and rows
-    // rho, rho + 64, ...; it visits its channels starting at rho % 8, so the
+    // rho, rho + 32, ...; it visits its channels starting at rho % 8, so the
     // lanes of a wave that share channels mostly update different channels
-    const int g = t & 3, rho = t >> 2;
+    const int g = t & 7, rho = t >> 3;
     const int c0 = blockIdx.x * kPctCh + 8 * g;        // K % 32 == 0: all 8 in range or none
     const bool valid = c0 < K;
+    const uint32_t inc = g >= 4 ? 0x10000u : 1u;       // the counter half of this thread's channels
     int hsel[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) hsel[e] = (pass == 1 && valid) ? sel[2 * (c0 + e)] : -1;
     __syncthreads();
     const int64_t r_begin = (int64_t)blockIdx.y * rows_per_chunk;
     const int64_t r_end = r_begin + rows_per_chunk < M ? r_begin + rows_per_chunk : M;
-    uint32_t* bg = bins + 8 * g * kPctStride;
+    uint32_t* bg = bins + 8 * (g & 3) * kPctStride;
     if (valid) {
-        for (int64_t r0 = r_begin + rho; r0 < r_end; r0 += 64 * kPctUnroll) {
+        for (int64_t r0 = r_begin + rho; r0 < r_end; r0 += 32 * kPctUnroll) {
             u32x4 w[kPctUnroll];
 #pragma unroll
             for (int u = 0; u < kPctUnroll; ++u) {
-                const int64_t r = r0 + 64 * u;
+                const int64_t r = r0 + 32 * u;
                 w[u] = r < r_end ? *reinterpret_cast<const u32x4*>(X + r * K + c0) : u32x4{0, 0, 0, 0};
             }
 #pragma unroll
             for (int u = 0; u < kPctUnroll; ++u) {
-                if (r0 + 64 * u >= r_end) break;
+                if (r0 + 32 * u >= r_end) break;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const int e = (i + rho) & 7;
+                    const int e = (i + rho + 4 * (g >> 2)) & 7;   // halves g and g + 4 share words: offset
                     const uint32_t a = half_of(w[u], e) & 0x7FFFu;
                     const uint32_t hi = a >> 7;
                     int h_e = hsel[0];
 #pragma unroll
                     for (int f = 1; f < 8; ++f) h_e = e == f ? hsel[f] : h_e;
                     if (pass == 0)
-                        atomicAdd(bg + e * kPctStride + hi, 1u);
+                        atomicAdd(bg + e * kPctStride + hi, inc);
                     else if ((int)hi == h_e)
-                        atomicAdd(bg + e * kPctStride + (a & 0x7Fu), 1u);
+                        atomicAdd(bg + e * kPctStride + (a & 0x7Fu), inc);
                 }
             }
         }
@@ -88,7 +94,7 @@ __global__ void __launch_bounds__(256) pct_count_kernel(const uint16_t* __restri
     for (int i = t; i < kPctCh * kPctBins; i += 256) {
         const int ch = i / kPctBins, b = i % kPctBins;
         const int c = blockIdx.x * kPctCh + ch;
-        const uint32_t v = bins[ch * kPctStride + b];
+        const uint32_t v = (bins[(ch & 31) * kPctStride + b] >> (16 * (ch >> 5))) & 0xFFFFu;
         if (v && c < K) atomicAdd(hist + (int64_t)c * kPctBins + b, v);
     }
 }
@@ -154,10 +160,13 @@ hipError_t launch_pct_count(const uint16_t* X, int64_t M, int32_t K, int pass, c
                             hipStream_t st) {
     if (M <= 0) return hipSuccess;
     const int gx = (K + kPctCh - 1) / kPctCh;
-    // about 8 workgroups per CU (33 KB of LDS each), row chunks of at least 256 rows
+    // about 8 workgroups per CU (33 KB of LDS each), row chunks of at least 256
+    // rows and at most kPctMaxRows (16-bit counters)
     int64_t gy = ((int64_t)device_cu_count() * 8 + gx - 1) / gx;
     int64_t max_gy = (M + 255) / 256;
     if (gy > max_gy) gy = max_gy;
+    const int64_t min_gy = (M + kPctMaxRows - 1) / kPctMaxRows;
+    if (gy < min_gy) gy = min_gy;
     if (gy < 1) gy = 1;
     if (gy > 65535) gy = 65535;
     const int64_t rows = (M + gy - 1) / gy;

@@ -198,6 +198,8 @@ int mg_pct_count(const mg_pct* st, int32_t pass, const uint16_t* X, int64_t M, h
     if (int e = check_pct(st)) return e;
     if (int e = check_pass(pass)) return e;
     if (M < 0) return fail(MG_ERR_SHAPE, "M=%lld must be >= 0", (long long)M);
+    // at most 65535 row chunks of at most 65535 rows (16-bit per-workgroup counters)
+    if (M > 65535ll * 65535ll) return fail(MG_ERR_UNSUPPORTED, "M=%lld exceeds 65535^2 rows per call", (long long)M);
     if (M == 0) return MG_OK;
     MG_CHECK_PTR(X, "X");
     hipError_t h = mg::launch_pct_count(X, M, st->K, pass, st->sel, st->hist, stream);

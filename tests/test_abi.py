@@ -169,6 +169,7 @@ def test_percentile_state_validation():
     assert L.mg_pct_count(ctypes.byref(st), 0, None, 8, None) == -1
     assert L.mg_pct_count(ctypes.byref(st), 0, FAKE + 4, 8, None) == -4
     assert L.mg_pct_count(ctypes.byref(st), 0, None, 0, None) == 0            # M == 0: no-op
+    assert L.mg_pct_count(ctypes.byref(st), 0, FAKE, 65535 * 65535 + 1, None) == -5   # 16-bit counters
     assert L.mg_pct_reset(ctypes.byref(mg.mg_pct(FAKE, FAKE, 60, 0)), None) == -2
     assert L.mg_pct_reset(ctypes.byref(mg.mg_pct(None, FAKE, 64, 0)), None) == -1
     assert L.mg_pct_reset(ctypes.byref(mg.mg_pct(FAKE, FAKE, 64, 1)), None) == -1
