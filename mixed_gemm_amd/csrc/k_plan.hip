@@ -91,9 +91,11 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const float* __restr
             if (t < 256) hist[t] = 0;
             __syncthreads();
             // Counting.  The high bytes of channel maxima take few values (similar
-            // exponents), so one bin can receive most of the 1024 threads' adds:
-            // lanes of a wave with the same bin as a leader lane are counted with
-            // one atomic (two such rounds per key), the rest add one by one.
+            // exponents), so in the first pass one bin can receive most of the
+            // 1024 threads' adds: there, lanes of a wave with the same bin as a
+            // leader lane are counted with one atomic (two such rounds per key)
+            // and the rest add one by one; the later passes, whose bins are
+            // spread, add one by one.
 #pragma unroll
             for (int i = 0; i < CMAX; ++i) {
                 if (i < C) {                                              // uniform
@@ -101,6 +103,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const float* __restr
                     const uint32_t bin = (kv[i] >> shift) & 255u;
 #pragma unroll
                     for (int r = 0; r < 2; ++r) {
+                        if (shift != 24) break;                           // uniform
                         const uint64_t m = __builtin_amdgcn_ballot_w64(act);
                         if (m != 0) {                                     // uniform
                             const int leader = __builtin_ctzll(m);
