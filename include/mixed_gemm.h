@@ -92,7 +92,9 @@ typedef struct {
  *  Wst                 compact codes: [N/32][K/32] u8 tile codes (MG_W_32X32),
  *                      [N][ceil(K/128)] u8 stripe codes (MG_W_128X1); null
  *                      allowed for MG_W_1X32;
- *  WO  [N][k]     bf16 folded outlier columns (null allowed when k == 0).
+ *  WO  [N][kp]    bf16 folded outlier columns, kp = k rounded up to a multiple
+ *                      of 8 (rows 16-byte aligned; columns k .. kp-1 hold +0);
+ *                      null allowed when k == 0.
  *
  * Scale windows (Ws, As).  The E8M0 codes of a [rows][K/32] scale matrix are
  * stored in windows of 256 rows x 16 blocks (512 channels), 16 bytes per row,
@@ -118,8 +120,8 @@ typedef struct {
 
 /* Per-forward activation workspace (sizes from mg_act_bytes):
  *  Aq [M][K/2] u8 MXFP4 payload of the bulk quotients, As the E8M0 code of
- *  each (row, 32-block) in scale windows (see mg_plan), XO [M][k] bf16
- *  outlier quotients (null allowed when k == 0). */
+ *  each (row, 32-block) in scale windows (see mg_plan), XO [M][kp] bf16
+ *  outlier quotients, kp as for WO (pad columns +0; null allowed when k == 0). */
 typedef struct {
     uint8_t* Aq;
     uint8_t* As;
@@ -233,9 +235,7 @@ int mg_quantize_act(const mg_plan* p, const void* X, int32_t dtype, int64_t M,
  * for checking the accumulation itself).  M == 0 is a no-op.  Each operand
  * (Aq, As, Wq, Ws, XO, WO) must stay below 3 GiB (32-bit buffer offsets),
  * else MG_ERR_UNSUPPORTED; Y has no limit (it is addressed per output tile).
- * Any K (a multiple of 32) runs at full speed; fastest when k % 8 == 0, an
- * even k keeps most of the speed, an odd k is correct but several times
- * slower. */
+ * Any K (a multiple of 32) and any k run on the same fast path. */
 int mg_dual_gemm(const mg_plan* p, const mg_act* a, int64_t M, void* Y, int32_t y_dtype,
                  hipStream_t stream);
 

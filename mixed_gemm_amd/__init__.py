@@ -182,6 +182,12 @@ def mg_act_bytes(desc: mg_plan_desc, M: int) -> list[int]:
     return list(out)
 
 
+def xo_cols(k: int) -> int:
+    """Row stride of the outlier operands XO [M][kp] and WO [N][kp]: k rounded
+    up to a multiple of 8 (pad columns hold +0)."""
+    return (k + 7) // 8 * 8
+
+
 def scale_shape(rows: int, K: int) -> tuple:
     """Shape of a scale array (As, Ws) for `rows` rows in its stored order:
     [ceil(rows/256)][ceil(K/512)][256 rows][16 blocks] (the C header's scale
@@ -210,7 +216,7 @@ class Plan:
         wst = {MG_W_32X32: (N // 32, K // 32), MG_W_128X1: (N, (K + 127) // 128)}.get(desc.layout, 0)
         p = Plan(desc, e(K, torch.float32), e(K, torch.float32), e(k, torch.int32), e(K, torch.int32),
                  e((N, K // 2), torch.uint8), e(scale_shape(N, K), torch.uint8), e(wst, torch.uint8),
-                 e((N, k), torch.bfloat16))
+                 e((N, xo_cols(k)), torch.bfloat16))
         got = [t.numel() * t.element_size() for t in p.tensors().values()]
         if got != b:
             raise RuntimeError(f"plan buffer sizes {got} differ from mg_plan_bytes {b}")
@@ -255,7 +261,7 @@ class Act:
         K, k = desc.K, desc.k
         a = Act(M, torch.empty((M, K // 2), dtype=torch.uint8, device=device),
                 torch.empty(scale_shape(M, K), dtype=torch.uint8, device=device),
-                torch.empty((M, k), dtype=torch.bfloat16, device=device))
+                torch.empty((M, xo_cols(k)), dtype=torch.bfloat16, device=device))
         got = [t.numel() * t.element_size() for t in (a.Aq, a.As, a.XO)]
         if got != mg_act_bytes(desc, M):
             raise RuntimeError(f"activation buffer sizes {got} differ from mg_act_bytes")

@@ -93,9 +93,10 @@ __global__ void __launch_bounds__(256) dual_gemm_simple(const uint8_t* __restric
         }
         acc = mfma_fp4(a, b, sa, sb, acc);
     }
+    const int kp = xo_cols(k);                  // outlier row stride
     for (int kk = 0; kk < k; kk += 16) {
-        const uint4 a = load_bf16x8(XO + row * k, kk + 8 * half, k);
-        const uint4 b = load_bf16x8(WO + col * k, kk + 8 * half, k);
+        const uint4 a = load_bf16x8(XO + row * kp, kk + 8 * half, k);
+        const uint4 b = load_bf16x8(WO + col * kp, kk + 8 * half, k);
         acc = mfma_bf16(a, b, acc);
     }
 #pragma unroll
@@ -212,11 +213,7 @@ struct TileOrg {
     int n0;
 };
 
-// OA: alignment of the outlier rows (2k bytes) -- 16 when k % 8 == 0 (whole
-// 16-byte chunks, one direct-to-LDS copy each), 4 when k is even (four
-// 4-byte copies per chunk), else 2 (values gathered through registers, which
-// waits for the stage's copies in flight).
-template <typename OutT, int OA>
+template <typename OutT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 dual_gemm_tiled(GemmArgs g) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -230,7 +227,7 @@ dual_gemm_tiled(GemmArgs g) {
     const int K = g.K, k = g.k, N = g.N;
     const int64_t M = g.M;
     const uint32_t rowA = (uint32_t)(K / 2);       // bytes per Aq / Wq row
-    const uint32_t rowX = (uint32_t)(2 * k);       // bytes per XO / WO row
+    const uint32_t rowX = (uint32_t)(2 * xo_cols(k));   // bytes per XO / WO row (16-byte multiple)
     const int S4 = (K / 2 + ROWB - 1) / ROWB;      // bulk stages
     const int S16 = (2 * k + ROWB - 1) / ROWB;     // outlier stages
     const int S = S4 + S16;
@@ -266,11 +263,6 @@ dual_gemm_tiled(GemmArgs g) {
     const uint32_t c16o = c16e ^ 64u;                                          // odd groups
     const uint32_t lrA0 = (uint32_t)(wave * 64 + lrow) * rowA;                 // copy row (group 0)
     const uint32_t lrX0 = (uint32_t)(wave * 64 + lrow) * rowX;
-    // 4-byte outlier copies (OA == 4): copy i of an 8-row group moves group
-    // rows 2 i + L/32, lane L landing at byte 4 (L % 32) of its row, i.e.
-    // physical chunk (L % 32) / 4, word L % 4.
-    const uint32_t lrX4 = (uint32_t)(wave * 64 + (lane >> 5)) * rowX + 4u * (uint32_t)(lane & 3);
-    const uint32_t pc4 = (uint32_t)((lane & 31) >> 2);
     const uint32_t lds_w = (uint32_t)(wave * 64 * ROWB);
     // scale windows: lane L of wave w copies window row 64 w + L of A and of
     // B; a lane reads its fragment rows' 8 bytes at these offsets (+ 512 i)
@@ -362,21 +354,6 @@ dual_gemm_tiled(GemmArgs g) {
         const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)(bulk ? nc.st : nc.st - S4) * ROWB);
         const uint32_t r0 = __builtin_amdgcn_readfirstlane((isB ? (uint32_t)nc.o.n0 : (uint32_t)nc.o.m0) * rowb);
         const uint32_t c = (part & 1) ? c16o : c16e;
-        if constexpr (OA == 4) {
-            if (!bulk) {
-                // outlier rows 4-byte aligned: four 4-byte copies (two rows each)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t b16 = (pc4 ^ (uint32_t)(i + 4 * (part & 1))) << 4;   // logical chunk
-                    const uint32_t off = b16 + 4u * (uint32_t)(lane & 3);
-                    const bool ok4 = nc.st >= 0 && so + off < rowb;
-                    const uint32_t v4 = ok4 ? lrX4 + b16 + r0 + (uint32_t)(8 * part + 2 * i) * rowb : OOB;
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(isB ? rWO : rXO, (lds_ptr_t)(dst + 256 * i), 4, v4, so,
-                                                             0, 0);
-                }
-                return;
-            }
-        }
         const bool ok = nc.st >= 0 && so + c < rowb;      // chunks past K / k read as zero
         const uint32_t v = ok ? lr + c + r0 + (uint32_t)part * 8 * rowb : OOB;
         if (bulk)
@@ -385,48 +362,13 @@ dual_gemm_tiled(GemmArgs g) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(isB ? rWO : rXO, (lds_ptr_t)dst, 16, v, so, 0, 0);
     };
 
-    // Outlier stage u of tile o when k % 8 != 0: the rows are not 16-byte
-    // aligned, so the bf16 values are gathered one by one and each chunk is
-    // stored through registers.
-    auto gather_outlier = [&](const TileOrg& o, int u, int b) {
-        uint8_t* base = lds + b * STAGE_BYTES + lds_w;
-        const int64_t ra0 = o.m0 + wave * 64 + lrow, rb0 = (int64_t)o.n0 + wave * 64 + lrow;
-#pragma unroll
-        for (int gi = 0; gi < 8; ++gi) {
-            const int cl = (int)(((gi & 1) ? c16o : c16e) >> 4);
-            const int64_t ra = ra0 + 8 * gi, rb = rb0 + 8 * gi;
-            uint32_t wa[4], wb[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                uint32_t xa = 0, xb = 0;
-#pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const int col = u * 64 + cl * 8 + 2 * e + q;
-                    const uint32_t ea = (col < k && ra < M)
-                        ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rXO, (uint32_t)((ra * k + col) * 2), 0, 0) : 0u;
-                    const uint32_t eb = (col < k && rb < N)
-                        ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rWO, (uint32_t)((rb * k + col) * 2), 0, 0) : 0u;
-                    xa |= (ea & 0xFFFFu) << (16 * q);
-                    xb |= (eb & 0xFFFFu) << (16 * q);
-                }
-                wa[e] = xa; wb[e] = xb;
-            }
-            *reinterpret_cast<u32x4*>(base + gi * 8 * ROWB + lane * 16) = u32x4{wa[0], wa[1], wa[2], wa[3]};
-            *reinterpret_cast<u32x4*>(base + TILE_BYTES + gi * 8 * ROWB + lane * 16) = u32x4{wb[0], wb[1], wb[2], wb[3]};
-        }
-    };
-
     // All copies of stage nc at once (the very first stage), with the scale
     // window it opens.
     auto load_stage = [&](const NextCopy& nc, int b) {
-        if (OA == 2 && nc.st >= S4) {
-            gather_outlier(nc.o, nc.st - S4, b);
-        } else {
 #pragma unroll
-            for (int gi = 0; gi < 8; ++gi) {
-                copy_part(nc, b, gi, false);
-                copy_part(nc, b, gi, true);
-            }
+        for (int gi = 0; gi < 8; ++gi) {
+            copy_part(nc, b, gi, false);
+            copy_part(nc, b, gi, true);
         }
         if (nc.st >= 0 && nc.st < S4 && (nc.st & 1) == 0) load_window(nc.o, nc.st >> 1);
     };
@@ -476,7 +418,6 @@ dual_gemm_tiled(GemmArgs g) {
         const uint8_t* base = lds + b * STAGE_BYTES;
         const uint8_t* wsc = nullptr;
         if constexpr (cb) wsc = window_of(st);
-        const bool dma_next = OA != 2 || nc.st < S4;
         const bool opens_window = nc.st >= 0 && nc.st < S4 && (nc.st & 1) == 0;
         static_for<80>([&](auto QC) {
             constexpr int q = decltype(QC)::value;
@@ -503,12 +444,7 @@ dual_gemm_tiled(GemmArgs g) {
                 if constexpr (q >= 16 && q < 24) frag_read(base, 1, 1, q - 16);
                 if constexpr (q >= 32 && q < 40) frag_read(base, 2, 0, q - 32);
                 if constexpr (q >= 48 && q < 56) frag_read(base, 3, 1, q - 48);
-                if constexpr (q >= 2 && q <= 32 && q % 2 == 0) {
-                    if (dma_next) copy_part(nc, b ^ 1, (q - 2) >> 2, ((q - 2) & 2) != 0);
-                }
-                if constexpr (OA == 2 && q == 2) {
-                    if (!dma_next) gather_outlier(nc.o, nc.st - S4, b ^ 1);
-                }
+                if constexpr (q >= 2 && q <= 32 && q % 2 == 0) copy_part(nc, b ^ 1, (q - 2) >> 2, ((q - 2) & 2) != 0);
                 if constexpr (q == 36) {
                     if (opens_window) load_window(nc.o, nc.st >> 1);
                 }
@@ -673,13 +609,13 @@ dual_gemm_tiled(GemmArgs g) {
     }
 }
 
-template <typename OutT, int OA>
+template <typename OutT>
 static hipError_t launch_tiled(const GemmArgs& a, hipStream_t st) {
     static thread_local int configured_dev = -1;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return hipErrorNoDevice;
     if (configured_dev != dev) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dual_gemm_tiled<OutT, OA>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dual_gemm_tiled<OutT>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_LDS_BYTES);
         if (e != hipSuccess) return e;
         configured_dev = dev;
@@ -688,16 +624,9 @@ static hipError_t launch_tiled(const GemmArgs& a, hipStream_t st) {
     const int per = (T + NXCD - 1) / NXCD;
     const int cus_per_xcd = device_cu_count() / NXCD;
     const int wg_per_xcd = per < cus_per_xcd ? per : (cus_per_xcd > 0 ? cus_per_xcd : 1);
-    hipLaunchKernelGGL((dual_gemm_tiled<OutT, OA>), dim3((unsigned)(wg_per_xcd * NXCD)), dim3(256),
+    hipLaunchKernelGGL((dual_gemm_tiled<OutT>), dim3((unsigned)(wg_per_xcd * NXCD)), dim3(256),
                        GEMM_LDS_BYTES, st, a);
     return hipGetLastError();
-}
-
-template <typename OutT>
-static hipError_t launch_tiled_t(const GemmArgs& a, hipStream_t st) {
-    if (a.k % 8 == 0) return launch_tiled<OutT, 16>(a, st);
-    if (a.k % 2 == 0) return launch_tiled<OutT, 4>(a, st);
-    return launch_tiled<OutT, 2>(a, st);
 }
 
 }  // namespace
@@ -719,7 +648,7 @@ hipError_t launch_dual_gemm(const uint8_t* Aq, const uint8_t* As, const uint16_t
         return hipGetLastError();
     }
     GemmArgs a{Aq, As, XO, Wq, Ws, WO, Y, M, N, K, k, (int32_t)((M + TBM - 1) / TBM), (N + TBN - 1) / TBN};
-    return y_dtype == MG_BF16 ? launch_tiled_t<uint16_t>(a, st) : launch_tiled_t<float>(a, st);
+    return y_dtype == MG_BF16 ? launch_tiled<uint16_t>(a, st) : launch_tiled<float>(a, st);
 }
 
 }  // namespace mg

@@ -251,7 +251,12 @@ __global__ void __launch_bounds__(256) fold_pack_kernel(const void* __restrict__
     };
     // outlier channels of row n to WO, then masked to +0 in f; returns the
     // lane's amax of the masked values
+    // WO rows are kp = xo_cols(k) values apart; the workgroup of channels
+    // 0..511 writes each row's pad columns k .. kp-1 (+0), one per lane
+    const int kp = xo_cols(k);
+    const bool pad_lane = blockIdx.x == 0 && lane < kp - k;
     auto extract = [&](int64_t n, float (&f)[8]) {
+        if (pad_lane && n < N) WO[n * kp + k + lane] = 0;
         if (omask && n < N) {
             for (uint32_t m = omask; m; m &= m - 1) {
                 const int i = __builtin_ctz(m);
@@ -261,7 +266,7 @@ __global__ void __launch_bounds__(256) fold_pack_kernel(const void* __restrict__
                 int pi = pv[0];
 #pragma unroll
                 for (int t = 1; t < 8; ++t) pi = i == t ? pv[t] : pi;
-                WO[n * k + pi] = (uint16_t)f32_to_bf16_rne(fi);
+                WO[n * kp + pi] = (uint16_t)f32_to_bf16_rne(fi);
             }
         }
         float amax = 0.0f;

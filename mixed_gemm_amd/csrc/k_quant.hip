@@ -179,7 +179,12 @@ __global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restr
     const uint32_t offXO = omask ? 2u * (uint32_t)op0 : kNoStore;
     const bool wave_o = __builtin_amdgcn_ballot_w64(omask != 0) != 0;
     const bool wave_rest = __builtin_amdgcn_ballot_w64(omask_rest != 0) != 0;
-    const uint32_t rowX = 2u * (uint32_t)K, rowAq = (uint32_t)K / 2u, rowXO = 2u * (uint32_t)k;
+    // XO rows are kp = xo_cols(k) values apart; the workgroup of channels
+    // 0..511 writes the pad columns k .. kp-1 (+0), one per lane
+    const int kp = xo_cols(k);
+    const uint32_t rowX = 2u * (uint32_t)K, rowAq = (uint32_t)K / 2u, rowXO = 2u * (uint32_t)kp;
+    const bool pad_wg = blockIdx.x == 0 && kp > k;
+    const uint32_t offPad = lane < kp - k ? 2u * (uint32_t)(k + lane) : kNoStore;
 
     auto rsrc = [](const void* p, uint32_t bytes) {
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
@@ -242,6 +247,7 @@ __global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restr
         uint32_t c;
         const uint32_t word = encode8(q, c);
         __builtin_amdgcn_raw_buffer_store_b32(word, rsrc(pq, live ? rowAq : 0u), offAq, 0, 0);
+        if (pad_wg) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)0, rsrc(po, live ? rowXO : 0u), offPad, 0, 0);
         if ((lane & 3) == 0)
             __builtin_amdgcn_raw_buffer_store_b8((uint8_t)c, rsrc(ps, (uint32_t)kScBlocks), offAs, 0, 0);
     };
@@ -257,13 +263,13 @@ __global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restr
     const int64_t Mp = (M + kScRows - 1) / kScRows * kScRows;
     const int n = r0 < Mp ? (int)((Mp - 1 - r0) / rstride) + 1 : 0;
     const int nv = r0 < M ? (int)((M - 1 - r0) / rstride) + 1 : 0;
-    const int64_t dX = rstride * K, dQ = rstride * (K / 2), dO = rstride * k;
+    const int64_t dX = rstride * K, dQ = rstride * (K / 2), dO = rstride * kp;
     const int64_t win_stride = sc_nwin(K) * kScWinBytes;     // bytes between 256-row groups of As
     static_assert(kScRows == 256, "row group = m >> 8");
     const uint16_t* px = X + r0 * K;
     uint8_t* pq = Aq + r0 * (K / 2);
     uint8_t* const asw = As + (int64_t)blockIdx.x * kScWinBytes;
-    uint16_t* po = XO + r0 * k;
+    uint16_t* po = XO + r0 * kp;
     int64_t m = r0;
     u32x4 a = load_row(px, nv > 0);
     px += dX;
@@ -311,6 +317,7 @@ __global__ void __launch_bounds__(256) quant_f32_kernel(const float* __restrict_
     const int64_t rstride = (int64_t)gridDim.y * kWaves;
     const int64_t Mp = (M + kScRows - 1) / kScRows * kScRows;   // through the last scale group's pad rows
     const int64_t nwin = sc_nwin(K);
+    const int kp = xo_cols(k);                                   // XO row stride; pads written below
     for (int64_t r = (int64_t)blockIdx.y * kWaves + wave; r < Mp; r += rstride) {
         const bool live = r < M;
         float q[8];
@@ -320,10 +327,11 @@ __global__ void __launch_bounds__(256) quant_f32_kernel(const float* __restrict_
             mx[i] = fmaxf(mx[i], __builtin_fabsf(x));
             q[i] = __fdiv_rn(x, sv[i]);
             if (pv[i] >= 0) {
-                if (live) XO[r * k + pv[i]] = (uint16_t)f32_to_bf16_rne(q[i]);
+                if (live) XO[r * kp + pv[i]] = (uint16_t)f32_to_bf16_rne(q[i]);
                 q[i] = 0.0f;
             }
         }
+        if (live && blockIdx.x == 0 && lane < kp - k) XO[r * kp + k + lane] = 0;
         encode_store(q, lane, valid && live, Aq + r * (K / 2),
                      As + sc_offset(r, (int32_t)blockIdx.x * kScBlocks, nwin), j0);
     }

@@ -75,7 +75,7 @@ int check_plan(const mg_plan* p, bool need_w) {
 // The GEMM addresses each operand with 32-bit offsets below 3 GiB.
 int check_gemm_size(const mg_plan* p, int64_t M) {
     const uint64_t lim = 0xC0000000ull;
-    const uint64_t K = (uint64_t)p->d.K, N = (uint64_t)p->d.N, k = (uint64_t)p->d.k;
+    const uint64_t K = (uint64_t)p->d.K, N = (uint64_t)p->d.N, k = (uint64_t)mg::xo_cols(p->d.k);
     if ((uint64_t)M * K / 2 >= lim || N * K / 2 >= lim || (uint64_t)M * 2 * k >= lim || N * 2 * k >= lim ||
         (uint64_t)mg::sc_bytes(M, p->d.K) >= lim || (uint64_t)mg::sc_bytes(p->d.N, p->d.K) >= lim)
         return fail(MG_ERR_UNSUPPORTED, "operands of M=%lld, N=%d, K=%d, k=%d exceed 3 GiB", (long long)M, p->d.N,
@@ -114,7 +114,7 @@ int device_cu_count() {
 
 extern "C" {
 
-int mg_version(void) { return 200; }   // 0.2.0: scales stored in windows
+int mg_version(void) { return 300; }   // 0.3.0: scales in windows, outlier rows padded to 8
 
 const char* mg_last_error(void) { return g_err; }
 
@@ -130,7 +130,7 @@ int mg_plan_bytes(const mg_plan_desc* d, size_t out[8]) {
     out[5] = (size_t)mg::sc_bytes((int64_t)N, d->K);       // Ws, in 256-row x 16-block windows
     out[6] = d->layout == MG_W_32X32 ? (N / 32) * (K / 32)       // Wst
            : d->layout == MG_W_128X1 ? N * ((K + 127) / 128) : 0;
-    out[7] = 2 * N * k;                                    // WO
+    out[7] = 2 * N * (size_t)mg::xo_cols(d->k);            // WO [N][kp], kp = k rounded up to 8
     return MG_OK;
 }
 
@@ -141,7 +141,7 @@ int mg_act_bytes(const mg_plan_desc* d, int64_t M, size_t out[3]) {
     const size_t K = (size_t)d->K, k = (size_t)d->k, m = (size_t)M;
     out[0] = m * K / 2;
     out[1] = (size_t)mg::sc_bytes(M, d->K);                // As, in 256-row x 16-block windows
-    out[2] = 2 * m * k;
+    out[2] = 2 * m * (size_t)mg::xo_cols(d->k);            // XO [M][kp]
     return MG_OK;
 }
 

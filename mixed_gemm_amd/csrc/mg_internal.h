@@ -24,6 +24,10 @@ __host__ __device__ constexpr int64_t sc_nwin(int32_t K) { return ((int64_t)K + 
 __host__ __device__ constexpr int64_t sc_bytes(int64_t rows, int32_t K) {
     return (rows + kScRows - 1) / kScRows * sc_nwin(K) * kScWinBytes;
 }
+// Row stride (in bf16 values) of the outlier operands XO [M][kp] and WO
+// [N][kp]: k rounded up to a multiple of 8, so every row starts 16-byte
+// aligned; the pad columns k .. kp-1 hold +0.
+__host__ __device__ constexpr int32_t xo_cols(int32_t k) { return (k + 7) & ~7; }
 __host__ __device__ constexpr int64_t sc_offset(int64_t row, int32_t blk, int64_t nwin) {
     return ((row / kScRows) * nwin + blk / kScBlocks) * kScWinBytes + (row % kScRows) * kScBlocks + blk % kScBlocks;
 }

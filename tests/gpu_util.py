@@ -41,6 +41,15 @@ def scale_rows(x, rows: int, K: int) -> np.ndarray:
     return np.ascontiguousarray(full[:rows, :nb])
 
 
+def outlier_cols(x, k: int) -> np.ndarray:
+    """The k outlier columns of XO [M][kp] or WO [N][kp] (kp = k rounded up to
+    a multiple of 8), asserting that the pad columns hold +0."""
+    a = host(x) if isinstance(x, torch.Tensor) else np.asarray(x)
+    assert a.ndim == 2 and a.shape[1] == (k + 7) // 8 * 8, (a.shape, k)
+    assert not np.asarray(a[:, k:]).view(np.uint16).any(), "outlier pad columns must hold +0"
+    return np.ascontiguousarray(a[:, :k])
+
+
 def run_pipeline(X: np.ndarray, W: np.ndarray, alpha: float, k: int, layout: str = "1x32",
                  smooth: bool = True, calib_batches: int = 1, score: str = "max") -> dict:
     """calibrate (optionally in several batches) -> weight ranges -> plan -> quantize -> GEMM,
@@ -68,7 +77,8 @@ def run_pipeline(X: np.ndarray, W: np.ndarray, alpha: float, k: int, layout: str
     out = dict(act_max=host(act_max), w_max=host(w_max), Y=host(Y), Y32=host(Y32))
     out.update({n: host(t) for n, t in p.tensors().items()})
     out["Ws"] = scale_rows(p.Ws, N, K)
-    out.update(Aq=host(a.Aq), As=scale_rows(a.As, M, K), XO=host(a.XO))
+    out["WO"] = outlier_cols(p.WO, k)
+    out.update(Aq=host(a.Aq), As=scale_rows(a.As, M, K), XO=outlier_cols(a.XO, k))
     return out
 
 

@@ -26,7 +26,7 @@ import torch
 import mixed_gemm_amd as mg
 import synth
 from oracle import layer
-from tests.gpu_util import assert_faithful_bf16, bf16_to_f64, check_output, dev, host, scale_rows
+from tests.gpu_util import assert_faithful_bf16, bf16_to_f64, check_output, dev, host, outlier_cols, scale_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -94,6 +94,7 @@ def test_block_stagewise(block, layout):
     for tag, p, op in (("ffn.0", blk.plan0, o_p0), ("ffn.2", blk.plan2, o_p2)):
         g = {n: host(t) for n, t in p.tensors().items()}
         g["Ws"] = scale_rows(p.Ws, p.desc.N, p.desc.K)
+        g["WO"] = outlier_cols(p.WO, p.desc.k)
         for name in ("s", "rcp", "O", "pos", "Wq", "Ws", "WO") + (("Wst",) if layout != "1x32" else ()):
             _bits_equal(g[name], op[name], f"{tag} {name}")
 
@@ -109,7 +110,7 @@ def test_block_stagewise(block, layout):
     ridx = torch.from_numpy(rows).cuda()
     Y0_32 = torch.empty((M, w0.N), dtype=torch.float32, device="cuda")
     mg.mg_dual_gemm(blk.plan0, a0, Y0_32)
-    g0 = dict(Aq=host(a0.Aq[ridx]), As=scale_rows(a0.As, M, w0.K)[rows], XO=host(a0.XO[ridx]), Y=host(Y0[ridx]),
+    g0 = dict(Aq=host(a0.Aq[ridx]), As=scale_rows(a0.As, M, w0.K)[rows], XO=outlier_cols(host(a0.XO[ridx]), w0.k), Y=host(Y0[ridx]),
               Y32=host(Y0_32[ridx]))
     del a0, Y0_32
     h = torch.empty_like(Y0)
@@ -127,7 +128,7 @@ def test_block_stagewise(block, layout):
     mg.mg_dual_gemm(blk.plan2, a2, Y2_32)
     torch.cuda.synchronize()
     hr = host(h[ridx])
-    g2 = dict(Aq=host(a2.Aq[ridx]), As=scale_rows(a2.As, M, w2.K)[rows], XO=host(a2.XO[ridx]), Y=host(Y2[ridx]),
+    g2 = dict(Aq=host(a2.Aq[ridx]), As=scale_rows(a2.As, M, w2.K)[rows], XO=outlier_cols(host(a2.XO[ridx]), w2.k), Y=host(Y2[ridx]),
               Y32=host(Y2_32[ridx]))
     del a2, Y2, Y2_32, h, X5d
     torch.cuda.empty_cache()

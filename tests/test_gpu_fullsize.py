@@ -17,7 +17,7 @@ import torch
 import mixed_gemm_amd as mg
 import synth
 from oracle import layer
-from tests.gpu_util import check_output, dev, host, scale_rows
+from tests.gpu_util import check_output, dev, host, outlier_cols, scale_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -66,9 +66,10 @@ def _run_full(w: synth.Workload, layout="1x32", score="max"):
     mg.mg_dual_gemm(p, a, Y32)
     torch.cuda.synchronize()
     g = dict(act_max=host(act_max), w_max=host(w_max), Y=host(Y[ridx]), Y32=host(Y32[ridx]),
-             Aq=host(a.Aq[ridx]), As=scale_rows(a.As, M, K)[rows], XO=host(a.XO[ridx]))
+             Aq=host(a.Aq[ridx]), As=scale_rows(a.As, M, K)[rows], XO=outlier_cols(host(a.XO[ridx]), w.k))
     g.update({n: host(t) for n, t in p.tensors().items()})
     g["Ws"] = scale_rows(p.Ws, N, K)
+    g["WO"] = outlier_cols(p.WO, w.k)
     del Y, Y32, a, Xd, Wd
     torch.cuda.empty_cache()
 

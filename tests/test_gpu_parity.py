@@ -16,7 +16,7 @@ import torch
 import mixed_gemm_amd as mg
 import synth
 from oracle import layer
-from tests.gpu_util import assert_faithful_bf16, bf16_to_f64, check_output, dev, host, run_pipeline, scale_rows
+from tests.gpu_util import assert_faithful_bf16, bf16_to_f64, check_output, dev, host, outlier_cols, run_pipeline, scale_rows
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
@@ -109,10 +109,12 @@ def test_smoothed_score(layout):
 @pytest.mark.parametrize("layout", ["1x32", "32x32", "128x1"])
 @pytest.mark.parametrize("M,K,N,k,bf16", [(300, 352, 96, 6, True), (600, 800, 288, 12, False)])
 def test_scale_pads_written_over_garbage(M, K, N, k, bf16, layout):
-    """Ragged M, N and K (not multiples of 256, 256 and 512): over scale
-    buffers pre-filled with 0xFF (the E8M0 NaN code), the writers fill every
-    pad row and pad block of the scale windows with code 0 (checked by
-    scale_rows), the codes equal the oracle's, and the output is exact."""
+    """Ragged M, N and K (not multiples of 256, 256 and 512) and k not a
+    multiple of 8: over scale buffers pre-filled with 0xFF (the E8M0 NaN code)
+    and outlier buffers pre-filled with bf16 NaNs, the writers fill every pad
+    row and pad block of the scale windows with code 0 and every pad column of
+    XO / WO with +0 (checked by scale_rows and outlier_cols), the codes equal
+    the oracle's, and the output is exact."""
     X, W = _heavy(M, K, N, 70 + K, bf16=bf16)
     Xd, Wd = dev(X), dev(W)
     act_max = mg.calibrate([Xd], K)
@@ -121,9 +123,11 @@ def test_scale_pads_written_over_garbage(M, K, N, k, bf16, layout):
     desc = mg.make_desc(K, N, k, 0.6, layout)
     p = mg.Plan.empty(desc)
     p.Ws.fill_(0xFF)
+    p.WO.view(torch.int16).fill_(-1)
     mg.mg_plan_build(p, act_max, w_max, Wd)
     a = mg.Act.empty(desc, M)
     a.As.fill_(0xFF)
+    a.XO.view(torch.int16).fill_(-1)
     mg.mg_quantize_act(p, Xd, a)
     Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     Y32 = torch.empty((M, N), dtype=torch.float32, device="cuda")
@@ -134,6 +138,7 @@ def test_scale_pads_written_over_garbage(M, K, N, k, bf16, layout):
     assert np.array_equal(scale_rows(p.Ws, N, K), o["Ws"])
     assert np.array_equal(scale_rows(a.As, M, K), o["As"])
     assert np.array_equal(host(a.Aq), o["Aq"]) and np.array_equal(host(p.Wq), o["Wq"])
+    assert np.array_equal(outlier_cols(a.XO, k), o["XO"]) and np.array_equal(outlier_cols(p.WO, k), o["WO"])
     check_output(host(Y), host(Y32), o["Y64"])
 
 
@@ -246,7 +251,7 @@ def test_gelu_quantize_fused(M, K, k):
     for n in ("Aq", "As", "XO"):
         assert torch.equal(getattr(a1, n).view(torch.uint8), getattr(a2, n).view(torch.uint8)), n
     oq = layer.quantize_act(host(h), host(p.s), host(p.O))
-    got = dict(Aq=host(a2.Aq), As=scale_rows(a2.As, M, K), XO=host(a2.XO))
+    got = dict(Aq=host(a2.Aq), As=scale_rows(a2.As, M, K), XO=outlier_cols(a2.XO, k))
     for n in ("Aq", "As", "XO"):
         assert np.array_equal(np.asarray(got[n]).view(np.uint8), np.asarray(oq[n]).view(np.uint8)), n
 
