@@ -161,6 +161,50 @@ def _dtype(t: torch.Tensor) -> int:
     raise ValueError(f"unsupported dtype {t.dtype}")
 
 
+# The C ABI receives bare pointers and cannot know buffer sizes, so the binding
+# checks every shape against the plan descriptor before anything is launched
+# (a mismatched buffer would make a kernel read or write past its allocation).
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _is_bf16(t: torch.Tensor) -> bool:
+    return t.dtype in (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _matrix(X: torch.Tensor, name: str, cols: int | None = None) -> tuple[int, int]:
+    _need(X.dim() == 2, f"{name} must be 2-D, got shape {tuple(X.shape)}")
+    if cols is not None:
+        _need(X.shape[1] == cols, f"{name} must have {cols} columns, got shape {tuple(X.shape)}")
+    return int(X.shape[0]), int(X.shape[1])
+
+
+def _vec(t: torch.Tensor, n: int, name: str) -> None:
+    _need(t is not None and t.numel() == n and t.dtype == torch.float32,
+          f"{name} must be a float32 tensor of {n} elements")
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def _check_act(desc, act: "Act", M: int | None = None) -> None:
+    _need(isinstance(act, Act), "act must be an Act")
+    if M is not None:
+        _need(act.M == M, f"act holds {act.M} rows, the input has {M}")
+    want = mg_act_bytes(desc, act.M)
+    got = [_nbytes(act.Aq), _nbytes(act.As), _nbytes(act.XO)]
+    _need(got == want, f"act buffers {got} bytes do not match the plan's sizes {want} for M={act.M}")
+    _need(tuple(act.Aq.shape) == (act.M, desc.K // 2), f"act.Aq must be [{act.M}][{desc.K // 2}]")
+
+
+def _check_y(desc, Y: torch.Tensor, M: int) -> None:
+    _need(Y.dim() == 2 and tuple(Y.shape) == (M, desc.N), f"Y must be [{M}][{desc.N}], got {tuple(Y.shape)}")
+    _need(Y.dtype == torch.float32 or _is_bf16(Y), f"Y must be bf16 or float32, got {Y.dtype}")
+
+
 # ----------------------------------------------------------------------------- plan / workspace
 
 def make_desc(K: int, N: int, k: int, alpha: float = 0.5, layout: str | int = "1x32",
@@ -208,18 +252,20 @@ class Plan:
     Wst: torch.Tensor
     WO: torch.Tensor
 
+    def __post_init__(self):
+        got = [_nbytes(t) for t in self.tensors().values()]
+        want = mg_plan_bytes(self.desc)
+        _need(got == want, f"plan buffer sizes {got} differ from mg_plan_bytes {want}")
+        _need(tuple(self.Wq.shape) == (self.desc.N, self.desc.K // 2), "plan.Wq must be [N][K/2]")
+
     @staticmethod
     def empty(desc: mg_plan_desc, device="cuda") -> "Plan":
-        b = mg_plan_bytes(desc)
         K, N, k = desc.K, desc.N, desc.k
         e = lambda n, dt: torch.empty(n, dtype=dt, device=device)
         wst = {MG_W_32X32: (N // 32, K // 32), MG_W_128X1: (N, (K + 127) // 128)}.get(desc.layout, 0)
         p = Plan(desc, e(K, torch.float32), e(K, torch.float32), e(k, torch.int32), e(K, torch.int32),
                  e((N, K // 2), torch.uint8), e(scale_shape(N, K), torch.uint8), e(wst, torch.uint8),
                  e((N, xo_cols(k)), torch.bfloat16))
-        got = [t.numel() * t.element_size() for t in p.tensors().values()]
-        if got != b:
-            raise RuntimeError(f"plan buffer sizes {got} differ from mg_plan_bytes {b}")
         return p
 
     def c(self) -> mg_plan:
@@ -241,11 +287,7 @@ class Plan:
         """A plan from state() (e.g. after torch.load(..., weights_only=True)),
         its buffers checked against mg_plan_bytes."""
         desc = mg_plan_desc(**state["desc"])
-        p = Plan(desc, **{n: t.to(device) for n, t in state["tensors"].items()})
-        got = [t.numel() * t.element_size() for t in p.tensors().values()]
-        if got != mg_plan_bytes(desc):
-            raise ValueError(f"plan buffer sizes {got} differ from mg_plan_bytes")
-        return p
+        return Plan(desc, **{n: t.to(device) for n, t in state["tensors"].items()})
 
 
 @dataclass
@@ -262,9 +304,7 @@ class Act:
         a = Act(M, torch.empty((M, K // 2), dtype=torch.uint8, device=device),
                 torch.empty(scale_shape(M, K), dtype=torch.uint8, device=device),
                 torch.empty((M, xo_cols(k)), dtype=torch.bfloat16, device=device))
-        got = [t.numel() * t.element_size() for t in (a.Aq, a.As, a.XO)]
-        if got != mg_act_bytes(desc, M):
-            raise RuntimeError(f"activation buffer sizes {got} differ from mg_act_bytes")
+        _check_act(desc, a)
         return a
 
     def c(self) -> mg_act:
@@ -278,70 +318,95 @@ def mg_version() -> int:
 
 
 def mg_calib_reset(act_max: torch.Tensor, stream=None) -> None:
+    _need(act_max.dtype == torch.float32, "act_max must be float32")
     _check(lib().mg_calib_reset(_ptr(act_max), act_max.numel(), _stream(stream)))
 
 
 def mg_calib_act(X: torch.Tensor, act_max: torch.Tensor, stream=None) -> None:
-    M, K = X.shape
+    M, K = _matrix(X, "X")
+    _vec(act_max, K, "act_max")
     _check(lib().mg_calib_act(_ptr(X), _dtype(X), M, K, _ptr(act_max), _stream(stream)))
 
 
 def mg_weight_range(W: torch.Tensor, w_max: torch.Tensor, stream=None) -> None:
-    N, K = W.shape
+    N, K = _matrix(W, "W")
+    _vec(w_max, K, "w_max")
     _check(lib().mg_weight_range(_ptr(W), _dtype(W), N, K, _ptr(w_max), _stream(stream)))
 
 
 def mg_smooth_scales(plan: Plan, act_max, w_max, stream=None) -> None:
+    if plan.desc.smooth:
+        _vec(act_max, plan.desc.K, "act_max")
+        _vec(w_max, plan.desc.K, "w_max")
     p = plan.c()
     _check(lib().mg_smooth_scales(ctypes.byref(p), _ptr(act_max), _ptr(w_max), _stream(stream)))
 
 
 def mg_outlier_set(plan: Plan, act_max, stream=None) -> None:
+    _vec(act_max, plan.desc.K, "score")
     p = plan.c()
     _check(lib().mg_outlier_set(ctypes.byref(p), _ptr(act_max), _stream(stream)))
 
 
 def mg_fold_pack(plan: Plan, W: torch.Tensor, stream=None) -> None:
+    _need(tuple(W.shape) == (plan.desc.N, plan.desc.K), f"W must be [{plan.desc.N}][{plan.desc.K}]")
     p = plan.c()
     _check(lib().mg_fold_pack(ctypes.byref(p), _ptr(W), _dtype(W), _stream(stream)))
 
 
 def mg_plan_build(plan: Plan, act_max, w_max, W: torch.Tensor, stream=None) -> None:
+    _vec(act_max, plan.desc.K, "act_max")
+    if plan.desc.smooth:
+        _vec(w_max, plan.desc.K, "w_max")
+    _need(tuple(W.shape) == (plan.desc.N, plan.desc.K), f"W must be [{plan.desc.N}][{plan.desc.K}]")
     p = plan.c()
     _check(lib().mg_plan_build(ctypes.byref(p), _ptr(act_max), _ptr(w_max), _ptr(W), _dtype(W),
                                _stream(stream)))
 
 
 def mg_quantize_act(plan: Plan, X: torch.Tensor, act: Act, stream=None) -> None:
+    M, _ = _matrix(X, "X", plan.desc.K)
+    _check_act(plan.desc, act, M)
     p, a = plan.c(), act.c()
     _check(lib().mg_quantize_act(ctypes.byref(p), _ptr(X), _dtype(X), X.shape[0], ctypes.byref(a),
                                  _stream(stream)))
 
 
 def mg_dual_gemm(plan: Plan, act: Act, Y: torch.Tensor, stream=None) -> None:
+    _check_act(plan.desc, act)
+    _check_y(plan.desc, Y, act.M)
     p, a = plan.c(), act.c()
     _check(lib().mg_dual_gemm(ctypes.byref(p), ctypes.byref(a), act.M, _ptr(Y), _dtype(Y), _stream(stream)))
 
 
 def mg_forward(plan: Plan, X: torch.Tensor, act: Act, Y: torch.Tensor, stream=None) -> None:
+    M, _ = _matrix(X, "X", plan.desc.K)
+    _check_act(plan.desc, act, M)
+    _check_y(plan.desc, Y, M)
     p, a = plan.c(), act.c()
     _check(lib().mg_forward(ctypes.byref(p), _ptr(X), _dtype(X), X.shape[0], ctypes.byref(a), _ptr(Y),
                             _dtype(Y), _stream(stream)))
 
 
 def mg_gelu_tanh_bf16(inp: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    _need(_is_bf16(inp) and _is_bf16(out), "bf16 input and output expected")
+    _need(out.numel() == inp.numel(), f"out holds {out.numel()} values, in {inp.numel()}")
     _check(lib().mg_gelu_tanh_bf16(_ptr(inp), _ptr(out), inp.numel(), _stream(stream)))
 
 
 def mg_quantize_act_stats(plan: Plan, X: torch.Tensor, act: Act, act_max: torch.Tensor, stream=None) -> None:
+    M, _ = _matrix(X, "X", plan.desc.K)
+    _check_act(plan.desc, act, M)
+    _vec(act_max, plan.desc.K, "act_max")
     p, a = plan.c(), act.c()
     _check(lib().mg_quantize_act_stats(ctypes.byref(p), _ptr(X), _dtype(X), X.shape[0], ctypes.byref(a),
                                        _ptr(act_max), _stream(stream)))
 
 
 def mg_gelu_quantize_act(plan: Plan, Y: torch.Tensor, act: Act, stream=None) -> None:
-    if Y.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
-        raise ValueError("bf16 input expected")
+    _need(_is_bf16(Y), "bf16 input expected")
+    M, _ = _matrix(Y, "Y", plan.desc.K)
+    _check_act(plan.desc, act, M)
     p, a = plan.c(), act.c()
     _check(lib().mg_gelu_quantize_act(ctypes.byref(p), _ptr(Y), Y.shape[0], ctypes.byref(a), _stream(stream)))
 
@@ -374,6 +439,8 @@ def mg_pct_count(st: PctState, pass_: int, X: torch.Tensor, stream=None) -> None
 
 
 def mg_pct_select(st: PctState, pass_: int, q: float, score: torch.Tensor | None = None, stream=None) -> None:
+    if score is not None:
+        _vec(score, st.K, "score")
     c = st.c()
     _check(lib().mg_pct_select(ctypes.byref(c), pass_, float(q), _ptr(score), _stream(stream)))
 

@@ -64,24 +64,7 @@ def build(verbose: bool = False) -> str:
     demo = build_c_demo()
     if verbose:
         print(f"built {demo}")
-    probe = build_mfma_ceiling()
-    if verbose:
-        print(f"built {probe}")
     return LIB
-
-
-def build_mfma_ceiling() -> str:
-    """tests/perf/mfma_ceiling: a stand-alone HIP program measuring the FP4
-    matrix cores with register operands only (the dual GEMM's practical
-    ceiling on this part); not linked to the library."""
-    src = os.path.join(ROOT, "tests", "perf", "mfma_ceiling.hip")
-    exe = os.path.join(ROOT, "tests", "perf", "mfma_ceiling")
-    flags = [f for f in FLAGS if f != "-fPIC"]
-    r = subprocess.run([hipcc(), *flags, src, "-o", exe + ".tmp"], capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"mfma_ceiling build failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(exe + ".tmp", exe)
-    return exe
 
 
 def build_c_demo() -> str:

@@ -28,35 +28,12 @@ __device__ __forceinline__ uint32_t e8m0_from_amax_bits(uint32_t amax_bits) {
     return (uint32_t)(e > 2 ? e - 2 : 0);
 }
 
-// E2M1 magnitude code of r >= 0 (already divided by the block scale):
-// nearest of {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the even code, saturating.
-// Each midpoint is counted when r passes it; at the midpoints whose upper
-// neighbour has an even code (0.75, 1.75, 3.5) equality also counts.
-__device__ __forceinline__ uint32_t e2m1_code(float r) {
-    uint32_t m = 0;
-    m += r > 0.25f;
-    m += r >= 0.75f;
-    m += r > 1.25f;
-    m += r >= 1.75f;
-    m += r > 2.5f;
-    m += r >= 3.5f;
-    m += r > 5.0f;
-    return m;
-}
-
-// Nibble (sign << 3 | code) of v under block scale code c.  ldexp is exact
-// (power-of-two scaling into the normal range).
-__device__ __forceinline__ uint32_t e2m1_nibble(float v, uint32_t c) {
-    float r = __builtin_ldexpf(__builtin_fabsf(v), 127 - (int)c);
-    return ((__float_as_uint(v) >> 28) & 8u) | e2m1_code(r);
-}
-
 // IEEE f32 quotient x / s from rcp = RN(1/s) with Markstein's FMA-based
 // correction (P. Markstein, IBM J. Res. Dev. 1990; Muller et al., Handbook of
 // Floating-Point Arithmetic, division with a fused multiply-add): q0 = x*rcp,
 // t = q0*s - x (exact), q = q0 - t*rcp.  The result is the correctly rounded
 // quotient when the remainder cannot underflow and the quotient is normal;
-// callers check the operand ranges (div_fast_ok_*) and otherwise divide with
+// callers check the operand ranges (div_fast_ok_s, and x on its bits) and otherwise divide with
 // __fdiv_rn.  The remainder is formed as q0*s - x and subtracted, so a zero x
 // keeps its sign (-0 / s = -0) without a separate sign fix-up.
 __device__ __forceinline__ float div_fast(float x, float s, float rcp) {
@@ -65,13 +42,9 @@ __device__ __forceinline__ float div_fast(float x, float s, float rcp) {
     return __builtin_fmaf(-t, rcp, q0);
 }
 
-// Range where div_fast is exact: x == 0 or 2^-100 <= |x| <= 2^100, given a
-// divisor with 2^-20 <= s <= 2^20 (so the quotient stays far from underflow
-// and overflow and the exact remainder is representable).
-__device__ __forceinline__ bool div_fast_ok_x(float x) {
-    const float ax = __builtin_fabsf(x);
-    return ax == 0.0f || (ax >= 0x1p-100f && ax <= 0x1p100f);
-}
+// Divisor range in which div_fast is exact for x == 0 or 2^-100 <= |x| <= 2^100
+// (the quotient stays far from underflow and overflow and the exact
+// remainder is representable); the callers check x on its raw bits.
 __device__ __forceinline__ bool div_fast_ok_s(float s) { return s >= 0x1p-20f && s <= 0x1p20f; }
 
 // GELU (tanh form) in f32 of one value: 0.5 y (1 + tanh u) with
@@ -108,8 +81,9 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t c) {
 // Hardware E2M1 encode of two f32 values divided by an f32 power-of-two scale
 // (v_cvt_scalef32_pk_fp4_f32: nearest, ties to even, saturating, sign kept),
 // written into byte `sel` of `word` (first value in the low nibble); the
-// other bytes of `word` are kept.  Checked against the threshold encoder
-// e2m1_nibble over every f32 bit pattern at scales 2^-127 .. 2^127.
+// other bytes of `word` are kept.  The quantizer's codes are checked bit for
+// bit against the oracle's threshold encoder on every finite bf16 value under
+// scale-setting blocks, at s = 1 and at the workloads' smoothing scales.
 #define MG_CVT_FP4X2(word, a, b, scale, sel) \
     (word) = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((word), (a), (b), (scale), (sel))
 

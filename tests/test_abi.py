@@ -215,3 +215,54 @@ def test_plan_state_round_trip(tmp_path):
         bad["tensors"]["Ws"] = bad["tensors"]["Ws"].reshape(-1)[:16]
         with pytest.raises(ValueError):
             mg.Plan.from_state(bad, device="cpu")
+
+
+def test_binding_checks_shapes_before_any_launch():
+    """Every binding entry point compares its tensors with the plan descriptor
+    before taking a pointer: a mismatched X, Y, W, act or statistic raises
+    ValueError (host tensors here, so no GPU call could be reached)."""
+    import torch
+    d = mg.make_desc(64, 96, 4, 0.5)
+    p = mg.Plan.empty(d, device="cpu")
+    a = mg.Act.empty(d, 8, device="cpu")
+    X = torch.zeros((8, 64), dtype=torch.bfloat16)
+    Y = torch.zeros((8, 96), dtype=torch.bfloat16)
+    W = torch.zeros((96, 64), dtype=torch.bfloat16)
+    v64, v32 = torch.zeros(64), torch.zeros(32)
+    cases = [
+        lambda: mg.mg_quantize_act(p, torch.zeros((8, 32), dtype=torch.bfloat16), a),      # K mismatch
+        lambda: mg.mg_quantize_act(p, torch.zeros((9, 64), dtype=torch.bfloat16), a),      # act.M != M
+        lambda: mg.mg_quantize_act(p, torch.zeros(64, dtype=torch.bfloat16), a),           # not 2-D
+        lambda: mg.mg_quantize_act(p, X, mg.Act.empty(mg.make_desc(64, 96, 12, 0.5), 8, device="cpu")),
+        lambda: mg.mg_quantize_act_stats(p, X, a, v32),                                     # stats of K
+        lambda: mg.mg_dual_gemm(p, a, torch.zeros((8, 64), dtype=torch.bfloat16)),         # Y not [M][N]
+        lambda: mg.mg_dual_gemm(p, a, torch.zeros((8, 96), dtype=torch.float64)),          # Y dtype
+        lambda: mg.mg_dual_gemm(p, mg.Act.empty(mg.make_desc(128, 96, 4, 0.5), 8, device="cpu"), Y),
+        lambda: mg.mg_forward(p, X, a, torch.zeros((7, 96), dtype=torch.bfloat16)),
+        lambda: mg.mg_forward(p, torch.zeros((8, 64), dtype=torch.bfloat16), mg.Act.empty(d, 4, device="cpu"), Y),
+        lambda: mg.mg_gelu_quantize_act(p, torch.zeros((8, 96), dtype=torch.bfloat16), a),
+        lambda: mg.mg_gelu_quantize_act(p, torch.zeros((8, 64), dtype=torch.float32), a),
+        lambda: mg.mg_fold_pack(p, torch.zeros((64, 96), dtype=torch.bfloat16)),           # W transposed
+        lambda: mg.mg_plan_build(p, v64, v64, torch.zeros((96, 32), dtype=torch.bfloat16)),
+        lambda: mg.mg_plan_build(p, v32, v64, W),
+        lambda: mg.mg_smooth_scales(p, v64, v32),
+        lambda: mg.mg_outlier_set(p, v32),
+        lambda: mg.mg_calib_act(X, v32),
+        lambda: mg.mg_calib_act(X, torch.zeros(64, dtype=torch.float64)),
+        lambda: mg.mg_weight_range(W, v32),
+        lambda: mg.mg_gelu_tanh_bf16(Y, torch.zeros((8, 95), dtype=torch.bfloat16)),
+        lambda: mg.mg_gelu_tanh_bf16(Y, torch.zeros((8, 96), dtype=torch.float32)),
+        lambda: mg.Plan(d, *[t for t in list(p.tensors().values())[:-1]], torch.zeros((96, 4), dtype=torch.bfloat16)),
+        lambda: mg.mg_pct_select(mg.PctState(64, device="cpu"), 1, 0.5, v32),
+    ]
+    for i, f in enumerate(cases):
+        with pytest.raises(ValueError):
+            f()
+            pytest.fail(f"case {i} was not rejected")
+    # the well-formed calls get past the shape checks and stop only at the
+    # host-tensor check of the pointer marshalling
+    for f in (lambda: mg.mg_quantize_act(p, X, a), lambda: mg.mg_dual_gemm(p, a, Y),
+              lambda: mg.mg_forward(p, X, a, Y), lambda: mg.mg_plan_build(p, v64, v64, W),
+              lambda: mg.mg_calib_act(X, v64)):
+        with pytest.raises(ValueError, match="device tensor"):
+            f()

@@ -2,13 +2,17 @@
 benchmark times).
 
 Per-channel statistics, s, rcp, O, pos and the packed weights (Wq, Ws, Wst,
-WO) are compared in full, bit-exactly.  Activation codes (Aq, As, XO) are
-compared bit-exactly on sampled rows, and the output on sampled rows: the
-GEMM's fp32 result within max|Y32 - Y64| / max|Y64| <= 2e-3 of the float64
-oracle, the bf16 output exactly its round-to-nearest-even.  The sampled rows
-always include the first row and the rows of the last (ragged) row tile.
+WO) are compared in full, bit-exactly, and so are the activation codes (Aq,
+As, XO) of every row (the oracle quantizes the rows in chunks on a thread
+pool; the weight-layout variants, whose activation path is the same, compare
+sampled rows).  The output is compared on sampled rows: the GEMM's fp32 result
+within max|Y32 - Y64| / max|Y64| <= 2e-3 of the float64 oracle, the bf16
+output exactly its round-to-nearest-even.  The sampled rows always include the
+first row and the rows of the last (ragged) row tile.
 """
+import concurrent.futures as cf
 import dataclasses
+import os
 
 import numpy as np
 import pytest
@@ -22,6 +26,8 @@ from tests.gpu_util import check_output, dev, host, outlier_cols, scale_rows
 pytestmark = pytest.mark.gpu
 
 SAMPLE = 48
+CHUNK = 2048
+THREADS = min(8, len(os.sched_getaffinity(0)))
 
 
 def _rows(M, seed):
@@ -43,8 +49,22 @@ def _bits_equal(a, b, name):
         raise AssertionError(f"{name} differs at {bad[:5].tolist()} ({len(bad)} places)")
 
 
-def _run_full(w: synth.Workload, layout="1x32", score="max"):
-    print(f"\n[full-size] {w.name} layout={layout} score={score} k={w.k} alpha={w.alpha}", flush=True)
+def _codes_all_rows(X, op, g, M, K, k):
+    """Aq, As, XO of every row against the oracle, chunk by chunk."""
+    def check(r0):
+        r1 = min(M, r0 + CHUNK)
+        oq = layer.quantize_act(X[r0:r1], op["s"], op["O"])
+        _bits_equal(g["Aq"][r0:r1], oq["Aq"], f"Aq rows {r0}..{r1}")
+        _bits_equal(g["As"][r0:r1], oq["As"], f"As rows {r0}..{r1}")
+        _bits_equal(g["XO"][r0:r1], oq["XO"], f"XO rows {r0}..{r1}")
+        return r1 - r0
+    with cf.ThreadPoolExecutor(THREADS) as ex:
+        assert sum(ex.map(check, range(0, M, CHUNK))) == M
+
+
+def _run_full(w: synth.Workload, layout="1x32", score="max", all_rows=True):
+    print(f"\n[full-size] {w.name} layout={layout} score={score} k={w.k} alpha={w.alpha} all_rows={all_rows}",
+          flush=True)
     X, W = w.make_x(), w.make_w()
     M, K, N = X.shape[0], X.shape[1], W.shape[0]
     Xd, Wd = dev(X), dev(W)
@@ -65,15 +85,18 @@ def _run_full(w: synth.Workload, layout="1x32", score="max"):
     Y32 = torch.empty((M, N), dtype=torch.float32, device="cuda")
     mg.mg_dual_gemm(p, a, Y32)
     torch.cuda.synchronize()
-    g = dict(act_max=host(act_max), w_max=host(w_max), Y=host(Y[ridx]), Y32=host(Y32[ridx]),
-             Aq=host(a.Aq[ridx]), As=scale_rows(a.As, M, K)[rows], XO=outlier_cols(host(a.XO[ridx]), w.k))
+    g = dict(act_max=host(act_max), w_max=host(w_max), Y=host(Y[ridx]), Y32=host(Y32[ridx]))
+    if all_rows:
+        g.update(Aq=host(a.Aq), As=scale_rows(a.As, M, K), XO=outlier_cols(host(a.XO), w.k))
+    else:
+        g.update(Aq=host(a.Aq[ridx]), As=scale_rows(a.As, M, K)[rows], XO=outlier_cols(host(a.XO[ridx]), w.k))
     g.update({n: host(t) for n, t in p.tensors().items()})
     g["Ws"] = scale_rows(p.Ws, N, K)
     g["WO"] = outlier_cols(p.WO, w.k)
     del Y, Y32, a, Xd, Wd
     torch.cuda.empty_cache()
 
-    # oracle: plan on the full data, forward on the sampled rows
+    # oracle: plan on the full data, codes on every (or the sampled) rows, output on the sampled rows
     o_a = layer.act_max(X)
     o_w = layer.weight_range(W)
     op = layer.plan(o_a, o_w, W, w.alpha, w.k, layout, True, score)
@@ -84,8 +107,12 @@ def _run_full(w: synth.Workload, layout="1x32", score="max"):
     if layout != "1x32":
         _bits_equal(g["Wst"], op["Wst"], "Wst")
     oq = layer.quantize_act(X[rows], op["s"], op["O"])
-    for name in ("Aq", "As", "XO"):
-        _bits_equal(g[name], oq[name], name)
+    if all_rows:
+        _codes_all_rows(X, op, g, M, K, w.k)
+        print(f"[full-size] {w.name}: Aq, As, XO equal on all {M} rows", flush=True)
+    else:
+        for name in ("Aq", "As", "XO"):
+            _bits_equal(g[name], oq[name], name)
     Y64 = layer.dual_gemm_f64(oq["Aq"], oq["As"], op["Wq"], op["Ws"], oq["XO"], op["WO"])
     err = check_output(g["Y"], g["Y32"], Y64)
     print(f"[full-size] {w.name}: max|dY32|/max|Y| = {err:.3e} on {rows.size} rows", flush=True)
@@ -104,11 +131,11 @@ def test_ffn0_720p_k128_alpha07():
 
 
 def test_ffn0_480p_tile_scales():
-    _run_full(synth.FFN0_480P, layout="32x32")
+    _run_full(synth.FFN0_480P, layout="32x32", all_rows=False)
 
 
 def test_ffn0_480p_stripe_scales():
-    _run_full(synth.FFN0_480P, layout="128x1")
+    _run_full(synth.FFN0_480P, layout="128x1", all_rows=False)
 
 
 def test_ffn2_480p_smoothed_score():

@@ -70,10 +70,54 @@ def test_bf16_shapes(M, K, N, k):
     or with a partial last window (K = 768 also has an odd number of 256-deep
     stages, so the last window's second half is all pad; K = 4128 ends in a
     window of one block; K = 32 is one block in one stage), M and N not
-    multiples of the 256x256 tile (M = 1 included), and outlier rows of whole
-    16-byte chunks (k % 8 == 0), of 4-byte words (even k; k = 70 and 130 span
-    two and three outlier stages, the last partial) or neither (odd k)."""
+    multiples of the 256x256 tile (M = 1 included), and every k: the outlier
+    rows are padded to a multiple of 8 values, so k % 8 != 0 leaves pad columns
+    inside the last 16-byte chunk, and k = 70 and 130 span two and three
+    outlier stages, the last one partial."""
     X, W = _heavy(M, K, N, 1000 + M)
+    g = run_pipeline(X, W, 0.6, k)
+    _compare(g, _oracle(X, W, 0.6, k))
+
+
+@pytest.mark.parametrize("layout", ["1x32", "32x32", "128x1"])
+def test_dead_channels(layout):
+    """Eq. (2) at the floor of its statistics (reading: 1e-5 on both before the
+    powers): all-zero activation channels (as after a gate), all-zero weight
+    columns, one channel zero in both; with k = 24 the dead activation
+    channels stay in the bulk, with k = K - 3 all but three channels, the dead
+    ones included, go to the outlier branch.  Every artefact is bit-exact,
+    including s on the dead channels.  Then an all-zero batch through a plan
+    whose statistics are all zero but one weight column: every code is the
+    zero code and the output is zero."""
+    M, K, N = 300, 512, 192
+    X, W = _heavy(M, K, N, 4242)
+    X[:, [3, 40, 41, 200]] = 0
+    W[:, [17, 40, 333]] = 0
+    for k in ((24, K - 3) if layout == "1x32" else (24,)):
+        o = _oracle(X, W, 0.6, k, layout)
+        assert all(o["act_max"][j] == 0 for j in (3, 40, 200)) and all(o["w_max"][j] == 0 for j in (17, 40, 333))
+        assert (3 in o["O"]) == (k == K - 3)
+        g = run_pipeline(X, W, 0.6, k, layout)
+        _compare(g, o, layout)
+    Z = np.zeros((40, 96), np.uint16)
+    WZ = np.zeros((64, 96), np.uint16)
+    WZ[:, 5] = synth.f32_to_bf16_bits(np.full(64, 0.25, np.float32))
+    g = run_pipeline(Z, WZ, 0.5, 4, layout)
+    o = _oracle(Z, WZ, 0.5, 4, layout)
+    for name in ("act_max", "w_max", "s", "rcp", "O", "pos", "Wq", "Ws", "WO", "Aq", "As", "XO"):
+        assert np.array_equal(np.asarray(g[name]).view(np.uint8), np.asarray(o[name]).view(np.uint8)), name
+    assert not np.asarray(g["Aq"]).any() and not np.asarray(g["As"]).any()
+    assert not np.abs(g["Y32"]).any() and not (np.asarray(g["Y"]) & 0x7FFF).any()
+
+
+@pytest.mark.parametrize("M,K,N,k", [(48, 16416, 64, 40), (24, 32768, 32, 64), (16, 65536, 32, 128),
+                                     (9, 40000, 64, 7)])
+def test_large_K(M, K, N, k):
+    """Input widths past 8192 and 16384 channels, where the top-k kernel holds
+    17-32 and 33-64 scores per thread (its two larger instantiations), up to
+    the header's limit K = 65536; the GEMM then walks 64-256 bulk stages."""
+    X, W = _heavy(M, K, N, 5000 + K)
+    X[:, 7] = X[:, 8]                           # a tie between two channels' maxima
     g = run_pipeline(X, W, 0.6, k)
     _compare(g, _oracle(X, W, 0.6, k))
 

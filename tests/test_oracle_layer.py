@@ -77,6 +77,52 @@ def test_smooth_scale_closed_form(alpha):
     assert spread(w * s2) > spread(w * s) and spread(a / s2) < spread(a / s)
 
 
+def _f32_neighbours(x: float) -> set:
+    """The f32 values next to the real x (one of them is any faithful rounding)."""
+    lo = float(np.float32(x))
+    if lo > x:
+        lo = float(np.nextafter(np.float32(lo), np.float32(-np.inf)))
+    return {lo, float(np.nextafter(np.float32(lo), np.float32(np.inf)))}
+
+
+def test_smooth_scale_floor_at_zero_statistics():
+    """Eq. (2) on dead channels (reading: both statistics are floored at 1e-5
+    before the powers).  Pinned without the oracle's own pow: at a = w = 0 the
+    scale is 1e-5^(2 alpha - 1) -- exactly 1 at alpha = 0.5, sqrt(1e-5) at
+    0.75, 1/sqrt(1e-5) at 0.25 --, a zero activation channel with a live
+    weight column gives exp(alpha ln 1e-5 - (1 - alpha) ln w), a live
+    activation channel with a zero weight column exp(alpha ln a - (1 - alpha)
+    ln 1e-5); everything below the floor (zero, subnormals, 1e-6) gives the
+    same s as the floor itself, and just above it s moves."""
+    z = np.zeros(1, np.float32)
+    s, rcp = layer.smooth_scales(z, z, 0.5)
+    assert float(s[0]) == 1.0 and float(rcp[0]) == 1.0
+    s, _ = layer.smooth_scales(z, z, 0.75)
+    assert float(s[0]) in _f32_neighbours(math.sqrt(1e-5))
+    s, _ = layer.smooth_scales(z, z, 0.25)
+    assert float(s[0]) in _f32_neighbours(1.0 / math.sqrt(1e-5))
+    w = np.array([0.09, 0.5, 3e-5], np.float32)
+    for alpha in (0.3, 0.5, 0.6, 0.7):
+        s, _ = layer.smooth_scales(np.zeros(3, np.float32), w, alpha)
+        for j in range(3):
+            want = math.exp(alpha * math.log(1e-5) - (1 - alpha) * math.log(float(w[j])))
+            assert float(s[j]) in _f32_neighbours(want), (alpha, j)
+        a = np.array([0.7, 25.0, 2e-5], np.float32)
+        s, _ = layer.smooth_scales(a, np.zeros(3, np.float32), alpha)
+        for j in range(3):
+            want = math.exp(alpha * math.log(float(a[j])) - (1 - alpha) * math.log(1e-5))
+            assert float(s[j]) in _f32_neighbours(want), (alpha, j)
+    below = np.array([0.0, 1e-45, 1e-38, 1e-6, 9.9e-6, 1e-5], np.float32)
+    below[-1] = np.float32(1e-5) if float(np.float32(1e-5)) <= 1e-5 else np.nextafter(np.float32(1e-5), np.float32(0))
+    wcol = np.full(below.size, 0.2, np.float32)
+    s_a, _ = layer.smooth_scales(below, wcol, 0.6)
+    s_w, _ = layer.smooth_scales(wcol, below, 0.6)
+    assert np.unique(s_a).size == 1 and np.unique(s_w).size == 1
+    above = np.array([2e-5], np.float32)
+    assert layer.smooth_scales(above, wcol[:1], 0.6)[0][0] > s_a[0]
+    assert layer.smooth_scales(wcol[:1], above, 0.6)[0][0] < s_w[0]
+
+
 def test_smooth_off_is_identity():
     a = np.array([3.0, 0.5], np.float32)
     s, rcp = layer.smooth_scales(a, a, 0.5, smooth=False)
