@@ -255,6 +255,24 @@ int mg_quantize_act_stats(const mg_plan* p, const void* X, int32_t dtype, int64_
 int mg_forward(const mg_plan* p, const void* X, int32_t dtype, int64_t M, const mg_act* a,
                void* Y, int32_t y_dtype, hipStream_t stream);
 
+/* mg_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * activation workspace (Aq, As, XO) is not passed in: it lives in a fixed
+ * 64 MiB array inside the library, one copy per GPU, created when the library
+ * is first used on that GPU and held until the process ends.  The call makes
+ * no hipMalloc / hipFree and no allocating library call.
+ * Limit: the workspace of M rows -- Aq, As, XO as mg_act_bytes gives them,
+ * each rounded up to 256 bytes -- must fit in 64 MiB (K = 5120, k = 64: up to
+ * about 23,500 rows), else MG_ERR_UNSUPPORTED before anything is launched.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (nothing in it has to start at zero: the quantize step writes every
+ * byte the GEMM reads).  Calls ordered on one stream are safe; calls that
+ * overlap on one GPU (other streams, or threads without ordering) race and
+ * give wrong results.  Otherwise the arguments, errors and results are those
+ * of mg_forward. */
+int mg_forward_noalloc(const mg_plan* p, const void* X, int32_t dtype, int64_t M, void* Y, int32_t y_dtype,
+                       hipStream_t stream);
+
 /* Between the two projections of the FFN block: out[i] = gelu_tanh(in[i]) for
  * n bf16 values (in == out allowed), gelu_tanh(y) = 0.5 y (1 + tanh(sqrt(2/pi)
  * (y + 0.044715 y^3))).  Evaluated in f32 as the equal y / (1 + exp(-2u))

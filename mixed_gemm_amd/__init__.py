@@ -63,7 +63,8 @@ class mg_pct(ctypes.Structure):
 EXPORTS = ("mg_version", "mg_last_error", "mg_plan_bytes", "mg_act_bytes", "mg_calib_reset",
            "mg_calib_act", "mg_weight_range", "mg_smooth_scales", "mg_outlier_set", "mg_fold_pack",
            "mg_plan_build", "mg_quantize_act", "mg_dual_gemm", "mg_forward", "mg_gelu_tanh_bf16",
-           "mg_gelu_quantize_act", "mg_pct_reset", "mg_pct_count", "mg_pct_select", "mg_quantize_act_stats")
+           "mg_gelu_quantize_act", "mg_pct_reset", "mg_pct_count", "mg_pct_select", "mg_quantize_act_stats",
+           "mg_forward_noalloc")
 
 _lib = None
 
@@ -92,6 +93,7 @@ def lib() -> ctypes.CDLL:
             "mg_quantize_act": ([P(mg_plan), vp, i32, i64, P(mg_act), vp], ctypes.c_int),
             "mg_dual_gemm": ([P(mg_plan), P(mg_act), i64, vp, i32, vp], ctypes.c_int),
             "mg_forward": ([P(mg_plan), vp, i32, i64, P(mg_act), vp, i32, vp], ctypes.c_int),
+            "mg_forward_noalloc": ([P(mg_plan), vp, i32, i64, vp, i32, vp], ctypes.c_int),
             "mg_gelu_tanh_bf16": ([vp, vp, i64, vp], ctypes.c_int),
             "mg_gelu_quantize_act": ([P(mg_plan), vp, i64, P(mg_act), vp], ctypes.c_int),
             "mg_quantize_act_stats": ([P(mg_plan), vp, i32, i64, P(mg_act), vp, vp], ctypes.c_int),
@@ -386,6 +388,15 @@ def mg_forward(plan: Plan, X: torch.Tensor, act: Act, Y: torch.Tensor, stream=No
     p, a = plan.c(), act.c()
     _check(lib().mg_forward(ctypes.byref(p), _ptr(X), _dtype(X), X.shape[0], ctypes.byref(a), _ptr(Y),
                             _dtype(Y), _stream(stream)))
+
+
+def mg_forward_noalloc(plan: Plan, X: torch.Tensor, Y: torch.Tensor, stream=None) -> None:
+    """mg_forward with the library's own per-GPU workspace (no Act; see the
+    header for the size limit and the sharing rule)."""
+    M, _ = _matrix(X, "X", plan.desc.K)
+    _check_y(plan.desc, Y, M)
+    p = plan.c()
+    _check(lib().mg_forward_noalloc(ctypes.byref(p), _ptr(X), _dtype(X), M, _ptr(Y), _dtype(Y), _stream(stream)))
 
 
 def mg_gelu_tanh_bf16(inp: torch.Tensor, out: torch.Tensor, stream=None) -> None:

@@ -95,6 +95,25 @@ int check_act(const mg_plan* p, const mg_act* a) {
 
 namespace mg {
 
+int check_forward(const mg_plan* p, const void* X, int32_t dtype, int64_t M, const void* Y, int32_t y_dtype) {
+    if (int e = check_plan(p, true)) return e;
+    if (int e = check_dtype(dtype)) return e;
+    if (int e = check_dtype(y_dtype)) return e;
+    if (M < 0) return fail(MG_ERR_SHAPE, "M=%lld must be >= 0", (long long)M);
+    if (M == 0) return MG_OK;
+    MG_CHECK_PTR(X, "X");
+    MG_CHECK_PTR(Y, "Y");
+    return check_gemm_size(p, M);
+}
+
+int fail_msg(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
 int device_cu_count() {
     static thread_local int cached_dev = -1;
     static thread_local int cached_cus = 0;
@@ -307,11 +326,10 @@ int mg_dual_gemm(const mg_plan* p, const mg_act* a, int64_t M, void* Y, int32_t 
 
 int mg_forward(const mg_plan* p, const void* X, int32_t dtype, int64_t M, const mg_act* a, void* Y,
                int32_t y_dtype, hipStream_t stream) {
-    if (int e = check_plan(p, true)) return e;
-    if (int e = check_dtype(y_dtype)) return e;
-    if (M < 0) return fail(MG_ERR_SHAPE, "M=%lld must be >= 0", (long long)M);
+    // every check of both steps before anything is launched
+    if (int e = mg::check_forward(p, X, dtype, M, Y, y_dtype)) return e;
     if (M == 0) return MG_OK;
-    MG_CHECK_PTR(Y, "Y");
+    if (int e = check_act(p, a)) return e;
     if (int e = mg_quantize_act(p, X, dtype, M, a, stream)) return e;
     return mg_dual_gemm(p, a, M, Y, y_dtype, stream);
 }

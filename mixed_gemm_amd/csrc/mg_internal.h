@@ -61,4 +61,12 @@ hipError_t launch_pct_select(int32_t K, int pass, double q, uint32_t* hist, int3
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 
+// Every argument check of mg_forward except the activation workspace (plan,
+// dtypes, M, X, Y, operand sizes); MG_OK or the error (message set).
+int check_forward(const mg_plan* p, const void* X, int32_t dtype, int64_t M, const void* Y, int32_t y_dtype);
+
+// Sets the calling thread's mg_last_error() message (printf format) and
+// returns code.
+int fail_msg(int code, const char* fmt, ...);
+
 }  // namespace mg

@@ -266,3 +266,26 @@ def test_binding_checks_shapes_before_any_launch():
               lambda: mg.mg_calib_act(X, v64)):
         with pytest.raises(ValueError, match="device tensor"):
             f()
+
+
+def test_forward_validates_both_steps_before_launching():
+    """mg_forward and mg_forward_noalloc check every argument of both steps
+    (including the GEMM's 3 GiB operand limit) before any launch: on this
+    GPU-less host an accepted call would fail with a HIP error instead."""
+    L = mg.lib()
+    p = _plan(K=5120, N=256, k=64)
+    a = mg.mg_act(FAKE, FAKE, FAKE)
+    big = (3 << 30) // 2560 + 1                    # Aq of this many rows passes 3 GiB
+    assert L.mg_forward(ctypes.byref(p), FAKE, 1, big, ctypes.byref(a), FAKE, 1, None) == -5
+    assert L.mg_forward(ctypes.byref(p), FAKE, 1, 8, ctypes.byref(a), FAKE, 9, None) == -3
+    assert L.mg_forward(ctypes.byref(p), FAKE, 1, 0, None, None, 1, None) == 0          # M == 0: no-op
+    # the no-allocation variant: the same checks, then its 64 MiB workspace limit
+    assert L.mg_forward_noalloc(None, FAKE, 1, 8, FAKE, 1, None) == -1
+    assert L.mg_forward_noalloc(ctypes.byref(p), FAKE, 1, -1, FAKE, 1, None) == -2
+    assert L.mg_forward_noalloc(ctypes.byref(p), FAKE, 7, 8, FAKE, 1, None) == -3
+    assert L.mg_forward_noalloc(ctypes.byref(p), FAKE, 1, 8, None, 1, None) == -1
+    assert L.mg_forward_noalloc(ctypes.byref(p), FAKE + 4, 1, 8, FAKE, 1, None) == -4
+    assert L.mg_forward_noalloc(ctypes.byref(p), FAKE, 1, 0, FAKE, 1, None) == 0
+    assert L.mg_forward_noalloc(ctypes.byref(p), FAKE, 1, 24000, FAKE, 1, None) == -5
+    assert b"limit" in L.mg_last_error()
+    assert L.mg_forward_noalloc(ctypes.byref(p), FAKE, 1, big, FAKE, 1, None) == -5
