@@ -84,7 +84,8 @@ typedef struct {
  *  O   [k]        i32  outlier channels, ascending (null allowed when k == 0);
  *  pos [K]        i32  index of channel j in O, or -1;
  *  Wq  [N][K/2]   u8   MXFP4 payload of the folded bulk weights RN(s_j W[n][j]),
- *                      outlier columns set to +0 before encoding;
+ *                      outlier columns set to +0 before encoding, in fragment
+ *                      order (below);
  *  Ws             u8   E8M0 scale of each (row, 32-block), in scale windows
  *                      (below) -- for MG_W_32X32 the tile's code repeated on
  *                      each of its 32 rows, for MG_W_128X1 the stripe's code
@@ -92,15 +93,27 @@ typedef struct {
  *  Wst                 compact codes: [N/32][K/32] u8 tile codes (MG_W_32X32),
  *                      [N][ceil(K/128)] u8 stripe codes (MG_W_128X1); null
  *                      allowed for MG_W_1X32;
- *  WO  [N][kp]    bf16 folded outlier columns, kp = k rounded up to a multiple
- *                      of 8 (rows 16-byte aligned; columns k .. kp-1 hold +0);
- *                      null allowed when k == 0.
+ *  WO  [N][k]     bf16 folded outlier columns (2k bytes per row) in fragment
+ *                      order; null allowed when k == 0.
+ *
+ * Fragment order (Wq, Aq: rows of K/2 bytes; WO, XO: rows of 2k bytes).  The
+ * [rows][row_bytes] byte matrix is cut into blocks of 32 rows x 32 bytes --
+ * one operand of a 32x32x64 FP4 or 32x32x16 bf16 matrix-core instruction --
+ * each stored as 1024 contiguous bytes: block (g = r / 32, c = byte / 32) at
+ * (g * ns + c) * 1024 with ns = 2 * ceil(row_bytes / 64) (an even number of
+ * 32-byte slices per row), and inside it byte b of row r's slice at
+ *     16 * (r % 32 + 32 * (b / 16)) + b % 16,
+ * for ceil(rows / 32) * ns * 1024 bytes in all.  Pads -- rows up to the next
+ * multiple of 32 and bytes up to ns * 32 per row -- hold 0 (zero codes, +0).
+ * The dual GEMM copies whole 1 KB blocks, and a block's 16-byte pieces are
+ * already in the order the instruction's 64 lanes take them.
  *
  * Scale windows (Ws, As).  The E8M0 codes of a [rows][K/32] scale matrix are
  * stored in windows of 256 rows x 16 blocks (512 channels), 16 bytes per row,
- * 4096 contiguous bytes per window, windows of a 256-row group consecutive:
- * the code of (row r, block b) is at byte
- *     ((r / 256) * nwin + b / 16) * 4096 + (r % 256) * 16 + b % 16,
+ * 4096 contiguous bytes per window, windows of a 256-row group consecutive.
+ * Inside a window row the codes of the even blocks come first, then those of
+ * the odd blocks: the code of (row r, block b) is at byte
+ *     ((r / 256) * nwin + b / 16) * 4096 + (r % 256) * 16 + 8 * (b % 2) + (b % 16) / 2,
  * nwin = ceil(K / 512), for ceil(rows / 256) * nwin * 4096 bytes in all.  The
  * layout depends on K only (a buffer sized for more rows serves fewer).  The
  * writers fill the whole last 256-row group: blocks past K/32 and rows past
@@ -119,9 +132,9 @@ typedef struct {
 } mg_plan;
 
 /* Per-forward activation workspace (sizes from mg_act_bytes):
- *  Aq [M][K/2] u8 MXFP4 payload of the bulk quotients, As the E8M0 code of
- *  each (row, 32-block) in scale windows (see mg_plan), XO [M][kp] bf16
- *  outlier quotients, kp as for WO (pad columns +0; null allowed when k == 0). */
+ *  Aq [M][K/2] u8 MXFP4 payload of the bulk quotients in fragment order, As
+ *  the E8M0 code of each (row, 32-block) in scale windows, XO [M][k] bf16
+ *  outlier quotients in fragment order (null allowed when k == 0); see mg_plan. */
 typedef struct {
     uint8_t* Aq;
     uint8_t* As;

@@ -199,7 +199,7 @@ def _check_act(desc, act: "Act", M: int | None = None) -> None:
     want = mg_act_bytes(desc, act.M)
     got = [_nbytes(act.Aq), _nbytes(act.As), _nbytes(act.XO)]
     _need(got == want, f"act buffers {got} bytes do not match the plan's sizes {want} for M={act.M}")
-    _need(tuple(act.Aq.shape) == (act.M, desc.K // 2), f"act.Aq must be [{act.M}][{desc.K // 2}]")
+    _need(tuple(act.Aq.shape) == frag_shape(act.M, desc.K // 2), f"act.Aq must have shape {frag_shape(act.M, desc.K // 2)}")
 
 
 def _check_y(desc, Y: torch.Tensor, M: int) -> None:
@@ -228,10 +228,12 @@ def mg_act_bytes(desc: mg_plan_desc, M: int) -> list[int]:
     return list(out)
 
 
-def xo_cols(k: int) -> int:
-    """Row stride of the outlier operands XO [M][kp] and WO [N][kp]: k rounded
-    up to a multiple of 8 (pad columns hold +0)."""
-    return (k + 7) // 8 * 8
+def frag_shape(rows: int, row_bytes: int) -> tuple:
+    """Shape of an operand stored in fragment order (Aq, Wq: row_bytes = K/2;
+    XO, WO: row_bytes = 2k), as bytes: [ceil(rows/32)][2 ceil(row_bytes/64)][1024]
+    (the C header's fragment order: 1 KB blocks of 32 rows x 32 bytes, an even
+    number of 32-byte slices per row)."""
+    return (-(-rows // 32), 2 * -(-row_bytes // 64), 1024)
 
 
 def scale_shape(rows: int, K: int) -> tuple:
@@ -258,7 +260,8 @@ class Plan:
         got = [_nbytes(t) for t in self.tensors().values()]
         want = mg_plan_bytes(self.desc)
         _need(got == want, f"plan buffer sizes {got} differ from mg_plan_bytes {want}")
-        _need(tuple(self.Wq.shape) == (self.desc.N, self.desc.K // 2), "plan.Wq must be [N][K/2]")
+        _need(self.Wq.dtype == torch.uint8 and tuple(self.Wq.shape) == frag_shape(self.desc.N, self.desc.K // 2),
+              "plan.Wq must be uint8 of frag_shape(N, K/2)")
 
     @staticmethod
     def empty(desc: mg_plan_desc, device="cuda") -> "Plan":
@@ -266,8 +269,8 @@ class Plan:
         e = lambda n, dt: torch.empty(n, dtype=dt, device=device)
         wst = {MG_W_32X32: (N // 32, K // 32), MG_W_128X1: (N, (K + 127) // 128)}.get(desc.layout, 0)
         p = Plan(desc, e(K, torch.float32), e(K, torch.float32), e(k, torch.int32), e(K, torch.int32),
-                 e((N, K // 2), torch.uint8), e(scale_shape(N, K), torch.uint8), e(wst, torch.uint8),
-                 e((N, xo_cols(k)), torch.bfloat16))
+                 e(frag_shape(N, K // 2), torch.uint8), e(scale_shape(N, K), torch.uint8), e(wst, torch.uint8),
+                 e(frag_shape(N, 2 * k), torch.uint8))
         return p
 
     def c(self) -> mg_plan:
@@ -303,9 +306,9 @@ class Act:
     @staticmethod
     def empty(desc: mg_plan_desc, M: int, device="cuda") -> "Act":
         K, k = desc.K, desc.k
-        a = Act(M, torch.empty((M, K // 2), dtype=torch.uint8, device=device),
+        a = Act(M, torch.empty(frag_shape(M, K // 2), dtype=torch.uint8, device=device),
                 torch.empty(scale_shape(M, K), dtype=torch.uint8, device=device),
-                torch.empty((M, xo_cols(k)), dtype=torch.bfloat16, device=device))
+                torch.empty(frag_shape(M, 2 * k), dtype=torch.uint8, device=device))
         _check_act(desc, a)
         return a
 

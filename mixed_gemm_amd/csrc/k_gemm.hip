@@ -15,6 +15,11 @@
 //   B (src1): lane l holds column l%32 and the same K range;
 //   E8M0 scale of lane l: the 32-block of its K range, byte 0 of the operand;
 //   D: lane l, register r holds row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+// The operands are stored in fragment order (frag_offset): every 32 rows x 32
+// bytes of Aq, Wq, XO, WO -- one A or B operand of either instruction -- is one
+// contiguous 1 KB block whose 16-byte lane pieces sit in lane order, so a copy
+// moves whole cache lines and a lane's fragment is one conflict-free 16-byte
+// LDS read.
 #include <type_traits>
 #include <utility>
 
@@ -35,58 +40,69 @@ namespace {
 // of 32x32 (256 fp32 accumulators per lane, held in the accumulation
 // registers).
 //
-// The K dimension is walked in stages that each move 128 bytes per tile row
-// into LDS: a bulk stage carries 256 FP4 values (128 B) of Aq / Wq, an outlier
-// stage carries 64 bf16 values (128 B) of XO / WO.  Both kinds use the same LDS
-// layout and the same fragment addressing -- sub-step ss of a stage reads
-// bytes [32 ss + 16 h, 32 ss + 16 h + 16) of a row for lane half h -- which is
-// 64 FP4 (one scaled FP4 MFMA) or 16 bf16 (one BF16 MFMA).  Bulk stages come
-// first, outlier stages follow, all accumulating into the same registers.
+// K is walked in half-stages of two 32-byte K-slices per tile row: a bulk
+// half-stage carries 128 FP4 values of Aq / Wq, an outlier half-stage 32 bf16
+// values of XO / WO.  A half-stage of a tile is 2 x 8 x 2 fragment blocks
+// (A and B, 8 row groups, 2 slices) = 32 KB.  Slice sl of a half-stage is one
+// MFMA sub-step: FP4 (32x32x64, scaled) or BF16 (32x32x16), both on the same
+// accumulators.  Bulk half-stages come first, outlier half-stages follow.
 //
-// E8M0 scales.  A bulk stage needs 8 scale bytes per tile row.  They are not
-// fetched per lane (one cache line per row, per wave, per stage): the 16 bytes
-// of two consecutive bulk stages ("a window") of all 512 tile rows are copied
-// into LDS, next to the operand copies, and each wave reads its rows' 8 bytes
-// from there.  The scale arrays are stored window by window (256 rows x 16
-// bytes contiguous, the tile's rows), so a window of the A (B) tile is 4 KB
-// of contiguous memory: one 16-byte load per lane and row, 8 cache lines per
-// load instruction.  Windows alternate between two LDS slots.
+// Pipeline.  The half-stages of all of a workgroup's tiles form one sequence
+// over a ring of four 32 KB LDS slots.  While half-stage g is multiplied out
+// of slot g % 4, the copies of half-stage g + 2 (which may belong to the next
+// tile) run straight from global memory into slot (g + 2) % 4; at the end of
+// g each wave waits for the copies of g + 1 only (the 8 younger ones stay in
+// flight) and the workgroup meets at one barrier.  Two half-stages of lead
+// keep the copy path streaming (with one 64 KB stage in flight and waited at
+// every stage end it was latency-bound).  Inside a half-stage the issue order
+// is fixed slot by slot, one MFMA per slot: the previous half-stage's second
+// sub-step (its fragments read before the barrier) fills the first 16 slots,
+// so the matrix cores stay busy while this half-stage's first fragments are
+// read; the 8 copies go one per two slots.
 //
-// Pipeline.  The stages of all of a workgroup's tiles form one sequence over
-// two LDS buffers (2 x 64 KB).  While stage g is multiplied out of one buffer,
-// the copies of stage g+1 (which may be the first stage of the next tile) run
-// straight from global memory into the other buffer.  One barrier per stage.
-// In the steady state (a bulk stage followed by bulk stages of the same tile)
-// the instruction order of a stage is fixed slot by slot: each of its 64 MFMAs
-// is followed by at most one fragment read, scale read or copy, so memory
-// instructions never hold up a run of MFMAs, and sub-step 3 -- whose
-// fragments are read before the barrier -- is multiplied after it, so the
-// matrix cores stay busy while the next stage's first fragments are read.
-// After a tile's last stage its 256x256 bf16 result is staged through the
-// freed buffer and written as whole 512-byte rows while the next tile's first
-// stage already sits in LDS.
+// E8M0 scales.  A bulk half-stage needs 4 scale bytes per tile row.  The 16
+// bytes of four consecutive bulk half-stages ("a window") of all 512 tile
+// rows are copied into LDS with the copies of the window's first
+// half-stage, and each wave reads its rows' 4 bytes per half-stage from
+// there.  The scale arrays are stored window by window (256 rows x 16 bytes
+// contiguous, the tile's rows), so a window of the A (B) tile is 4 KB of
+// contiguous memory: one 16-byte load per lane and row, 8 cache lines per
+// load instruction.  Windows rotate over three LDS slots: a window is issued
+// two half-stages before its first use, and the two windows between it and
+// the previous occupant of its slot span at least two half-stages, so the
+// occupant's last read is at least one barrier older than the overwrite
+// (with two slots a tile ending one half-stage into a window -- k = 0 and
+// K mod 512 in (0, 128] -- would have its window overwritten while read).
 //
-// LDS rows are 128 B; logical 16-byte chunk c of tile row r is stored at
-// physical chunk c ^ ((r >> 1) & 7), which spreads the 16 rows a fragment load
-// reads at once over all 64 banks.  Loads use buffer descriptors sized to each
-// operand: rows past M (or N) and chunks past K / k read as zeros.  Tiles are
-// dealt so that each XCD (workgroups go round-robin to the 8 XCDs) walks a
-// contiguous run of the tile order, grouped 8 row-tiles at a time, which keeps
-// the operand panels of its concurrently running tiles in its L2.
+// After a tile's last half-stage its 256x256 bf16 result is staged through
+// the two ring slots that hold no pending copy and written as whole 512-byte
+// rows while the next tile's first half-stage already sits in LDS.
+// Operand rows past M (or N) and slices past K / k read as zeros through
+// buffer range checks.  Tiles are dealt so that each XCD (workgroups go
+// round-robin to the 8 XCDs) walks a contiguous run of the tile order,
+// grouped 8 row-tiles at a time, which keeps the operand panels of its
+// concurrently running tiles in its L2.
 // ---------------------------------------------------------------------------
 
 constexpr int TBM = 256, TBN = 256;
-constexpr int ROWB = 128;                         // bytes per tile row per stage
-constexpr int TILE_BYTES = TBM * ROWB;            // 32 KB
-constexpr int STAGE_BYTES = 2 * TILE_BYTES;       // A + B
-constexpr int SCW_ROWB = 16;                      // scale bytes per row per window (two bulk stages)
-constexpr int SCW_BYTES = (TBM + TBN) * SCW_ROWB; // one window slot: A rows then B rows (8 KB)
-constexpr int SCW_OFF = 2 * STAGE_BYTES;
-constexpr int GEMM_LDS_BYTES = 2 * STAGE_BYTES + 2 * SCW_BYTES;
-constexpr uint32_t OOB = 0xC0000000u;             // offset that reads as zero
+constexpr int NRG = TBM / kFragRows;                  // row groups per tile operand (8)
+constexpr int HS_SL = 2;                              // K-slices per half-stage
+constexpr int OP_BYTES = NRG * HS_SL * kFragBlock;    // one operand of a half-stage (16 KB)
+constexpr int HS_BYTES = 2 * OP_BYTES;                // A + B (32 KB)
+constexpr int RING = 4;                               // LDS slots
+constexpr int LEAD = 2;                               // half-stages copied ahead
+constexpr int NCOPY = 2 * NRG * HS_SL / 4;            // copies per wave and half-stage (8)
+constexpr int SCW_ROWB = 16;                          // scale bytes per row per window (4 half-stages)
+constexpr int SCW_BYTES = (TBM + TBN) * SCW_ROWB;     // one window slot: A rows then B rows (8 KB)
+constexpr int SCW_SLOTS = 3;
+constexpr int SCW_OFF = RING * HS_BYTES;
+constexpr int GEMM_LDS_BYTES = SCW_OFF + SCW_SLOTS * SCW_BYTES;   // 152 KB
+constexpr uint32_t OOB = 0xC0000000u;                 // offset that reads as zero
 constexpr int NXCD = 8;
 constexpr int GROUP_M = 8;
 static_assert(TBM == kScRows && TBN == kScRows && SCW_ROWB == kScBlocks, "a tile's scale window is one stored window");
+static_assert(kScBlocks == 4 * HS_SL * 2, "a window holds the scale bytes of four half-stages");
+static_assert(LEAD == 2 && NCOPY == 8, "the end-of-half-stage wait keeps exactly one half-stage of copies in flight");
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -149,11 +165,10 @@ dual_gemm_tiled(GemmArgs g) {
 
     const int K = g.K, k = g.k, N = g.N;
     const int64_t M = g.M;
-    const uint32_t rowA = (uint32_t)(K / 2);       // bytes per Aq / Wq row
-    const uint32_t rowX = (uint32_t)(2 * xo_cols(k));   // bytes per XO / WO row (16-byte multiple)
-    const int S4 = (K / 2 + ROWB - 1) / ROWB;      // bulk stages
-    const int S16 = (2 * k + ROWB - 1) / ROWB;     // outlier stages
-    const int S = S4 + S16;
+    const uint32_t ns4 = (uint32_t)frag_slices(K / 2);          // K-slices of a bulk row
+    const uint32_t nso = (uint32_t)frag_slices(2 * (int64_t)k); // K-slices of an outlier row
+    const int H4 = (int)(ns4 + 1) / 2;                          // bulk half-stages per tile
+    const int H = H4 + (int)(nso + 1) / 2;                      // all half-stages per tile
 
     // ---- this workgroup's tiles: XCD x owns tiles [x per, (x+1) per); its
     // workgroups take every nl-th one.
@@ -165,40 +180,37 @@ dual_gemm_tiled(GemmArgs g) {
     int t = xcd * per + (int)blockIdx.x / NXCD;
     if (t >= t_end) return;
 
-    const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.Aq, (uint64_t)M * rowA);
-    const __amdgpu_buffer_rsrc_t rB = make_rsrc(g.Wq, (uint64_t)N * rowA);
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.Aq, (uint64_t)frag_bytes(M, K / 2));
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(g.Wq, (uint64_t)frag_bytes(N, K / 2));
     const __amdgpu_buffer_rsrc_t rAs = make_rsrc(g.As, (uint64_t)sc_bytes(M, K));
     const __amdgpu_buffer_rsrc_t rBs = make_rsrc(g.Ws, (uint64_t)sc_bytes(N, K));
     const uint32_t nwin = (uint32_t)sc_nwin(K);
-    const __amdgpu_buffer_rsrc_t rXO = make_rsrc(g.XO, (uint64_t)M * rowX);
-    const __amdgpu_buffer_rsrc_t rWO = make_rsrc(g.WO, (uint64_t)N * rowX);
+    const __amdgpu_buffer_rsrc_t rXO = make_rsrc(g.XO, (uint64_t)frag_bytes(M, 2 * (int64_t)k));
+    const __amdgpu_buffer_rsrc_t rWO = make_rsrc(g.WO, (uint64_t)frag_bytes(N, 2 * (int64_t)k));
+    // row groups of the operands; tile row groups past them are clamped to
+    // the last one (their rows only feed output rows / columns past M / N,
+    // which are never stored)
+    const int GA = (int)((M + kFragRows - 1) / kFragRows), GB = N / kFragRows;
 
-    // ---- tile-independent lane constants.  Every per-row offset goes into
-    // the range-checked vector offset of the buffer instructions (the scalar
-    // offset is not range-checked), so rows past M / N read as zero.
-    // Copies: each load instruction of a wave moves 8 tile rows x 128 B = 1 KB
-    // into LDS, lane L landing at byte 16 L (row L/8 of the group, physical
-    // chunk L%8).  For 8-row group gi that slot holds logical chunk
-    // (L%8) ^ ((L/16) + 4 (gi & 1)), which the lane reads from global memory.
-    // Wave w copies rows [64 w, 64 w + 64) of the A and of the B tile.
-    const int lrow = lane >> 3;
-    const uint32_t c16e = (uint32_t)(((lane & 7) ^ (lrow >> 1)) << 4);        // even groups
-    const uint32_t c16o = c16e ^ 64u;                                          // odd groups
-    const uint32_t lrA0 = (uint32_t)(wave * 64 + lrow) * rowA;                 // copy row (group 0)
-    const uint32_t lrX0 = (uint32_t)(wave * 64 + lrow) * rowX;
-    const uint32_t lds_w = (uint32_t)(wave * 64 * ROWB);
+    // ---- tile-independent lane constants.  A copy moves one 1 KB fragment
+    // block (lane L: bytes 16 L .. 16 L + 15, landing at byte 16 L of the
+    // block's LDS place).  Wave w copies row groups 2 w and 2 w + 1 of the A
+    // and of the B tile, slices 0 and 1 of the half-stage: block (operand,
+    // row group rg, slice sl) of a slot sits at operand * 16 KB + (2 rg + sl)
+    // * 1 KB.  The block's global offset goes into the scalar offset, slice 1
+    // into the instruction offset (which moves the global and the LDS
+    // address alike), the lane's 16 L into the vector offset.
+    const uint32_t l16 = (uint32_t)lane * 16u;
     // scale windows: lane L of wave w copies window row 64 w + L of A and of
-    // B; a lane reads its fragment rows' 8 bytes at these offsets (+ 512 i)
+    // B; a lane reads the 2 codes of a half-stage (slices 0, 1 of its half of
+    // the K steps) of each of its fragment rows at these offsets (+ 512 i,
+    // + 2 (half-stage % 4)): row * 16 + 8 h
     const uint32_t lwr = (uint32_t)(wave * 64 + lane) * SCW_ROWB;
-    const uint32_t scw_a = (uint32_t)((wm * 128 + l32) * SCW_ROWB);
-    const uint32_t scw_b = (uint32_t)(TBM * SCW_ROWB + (wn * 128 + l32) * SCW_ROWB);
-    uint32_t fa[4], fb[4];                        // fragment rows within a stage buffer
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        fa[i] = (uint32_t)((wm * 128 + i * 32 + l32) * ROWB);
-        fb[i] = (uint32_t)(TILE_BYTES + (wn * 128 + i * 32 + l32) * ROWB);
-    }
-    const int sw = (l32 >> 1) & 7;   // (row >> 1) & 7 of every fragment row of this lane
+    const uint32_t scw_a = (uint32_t)((wm * 128 + l32) * SCW_ROWB + 8 * h);
+    const uint32_t scw_b = (uint32_t)(TBM * SCW_ROWB + (wn * 128 + l32) * SCW_ROWB + 8 * h);
+    // fragment reads: A row group 4 wm + i, B row group 4 wn + j
+    const uint32_t fa0 = (uint32_t)(wm * 4 * HS_SL * kFragBlock) + l16;
+    const uint32_t fb0 = (uint32_t)(OP_BYTES + wn * 4 * HS_SL * kFragBlock) + l16;
 
     auto tile_org = [&](int tt) {
         TileOrg o;
@@ -211,172 +223,178 @@ dual_gemm_tiled(GemmArgs g) {
     };
 
     v16f acc[4][4];
-    uint32_t scA[4][2], scB[4][2], nA[4][2], nB[4][2];
-    int wiss = 0;      // scale windows issued so far (slot of the next one: wiss & 1)
-    int wuse = 0;      // scale windows taken into use so far
-    int wcur = 0;      // slot of the window of the current bulk stage
+    uint32_t scA[4], scB[4], pA[4], pB[4];
+    int wiss = 0;      // slot of the next scale window to issue (0, 1, 2, 0, ...)
+    int wnext = 0;     // slot of the next scale window to take into use
+    int wcur = 0;      // slot of the window of the current bulk half-stage
 
-    // ---- scale window w (bulk stages 2w, 2w+1) of a tile into the next slot:
-    // the stored windows of the tile's 256 A rows and 256 B rows (4 KB each)
+    // ---- copy cursor: the next half-stage to copy -- tile ct, half-stage
+    // cst, origin corg -- and its source: the resources of the A and B
+    // operands (bulk or outlier) and the global offsets of its slice-0
+    // blocks in this wave's two A and two B row groups.  `issued`
+    // half-stages have been copied, into ring slots issued % 4.  Wave-uniform
+    // (scalar registers); inside a tile's bulk or outlier run an advance is
+    // four scalar adds.
+    int ct = t, cst = 0, issued = 0;
+    TileOrg corg = tile_org(t);
+    __amdgpu_buffer_rsrc_t csA = rA, csB = rB;
+    uint32_t cA0 = 0, cA1 = 0, cB0 = 0, cB1 = 0;
+    auto cursor_src = [&]() {        // sources of half-stage cst of tile ct (ct < t_end)
+        const bool bulk = cst < H4;
+        const uint32_t ns = bulk ? ns4 : nso;
+        const uint32_t s0 = (uint32_t)(2 * (bulk ? cst : cst - H4)) * (uint32_t)kFragBlock;
+        const int ga = (int)(corg.m0 / kFragRows) + 2 * wave, gb = corg.n0 / kFragRows + 2 * wave;
+        csA = bulk ? rA : rXO;
+        csB = bulk ? rB : rWO;
+        cA0 = (uint32_t)min(ga, GA - 1) * ns * (uint32_t)kFragBlock + s0;
+        cA1 = (uint32_t)min(ga + 1, GA - 1) * ns * (uint32_t)kFragBlock + s0;
+        cB0 = (uint32_t)min(gb, GB - 1) * ns * (uint32_t)kFragBlock + s0;
+        cB1 = (uint32_t)min(gb + 1, GB - 1) * ns * (uint32_t)kFragBlock + s0;
+    };
+    cursor_src();
+
+    // scale window w (bulk half-stages 4w .. 4w+3) of a tile into the next
+    // slot: the stored windows of the tile's 256 A rows and 256 B rows (4 KB each)
     auto load_window = [&](const TileOrg& o, int w) {
-        const int slot = wiss & 1;
-        ++wiss;
+        const int slot = wiss;
+        wiss = wiss == SCW_SLOTS - 1 ? 0 : wiss + 1;
         uint8_t* dst = lds + SCW_OFF + slot * SCW_BYTES + wave * 64 * SCW_ROWB;
-        uint32_t r = lwr;
-        asm volatile("" : "+v"(r));
         const uint32_t wa = __builtin_amdgcn_readfirstlane(((uint32_t)(o.m0 / TBM) * nwin + (uint32_t)w) * kScWinBytes);
         const uint32_t wb = __builtin_amdgcn_readfirstlane(((uint32_t)(o.n0 / TBN) * nwin + (uint32_t)w) * kScWinBytes);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rAs, (lds_ptr_t)dst, 16, wa + r, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rBs, (lds_ptr_t)(dst + TBM * SCW_ROWB), 16, wb + r, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rAs, (lds_ptr_t)dst, 16, lwr, wa, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rBs, (lds_ptr_t)(dst + TBM * SCW_ROWB), 16, lwr, wb, 0, 0);
     };
-
-    // ---- this lane's scale words of bulk stage st (from its window)
-    auto read_scales_i = [&](const uint8_t* wsc, int q) {
-        if (q < 4) {
-            const u32x2 x = *reinterpret_cast<const u32x2*>(wsc + scw_a + q * 32 * SCW_ROWB);
-            nA[q][0] = x[0]; nA[q][1] = x[1];
-        } else {
-            const u32x2 x = *reinterpret_cast<const u32x2*>(wsc + scw_b + (q - 4) * 32 * SCW_ROWB);
-            nB[q - 4][0] = x[0]; nB[q - 4][1] = x[1];
-        }
-    };
-    auto window_of = [&](int st) -> const uint8_t* {
-        if ((st & 1) == 0) { wcur = wuse & 1; ++wuse; }
-        return lds + SCW_OFF + wcur * SCW_BYTES + (st & 1) * 8;
-    };
-    // lane half h uses the odd scale bytes: shift them down so sub-step ss
-    // finds its byte at position 2*(ss&1) of word ss>>1.
-    const uint32_t sc_shift = (uint32_t)h * 8u;
-    auto take_scales = [&]() {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            scA[i][0] = nA[i][0] >> sc_shift;
-            scA[i][1] = nA[i][1] >> sc_shift;
-            scB[i][0] = nB[i][0] >> sc_shift;
-            scB[i][1] = nB[i][1] >> sc_shift;
-        }
-    };
-
-    // ---- the stage whose copies are issued during the current one: stage
-    // `st` of tile `o` (bulk stages first, then outlier stages), or nothing
-    // (st < 0).  Wave-uniform.
-    struct NextCopy {
-        TileOrg o;
-        int st;
-    };
-
-    // Copies of one 8-row group of the A (B) tile of stage nc (asynchronous,
-    // straight into LDS buffer b).  With nothing to copy every lane reads out
-    // of range, which lands zeros in the free buffer.
-    auto copy_part = [&](const NextCopy& nc, int b, int part, bool isB) {
-        uint8_t* dst = lds + b * STAGE_BYTES + lds_w + (isB ? TILE_BYTES : 0) + part * 8 * ROWB;
-        const bool bulk = nc.st < S4;
-        const uint32_t rowb = bulk ? rowA : rowX;
-        uint32_t lr = bulk ? lrA0 : lrX0;
-        asm volatile("" : "+v"(lr));
-        const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)(bulk ? nc.st : nc.st - S4) * ROWB);
-        const uint32_t r0 = __builtin_amdgcn_readfirstlane((isB ? (uint32_t)nc.o.n0 : (uint32_t)nc.o.m0) * rowb);
-        const uint32_t c = (part & 1) ? c16o : c16e;
-        const bool ok = nc.st >= 0 && so + c < rowb;      // chunks past K / k read as zero
-        const uint32_t v = ok ? lr + c + r0 + (uint32_t)part * 8 * rowb : OOB;
-        if (bulk)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(isB ? rB : rA, (lds_ptr_t)dst, 16, v, so, 0, 0);
+    // does the cursor's half-stage open a scale window?
+    auto cursor_opens_window = [&]() { return ct < t_end && cst < H4 && (cst & 3) == 0; };
+    // copies c = 2 r + sl of the cursor's half-stage into its ring slot: row
+    // group 2 w + r of operand A (c < 4) or B, slice sl
+    // (fast: the cursor is known to be in the bulk part, whose resources are
+    // rA and rB)
+    auto copy_part = [&](int c, bool fast) {
+        const int op = c >> 2, r = (c >> 1) & 1, sl = c & 1;
+        uint8_t* dst = lds + (issued & (RING - 1)) * HS_BYTES + op * OP_BYTES + (2 * (2 * wave + r)) * kFragBlock;
+        const uint32_t so = op ? (r ? cB1 : cB0) : (r ? cA1 : cA0);
+        const __amdgpu_buffer_rsrc_t rs = fast ? (op ? rB : rA) : (op ? csB : csA);
+        if (sl)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst, 16, l16, so, kFragBlock, 0);
         else
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(isB ? rWO : rXO, (lds_ptr_t)dst, 16, v, so, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst, 16, l16, so, 0, 0);
     };
-
-    // All copies of stage nc at once (the very first stage), with the scale
-    // window it opens.
-    auto load_stage = [&](const NextCopy& nc, int b) {
-#pragma unroll
-        for (int gi = 0; gi < 8; ++gi) {
-            copy_part(nc, b, gi, false);
-            copy_part(nc, b, gi, true);
+    // after the 8 copies: the cursor moves to the next half-stage (past the
+    // last tile it stays put: its copies then re-read valid memory into a
+    // free slot)
+    auto advance_fast = [&]() {      // the cursor stays in the same tile's bulk part
+        ++issued;
+        ++cst;
+        cA0 += 2 * kFragBlock; cA1 += 2 * kFragBlock; cB0 += 2 * kFragBlock; cB1 += 2 * kFragBlock;
+    };
+    auto advance = [&]() {
+        ++issued;
+        if (ct >= t_end) return;
+        ++cst;
+        if (cst == H) {
+            cst = 0;
+            ct += nl;
+            if (ct >= t_end) return;
+            corg = tile_org(ct);
+            cursor_src();
+        } else if (cst == H4) {
+            cursor_src();
+        } else {
+            cA0 += 2 * kFragBlock; cA1 += 2 * kFragBlock; cB0 += 2 * kFragBlock; cB1 += 2 * kFragBlock;
         }
-        if (nc.st >= 0 && nc.st < S4 && (nc.st & 1) == 0) load_window(nc.o, nc.st >> 1);
     };
 
-    // End of a stage: this wave's copies into the other buffer have landed and
-    // its reads of the current buffer are done, then every wave arrives.  The
-    // scheduling barriers keep the stage's MFMAs above the wait, so they run
-    // while copies fly.  (__syncthreads would add a release fence and wait
-    // for the previous tile's stores as well.)
+    // End of a half-stage: this wave's copies of the next half-stage have
+    // landed (the 8 younger ones, of the half-stage after it, stay in
+    // flight; loads complete in order) and its reads of the current slot are
+    // done, then every wave arrives.  The scheduling barriers keep the MFMAs
+    // above the wait, so they run while copies fly.
     auto stage_sync = [&]() {
         __builtin_amdgcn_sched_barrier(0);
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // ---- one stage, in a fixed issue order of one slot per MFMA.  A stage
-    // is 4 sub-steps of 16 MFMAs (FP4 for a bulk stage, BF16 for an outlier
-    // stage); sub-step 3 is normally read before the stage barrier and
-    // multiplied after it, at the start of the next stage (DEFER_OUT), so
-    // the matrix cores have 16 MFMAs of work while the next stage's first
-    // fragments are read.  Slots:
-    //   0-15   the previous stage's sub-step 3 (kind DK: 0 none, 1 FP4, 2
-    //          BF16); slots 0-7 also read this stage's scale words and
-    //          sub-step 0's fragments (A0 B0 B1 B2 B3 A1 A2 A3, the order its
-    //          MFMAs need them), slot 12 shuffles the scales;
-    //   16-63  sub-steps 0, 1, 2; the next sub-step's fragments are read in
-    //          the first 8 slots of each;
-    //   64-79  sub-step 3 when it is not deferred (the last stage of a tile).
-    // The next stage's 16 copies go one per 2 slots from slot 2 to 32, the
-    // scale window it opens (if any) in slot 36: never two memory
-    // instructions back to back, so the address unit is shared evenly
-    // between the four waves.
-    u32x4 pf[2][2][4];                 // fragment sets [set][A/B][i]
-    uint32_t pA[4], pB[4];             // sub-step 3 scales of the previous stage
-    auto frag_read = [&](const uint8_t* base, int ss, int set, int q) {
-        const uint32_t co = (uint32_t)(((2 * ss + h) ^ sw) << 4);
+    // ---- this lane's scale codes of a bulk half-stage (from its window):
+    // byte 0 = slice 0, byte 1 = slice 1 (the MFMA's op_sel = slice)
+    auto read_scale = [&](const uint8_t* wsc, int q) {
+        if (q < 4) scA[q] = *reinterpret_cast<const uint16_t*>(wsc + scw_a + q * 32 * SCW_ROWB);
+        else       scB[q - 4] = *reinterpret_cast<const uint16_t*>(wsc + scw_b + (q - 4) * 32 * SCW_ROWB);
+    };
+
+    // ---- one half-stage in a fixed issue order of one slot per MFMA:
+    //   0-15   the previous half-stage's slice 1 (kind DK: 0 none, 1 FP4, 2
+    //          BF16); slots 0-7 also read slice 0's fragments (A0 B0 B1 B2 B3
+    //          A1 A2 A3, the order its MFMAs need them) and the half-stage's
+    //          scale codes;
+    //   16-31  slice 0; slots 16-23 read slice 1's fragments;
+    //   32-47  slice 1 when it is not deferred (the last bulk half-stage of a
+    //          tile, and every outlier half-stage).
+    // Slot 1 opens the cursor's scale window (if it starts one), slots 2,
+    // 4, .., 16 issue its 8 copies: never two memory instructions back to
+    // back, so the address unit is shared evenly between the four waves.
+    u32x4 pf[2][2][4];                 // fragment sets [set = slice][A/B][i]
+    auto frag_read = [&](const uint8_t* base, int sl, int q) {
         const bool isA = q == 0 || q >= 5;
         const int r = q == 0 ? 0 : (q < 5 ? q - 1 : q - 4);
-        if (isA) pf[set][0][r] = *reinterpret_cast<const u32x4*>(base + fa[r] + co);
-        else     pf[set][1][r] = *reinterpret_cast<const u32x4*>(base + fb[r] + co);
+        const uint32_t off = (uint32_t)(r * HS_SL * kFragBlock + sl * kFragBlock);
+        if (isA) pf[sl][0][r] = *reinterpret_cast<const u32x4*>(base + fa0 + off);
+        else     pf[sl][1][r] = *reinterpret_cast<const u32x4*>(base + fb0 + off);
     };
-    auto run_stage = [&](auto CUR_BULK, auto DK, auto DEFER_OUT, const NextCopy& nc, int st, int b) {
+    // FAST: the cursor copies a bulk half-stage of the current tile and
+    // stays in its bulk part (no transition in the advance).
+    auto run_hs = [&](auto CUR_BULK, auto DK, auto DEFER_OUT, auto FAST, int hs, int slot) {
         constexpr bool cb = decltype(CUR_BULK)::value;
         constexpr int dk = decltype(DK)::value;
         constexpr bool dout = decltype(DEFER_OUT)::value;
-        const uint8_t* base = lds + b * STAGE_BYTES;
+        constexpr bool fast = decltype(FAST)::value;
+        const uint8_t* base = lds + slot * HS_BYTES;
         const uint8_t* wsc = nullptr;
-        if constexpr (cb) wsc = window_of(st);
-        const bool opens_window = nc.st >= 0 && nc.st < S4 && (nc.st & 1) == 0;
-        static_for<80>([&](auto QC) {
+        if constexpr (cb) {
+            if ((hs & 3) == 0) {
+                wcur = wnext;
+                wnext = wnext == SCW_SLOTS - 1 ? 0 : wnext + 1;
+            }
+            wsc = lds + SCW_OFF + wcur * SCW_BYTES + 2 * (hs & 3);
+        }
+        const bool opens_window = fast ? (cst & 3) == 0 : cursor_opens_window();
+        static_for<48>([&](auto QC) {
             constexpr int q = decltype(QC)::value;
-            if constexpr (q < 64 || !dout) {
+            if constexpr (q < 32 || !dout) {
                 if constexpr (q < 16) {
                     constexpr int i = q >> 2, j = q & 3;
                     if constexpr (dk == 1)
-                        acc[i][j] = mfma_fp4_op<2>(pf[1][1][j], pf[1][0][i], pB[j], pA[i], acc[i][j]);
+                        acc[i][j] = mfma_fp4_op<1>(pf[1][1][j], pf[1][0][i], pB[j], pA[i], acc[i][j]);
                     else if constexpr (dk == 2)
                         acc[i][j] = mfma_bf16_v(pf[1][1][j], pf[1][0][i], acc[i][j]);
                 } else {
-                    constexpr int ss = (q - 16) >> 4, r = (q - 16) & 15, i = r >> 2, j = r & 3, set = ss & 1;
+                    constexpr int sl = (q - 16) >> 4, r = (q - 16) & 15, i = r >> 2, j = r & 3;
                     if constexpr (cb)
-                        acc[i][j] = mfma_fp4_op<(ss & 1) ? 2 : 0>(pf[set][1][j], pf[set][0][i], scB[j][ss >> 1],
-                                                                  scA[i][ss >> 1], acc[i][j]);
+                        acc[i][j] = mfma_fp4_op<sl>(pf[sl][1][j], pf[sl][0][i], scB[j], scA[i], acc[i][j]);
                     else
-                        acc[i][j] = mfma_bf16_v(pf[set][1][j], pf[set][0][i], acc[i][j]);
+                        acc[i][j] = mfma_bf16_v(pf[sl][1][j], pf[sl][0][i], acc[i][j]);
                 }
                 if constexpr (q < 8) {
-                    if constexpr (cb) read_scales_i(wsc, q);
-                    frag_read(base, 0, 0, q);
+                    if constexpr (cb) read_scale(wsc, q);
+                    frag_read(base, 0, q);
                 }
-                if constexpr (cb && q == 12) take_scales();
-                if constexpr (q >= 16 && q < 24) frag_read(base, 1, 1, q - 16);
-                if constexpr (q >= 32 && q < 40) frag_read(base, 2, 0, q - 32);
-                if constexpr (q >= 48 && q < 56) frag_read(base, 3, 1, q - 48);
-                if constexpr (q >= 2 && q <= 32 && q % 2 == 0) copy_part(nc, b ^ 1, (q - 2) >> 2, ((q - 2) & 2) != 0);
-                if constexpr (q == 36) {
-                    if (opens_window) load_window(nc.o, nc.st >> 1);
+                if constexpr (q >= 16 && q < 24) frag_read(base, 1, q - 16);
+                if constexpr (q == 1) {
+                    if (opens_window) load_window(corg, cst >> 2);
                 }
+                if constexpr (q >= 2 && q <= 16 && q % 2 == 0) copy_part((q - 2) >> 1, fast);
                 __builtin_amdgcn_sched_barrier(0);
             }
         });
+        if constexpr (fast)
+            advance_fast();
+        else
+            advance();
         if constexpr (cb && dout) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) { pA[i] = scA[i][1]; pB[i] = scB[i][1]; }
+            for (int i = 0; i < 4; ++i) { pA[i] = scA[i]; pB[i] = scB[i]; }
         }
         stage_sync();
     };
@@ -386,11 +404,11 @@ dual_gemm_tiled(GemmArgs g) {
     // lane (l32, h), register 4 q + e holds output row 32 i + l32 and output
     // column 32 j + 8 q + 4 h + e of this wave's quarter -- four consecutive
     // columns per register group.
-    auto epilogue = [&](const TileOrg& o, uint8_t* stagebuf) {
+    auto epilogue = [&](const TileOrg& o, uint8_t* wbuf) {
         if constexpr (sizeof(OutT) == 2) {
             // bf16: round pairs with the hardware converter (nearest even).
             // Each wave stages its own 128x128 quarter through its own 16 KB
-            // of the free buffer, 64 rows x 256 B per pass, and writes the
+            // of a free ring slot (wbuf), 64 rows x 256 B per pass, and writes the
             // rows back out with 16-byte streaming stores (four 256-byte row
             // pieces per instruction).  No wave reads another wave's staging,
             // so a pass needs no barrier: one wave's LDS accesses are
@@ -404,7 +422,6 @@ dual_gemm_tiled(GemmArgs g) {
             const uint32_t nrec = (uint32_t)(rows_left < TBM ? rows_left : TBM) * rowY;
             const __amdgpu_buffer_rsrc_t rY =
                 make_rsrc(static_cast<uint16_t*>(g.Y) + o.m0 * (int64_t)N, (uint64_t)nrec);
-            uint8_t* wbuf = stagebuf + wave * 16384;
             // Lane-dependent values come from an opaque copy of the thread
             // index, so they are formed here, once per tile, instead of being
             // hoisted out of the tile loop and held (or spilled) across it.
@@ -453,7 +470,7 @@ dual_gemm_tiled(GemmArgs g) {
                 __builtin_amdgcn_sched_barrier(0);
             }
             // every wave's staging reads are done (their data fed the stores
-            // above) before the next stage's copies reuse the buffer
+            // above) before the next copies reuse the slots
             __builtin_amdgcn_s_barrier();
         } else {
             // fp32: four consecutive columns per register group -> 16-byte stores
@@ -476,14 +493,19 @@ dual_gemm_tiled(GemmArgs g) {
         }
     };
 
-    // ---- prologue: first stage of the first tile
-    TileOrg cur = tile_org(t);
-    int tn = t + nl;
-    load_stage(NextCopy{cur, 0}, 0);
+
+    // ---- prologue: the first two half-stages (and the first scale window)
+    for (int p = 0; p < LEAD; ++p) {
+        if (cursor_opens_window()) load_window(corg, cst >> 2);
+#pragma unroll
+        for (int c = 0; c < NCOPY; ++c) copy_part(c, false);
+        advance();
+    }
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
     __syncthreads();
-    int buf = 0;
+    TileOrg cur = tile_org(t);
+    int gs = 0;        // half-stages computed so far (the current one's slot: gs % 4)
 
     using T_ = std::true_type;
     using F_ = std::false_type;
@@ -494,41 +516,41 @@ dual_gemm_tiled(GemmArgs g) {
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
-        const bool has_next = tn < t_end;
-        const TileOrg nxt = tile_org(has_next ? tn : t);
-        // the stage after st: the next one of this tile, the first one of the
-        // next tile, or none
-        auto next_of = [&](int st) {
-            NextCopy nc{cur, st + 1};
-            if (st + 1 == S) nc = has_next ? NextCopy{nxt, 0} : NextCopy{cur, -1};
-            return nc;
-        };
-        // bulk stages, each leaving its sub-step 3 to the next
-        run_stage(T_{}, D0{}, T_{}, next_of(0), 0, buf);
-        buf ^= 1;
-        int st = 1;
-        for (; st < S4; ++st) {
-            run_stage(T_{}, D1{}, T_{}, next_of(st), st, buf);
-            buf ^= 1;
+        // bulk half-stages, each leaving its slice 1 to the next.  While hs
+        // + 3 < H4 the copies (two half-stages ahead) stay in this tile's
+        // bulk part: the fast cursor step.
+        run_hs(T_{}, D0{}, T_{}, F_{}, 0, gs & (RING - 1));
+        ++gs;
+        int hs = 1;
+        for (; hs + 3 < H4; ++hs) {
+            run_hs(T_{}, D1{}, T_{}, T_{}, hs, gs & (RING - 1));
+            ++gs;
         }
-        // the last bulk stage's sub-step 3
+        for (; hs < H4; ++hs) {
+            run_hs(T_{}, D1{}, T_{}, F_{}, hs, gs & (RING - 1));
+            ++gs;
+        }
+        // the last bulk half-stage's slice 1
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                acc[i][j] = mfma_fp4_op<2>(pf[1][1][j], pf[1][0][i], pB[j], pA[i], acc[i][j]);
-        // outlier stages, each complete in itself
-        for (; st < S; ++st) {
-            run_stage(F_{}, D0{}, F_{}, next_of(st), st, buf);
-            buf ^= 1;
+                acc[i][j] = mfma_fp4_op<1>(pf[1][1][j], pf[1][0][i], pB[j], pA[i], acc[i][j]);
+        // outlier half-stages, each complete in itself
+        for (; hs < H; ++hs) {
+            run_hs(F_{}, D0{}, F_{}, F_{}, hs, gs & (RING - 1));
+            ++gs;
         }
-        // buffer buf^1 held the last stage and is free; buf holds the next
-        // tile's first stage (if any)
-        epilogue(cur, lds + (buf ^ 1) * STAGE_BYTES);
-        if (!has_next) break;
-        t = tn;
-        tn += nl;
-        cur = nxt;
+        // the slots of the last two half-stages, (gs - 1) % 4 and (gs - 2) % 4,
+        // hold no pending copy: waves 0, 1 stage their output through the
+        // first, waves 2, 3 through the second
+        {
+            const int fs = (wave < 2 ? gs - 1 : gs - 2) & (RING - 1);
+            epilogue(cur, lds + fs * HS_BYTES + (wave & 1) * (HS_BYTES / 2));
+        }
+        t += nl;
+        if (t >= t_end) break;
+        cur = tile_org(t);
     }
 }
 

@@ -250,13 +250,18 @@ __global__ void __launch_bounds__(256) fold_pack_kernel(const void* __restrict__
         for (int i = 0; i < 8; ++i) f[i] = __fmul_rn(sv[i], x[i]);
     };
     // outlier channels of row n to WO, then masked to +0 in f; returns the
-    // lane's amax of the masked values
-    // WO rows are kp = xo_cols(k) values apart; the workgroup of channels
-    // 0..511 writes each row's pad columns k .. kp-1 (+0), one per lane
-    const int kp = xo_cols(k);
-    const bool pad_lane = blockIdx.x == 0 && lane < kp - k;
+    // lane's amax of the masked values.  Wq and WO are stored in fragment
+    // order (frag_offset); N % 32 == 0, so there are no pad rows.  The
+    // workgroup of channels 0..511 writes each WO row's pad columns k ..
+    // 16 * nso - 1 (+0), one per lane.
+    const int64_t ns4 = frag_slices(K / 2), nso = frag_slices(2 * (int64_t)k);
+    uint8_t* const WOb = reinterpret_cast<uint8_t*>(WO);
+    const bool pad_lane = blockIdx.x == 0 && lane < 16 * nso - k;
+    auto wo_store = [&](int64_t n, int i, uint16_t v) {
+        *reinterpret_cast<uint16_t*>(WOb + frag_offset(n, 2 * (int64_t)i, nso)) = v;
+    };
     auto extract = [&](int64_t n, float (&f)[8]) {
-        if (pad_lane && n < N) WO[n * kp + k + lane] = 0;
+        if (pad_lane && n < N) wo_store(n, k + lane, 0);
         if (omask && n < N) {
             for (uint32_t m = omask; m; m &= m - 1) {
                 const int i = __builtin_ctz(m);
@@ -266,7 +271,7 @@ __global__ void __launch_bounds__(256) fold_pack_kernel(const void* __restrict__
                 int pi = pv[0];
 #pragma unroll
                 for (int t = 1; t < 8; ++t) pi = i == t ? pv[t] : pi;
-                WO[n * kp + pi] = (uint16_t)f32_to_bf16_rne(fi);
+                wo_store(n, pi, (uint16_t)f32_to_bf16_rne(fi));
             }
         }
         float amax = 0.0f;
@@ -277,9 +282,10 @@ __global__ void __launch_bounds__(256) fold_pack_kernel(const void* __restrict__
         }
         return amax;
     };
-    // the nibbles of row n (lanes inside K, rows inside N) and, from one lane
-    // per quad, the block's scale code (every lane of rows < Np: past K or N
-    // the code 0 of an all-zero block)
+    // the nibbles of row n (rows inside N; lanes inside K, and past K up to
+    // the last 32-byte slice, whose pad half gets the zero codes) and, from
+    // one lane per quad, the block's scale code (every lane of rows < Np: past
+    // K or N the code 0 of an all-zero block)
     auto encode_store = [&](int64_t n, const float (&f)[8], uint32_t c) {
         const float scale = e8m0_to_f32(c);
         uint32_t word = 0;
@@ -287,7 +293,7 @@ __global__ void __launch_bounds__(256) fold_pack_kernel(const void* __restrict__
         MG_CVT_FP4X2(word, f[2], f[3], scale, 1);
         MG_CVT_FP4X2(word, f[4], f[5], scale, 2);
         MG_CVT_FP4X2(word, f[6], f[7], scale, 3);
-        if (valid && n < N) *reinterpret_cast<uint32_t*>(Wq + n * (K / 2) + j0 / 2) = word;
+        if (j0 < 64 * ns4 && n < N) *reinterpret_cast<uint32_t*>(Wq + frag_offset(n, j0 / 2, ns4)) = word;
         if ((lane & 3) == 0) Ws[sc_offset(n, j0 / 32, nwin)] = (uint8_t)(valid ? c : 0u);   // a short stripe's pads: 0
     };
 

@@ -17,10 +17,15 @@
 // RN(1/s) and outlier masks of a lane's 8 channels stay in registers for all
 // of its rows.  Rows are read and written through buffer resources built per
 // row in scalar registers, so channels past K need no per-lane bounds code.
-// The codes As[m][b] are stored in scale windows of 256 rows x 16 blocks
-// (sc_offset): a workgroup's 512 channels are one window, so a row's 16
-// codes are 16 contiguous bytes; the rows run on to the end of the last
-// 256-row group, whose pad rows (and the blocks past K) get code 0.
+// Aq and XO are stored in the GEMM's fragment order (frag_offset): a row's
+// bytes sit in 16-byte pieces, one per 32x32-byte block, at an offset that
+// splits into a per-row part (scalar) and a per-lane part (constant), so the
+// per-row resource covers exactly the row's pieces.  Rows up to the next
+// multiple of 32 and the pad half of a last 32-byte slice (K % 64 == 32) get
+// zero codes.  The codes As[m][b] are stored in scale windows of 256 rows x
+// 16 blocks (sc_offset): a workgroup's 512 channels are one window, so a
+// row's 16 codes are 16 contiguous bytes; the rows run on to the end of the
+// last 256-row group, whose pad rows (and the blocks past K) get code 0.
 //
 // With GELU, X is the previous projection's bf16 output and the quantized
 // input is h = gelu_bf16x2 of X (the FFN block's hidden activation), computed
@@ -43,7 +48,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
-constexpr int WAVES_PER_CU = 32;  // launch size: about this many waves per CU
+constexpr int kStgRow = 272;      // LDS staging row: 256 bytes of codes + 16 pad
 
 // |x| bit patterns of bf16 2^-100 and 2^100 (biased exponents 27 and 227)
 constexpr unsigned short kBf16Lo = 0x0D80, kBf16Hi = 0x7180;
@@ -87,16 +92,22 @@ __device__ __forceinline__ uint32_t encode8(const float (&q)[8], uint32_t& c) {
     return word;
 }
 
-// encode8, then the packed nibbles (lanes inside K, rows inside M) and, from
-// one lane per quad, the block's scale byte into the row's 16 bytes of its
-// scale window (every lane: past K or M the code of a zero block).
-__device__ __forceinline__ void encode_store(const float (&q)[8], int lane, bool store_q, uint8_t* aq_row,
-                                             uint8_t* as_win_row, int j0) {
+// encode8, then the packed nibbles (to aq when non-null) and, from one lane
+// per quad, the block's scale byte into the row's 16 bytes of its scale
+// window (every lane: past K or M the code of a zero block).
+__device__ __forceinline__ void encode_store(const float (&q)[8], int lane, uint8_t* aq, uint8_t* as_win_row) {
     uint32_t c;
     const uint32_t word = encode8(q, c);
-    if (store_q) *reinterpret_cast<uint32_t*>(aq_row + j0 / 2) = word;
-    if ((lane & 3) == 0) as_win_row[lane >> 2] = (uint8_t)c;
+    if (aq) *reinterpret_cast<uint32_t*>(aq) = word;
+    if ((lane & 3) == 0) as_win_row[sc_pos(lane >> 2)] = (uint8_t)c;
 }
+
+// Per-lane parts of frag_offset (the row part is (r / 32) * ns * 1024 +
+// (r % 32) * 16): byte b of a row sits at (b / 32) * 1024 + ((b / 16) % 2) *
+// 512 + b % 16 past it.  Aq: the 4 bytes of channels j0 .. j0 + 7 (b = j0 / 2);
+// XO: outlier column i (b = 2 i).
+__device__ __forceinline__ uint32_t frag_lane_off(uint32_t b) { return (b >> 5) * 1024u + ((b >> 4) & 1u) * 512u + (b & 15u); }
+__device__ __forceinline__ int64_t frag_row_off(int64_t r, int64_t ns) { return (r >> 5) * ns * kFragBlock + ((r & 31) << 4); }
 
 template <bool GELU, bool STATS>
 __global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restrict__ X, int64_t M, int32_t K,
@@ -118,6 +129,9 @@ __global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restr
     __shared__ float t_s[512], t_r[512];
     __shared__ int t_p[512];
     __shared__ uint32_t t_m[512];    // STATS: the workgroup's per-channel max |x| (bf16 bits)
+    // Aq codes of each wave's 8 rows (rows of 256 bytes, padded to 272 so
+    // that the row writes are conflict-free)
+    __shared__ __attribute__((aligned(16))) uint8_t stg[kWaves * 8 * kStgRow];
     for (int t = threadIdx.x; t < 512; t += 256) {
         const int j = blockIdx.x * 512 + t;
         t_s[t] = j < K ? s[j] : 1.0f;
@@ -126,6 +140,7 @@ __global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restr
         t_m[t] = 0;
     }
     __syncthreads();
+    uint8_t* const stgw = stg + wave * 8 * kStgRow;   // this wave's staging rows
     u16x2 mx[4] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};   // STATS: running max of the lane's |x| bit patterns
     // the lane's 8 channels: three pairs of 16-byte loads (j0 is a multiple of 8)
     float sv[8] = {1, 1, 1, 1, 1, 1, 1, 1}, rv[8] = {1, 1, 1, 1, 1, 1, 1, 1};
@@ -171,20 +186,22 @@ __global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restr
     // K read zeros and drop their stores by the hardware range check, and so
     // do the lanes that store no scale byte or no outlier value (offset
     // kNoStore).  The workgroup's 512 channels are one scale window: a row's
-    // 16 scale bytes are contiguous, lane 4 i storing byte i (past K: the
-    // code 0 of its all-zero block).
+    // 16 scale bytes are contiguous, lane 4 i storing block i's code at byte
+    // sc_pos(i) (past K: the code 0 of its all-zero block).
     constexpr uint32_t kNoStore = 0x40000000u;
-    const uint32_t offX = 2u * (uint32_t)j0, offAq = (uint32_t)j0 / 2u;
-    const uint32_t offAs = (lane & 3) == 0 ? (uint32_t)(lane >> 2) : kNoStore;
-    const uint32_t offXO = omask ? 2u * (uint32_t)op0 : kNoStore;
+    const uint32_t offX = 2u * (uint32_t)j0;
+    const uint32_t offAs = (lane & 3) == 0 ? (uint32_t)sc_pos(lane >> 2) : kNoStore;
+    const uint32_t offXO = omask ? frag_lane_off(2u * (uint32_t)op0) : kNoStore;
     const bool wave_o = __builtin_amdgcn_ballot_w64(omask != 0) != 0;
     const bool wave_rest = __builtin_amdgcn_ballot_w64(omask_rest != 0) != 0;
-    // XO rows are kp = xo_cols(k) values apart; the workgroup of channels
-    // 0..511 writes the pad columns k .. kp-1 (+0), one per lane
-    const int kp = xo_cols(k);
-    const uint32_t rowX = 2u * (uint32_t)K, rowAq = (uint32_t)K / 2u, rowXO = 2u * (uint32_t)kp;
-    const bool pad_wg = blockIdx.x == 0 && kp > k;
-    const uint32_t offPad = lane < kp - k ? 2u * (uint32_t)(k + lane) : kNoStore;
+    // Aq rows of K/2 bytes in ns4 slices, XO rows of 2k bytes in nso slices;
+    // the workgroup of channels 0..511 writes XO's pad columns k .. 16 nso - 1
+    // (+0), one per lane
+    const int64_t ns4 = frag_slices(K / 2), nso = frag_slices(2 * (int64_t)k);
+    const int kp16 = 16 * (int)nso;
+    const uint32_t rowX = 2u * (uint32_t)K;
+    const bool pad_wg = blockIdx.x == 0 && kp16 > k;
+    const uint32_t offPad = lane < kp16 - k ? frag_lane_off(2u * (uint32_t)(k + lane)) : kNoStore;
 
     auto rsrc = [](const void* p, uint32_t bytes) {
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
@@ -194,10 +211,16 @@ __global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restr
                                                                                 2));   // nt
     };
 
-    // one row: w its 8 bf16 per lane, pq/ps/po its Aq row, its 16 bytes of
-    // the As window and its XO row; live: a row of X (else a pad row of the
-    // last 256-row scale group, whose Aq and XO stores are dropped)
-    auto process_row = [&](u32x4 w, uint8_t* pq, uint8_t* ps, uint16_t* po, bool live) {
+    // one row m: w its 8 bf16 per lane, ps its 16 bytes of the As window;
+    // live: a row below M rounded up to 32 (rows of X, and pad rows whose
+    // zero codes the fragment order holds); else a pad row of the last
+    // 256-row scale group, of which only the scale codes are written.  The
+    // row's resources start at its fragment-order row part and cover its
+    // pieces: ns * 1024 - 16 (m % 32) bytes.
+    auto process_row = [&](u32x4 w, int64_t m, uint8_t* ps, bool live) {
+        const uint32_t rsub = (uint32_t)(m & 31) << 4;
+        uint8_t* const po = reinterpret_cast<uint8_t*>(XO) + frag_row_off(m, nso);
+        const uint32_t rowXO = nso ? (uint32_t)nso * 1024u - rsub : 0u;    // k == 0: no XO
         if constexpr (GELU) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) w[i] = gelu_bf16x2(w[i]);
@@ -239,46 +262,74 @@ __global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restr
                     const float xi = __uint_as_float((i & 1) ? (wi & 0xFFFF0000u) : (wi << 16));
                     const float si = t_s[jl];
                     const float qi = fast ? div_fast(xi, si, t_r[jl]) : __fdiv_rn(xi, si);
-                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_rne(qi), rxo, 2u * (uint32_t)t_p[jl],
-                                                          0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_rne(qi), rxo,
+                                                          frag_lane_off(2u * (uint32_t)t_p[jl]), 0, 0);
                 }
             }
         }
         uint32_t c;
         const uint32_t word = encode8(q, c);
-        __builtin_amdgcn_raw_buffer_store_b32(word, rsrc(pq, live ? rowAq : 0u), offAq, 0, 0);
+        *reinterpret_cast<uint32_t*>(stgw + (m & 7) * kStgRow + 4 * lane) = word;
         if (pad_wg) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)0, rsrc(po, live ? rowXO : 0u), offPad, 0, 0);
         if ((lane & 3) == 0)
             __builtin_amdgcn_raw_buffer_store_b8((uint8_t)c, rsrc(ps, (uint32_t)kScBlocks), offAs, 0, 0);
     };
 
-    // Rows r0, r0 + rstride, ...: the next row's load is in flight while the
-    // current one is processed.  Row addresses advance by a fixed stride
-    // (scalar adds).  The rows run on to the end of the last 256-row scale
-    // group, so its pad rows get their zero codes.
-    // The wave's row counts n (with pad rows) and nv (rows of X) are 32-bit
-    // scalars (64-bit scalar compares do not exist on this architecture).
-    const int64_t rstride = (int64_t)gridDim.y * kWaves;
-    const int64_t r0 = (int64_t)blockIdx.y * kWaves + wave;
+    // 32-row groups G = blockIdx.y, blockIdx.y + gridDim.y, ...; wave w takes
+    // rows 32 G + 8 w .. 32 G + 8 w + 7, loaded together (8 KB per wave) while
+    // the wave's previous group is processed, row by row.  The groups run on to the end of the
+    // last 256-row scale group, so its pad rows get their zero codes.  The
+    // wave's 8 rows fill whole 128-byte lines of the fragment blocks (8 rows x
+    // 16 bytes of one slice half), so it stages its Aq codes in its own LDS
+    // rows and stores them as 16 full lines (two 1 KB store instructions;
+    // lane L of store t takes row L % 8 of line 8 t + L / 8 = (slice, half)).
+    // No wave reads another's staging, so no barrier is needed.  Groups past
+    // the row groups of Aq (pad rows of the scale group only) store nothing
+    // but scale codes.
     const int64_t Mp = (M + kScRows - 1) / kScRows * kScRows;
-    const int n = r0 < Mp ? (int)((Mp - 1 - r0) / rstride) + 1 : 0;
-    const int nv = r0 < M ? (int)((M - 1 - r0) / rstride) + 1 : 0;
-    const int64_t dX = rstride * K, dQ = rstride * (K / 2), dO = rstride * kp;
+    const int ngr = (int)(Mp / 32);                                       // groups with scale rows
+    const int GA = (int)((M + 31) / 32);                                  // groups with Aq / XO pieces
+    const int gstride = (int)gridDim.y;
     const int64_t win_stride = sc_nwin(K) * kScWinBytes;     // bytes between 256-row groups of As
     static_assert(kScRows == 256, "row group = m >> 8");
-    const uint16_t* px = X + r0 * K;
-    uint8_t* pq = Aq + r0 * (K / 2);
     uint8_t* const asw = As + (int64_t)blockIdx.x * kScWinBytes;
-    uint16_t* po = XO + r0 * kp;
-    int64_t m = r0;
-    u32x4 a = load_row(px, nv > 0);
-    px += dX;
-    for (int i = 0; i < n; ++i) {
-        const u32x4 b = load_row(px, i + 1 < nv);
-        px += dX;
-        process_row(a, pq, asw + (m >> 8) * win_stride + (m & 255) * kScBlocks, po, i < nv);   // 256-row groups
-        pq += dQ; po += dO; m += rstride;
-        a = b;
+    // the store lanes' staged pieces and their offsets inside the row group's blocks
+    uint32_t srd[2], sof[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int line = 8 * t + (lane >> 3), sl = line >> 1, hf = line & 1, rr = lane & 7;
+        srd[t] = (uint32_t)(rr * kStgRow + sl * 32 + hf * 16);
+        sof[t] = (uint32_t)((blockIdx.x * 8 + sl) * 1024 + 16 * (wave * 8 + rr + 32 * hf));
+    }
+    // the next group's 8 rows are loaded before the current group is processed
+    auto load8 = [&](int g, u32x4 (&xr)[8]) {
+        const int64_t m0 = (int64_t)g * 32 + wave * 8;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) xr[r] = load_row(X + (m0 + r) * K, g < ngr && m0 + r < M);
+    };
+    u32x4 xn[8];
+    load8((int)blockIdx.y, xn);
+    for (int G = (int)blockIdx.y; G < ngr; G += gstride) {
+        const int64_t m0 = (int64_t)G * 32 + wave * 8;
+        u32x4 xr[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) xr[r] = xn[r];
+        if (G + gstride < ngr) load8(G + gstride, xn);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int64_t m = m0 + r;
+            process_row(xr[r], m, asw + (m >> 8) * win_stride + (m & 255) * kScBlocks, G < GA);   // 256-row groups
+        }
+        if (G < GA) {
+            // the row group's blocks from a 64-bit base (Aq may exceed 4 GiB);
+            // slices past the row's (ns4) fall outside the range and are dropped
+            const __amdgpu_buffer_rsrc_t rg = rsrc(Aq + (int64_t)G * ns4 * 1024, (uint32_t)ns4 * 1024u);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(stgw + srd[t]);
+                __builtin_amdgcn_raw_buffer_store_b128(v, rg, sof[t], 0, 0);
+            }
+        }
     }
     if constexpr (STATS) {
         // the magnitudes' bit patterns order like the magnitudes: integer max, in LDS across the
@@ -317,9 +368,14 @@ __global__ void __launch_bounds__(256) quant_f32_kernel(const float* __restrict_
     const int64_t rstride = (int64_t)gridDim.y * kWaves;
     const int64_t Mp = (M + kScRows - 1) / kScRows * kScRows;   // through the last scale group's pad rows
     const int64_t nwin = sc_nwin(K);
-    const int kp = xo_cols(k);                                   // XO row stride; pads written below
+    // Aq and XO in fragment order (rows through M rounded up to 32 get zero
+    // codes; lanes past K up to the last 32-byte slice of Aq store zero codes)
+    const int64_t ns4 = frag_slices(K / 2), nso = frag_slices(2 * (int64_t)k);
+    const int64_t M32 = (M + 31) / 32 * 32;
+    const int kp16 = 16 * (int)nso;
+    uint8_t* const XOb = reinterpret_cast<uint8_t*>(XO);
     for (int64_t r = (int64_t)blockIdx.y * kWaves + wave; r < Mp; r += rstride) {
-        const bool live = r < M;
+        const bool live = r < M, piece = r < M32;
         float q[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -327,13 +383,16 @@ __global__ void __launch_bounds__(256) quant_f32_kernel(const float* __restrict_
             mx[i] = fmaxf(mx[i], __builtin_fabsf(x));
             q[i] = __fdiv_rn(x, sv[i]);
             if (pv[i] >= 0) {
-                if (live) XO[r * kp + pv[i]] = (uint16_t)f32_to_bf16_rne(q[i]);
+                if (piece)
+                    *reinterpret_cast<uint16_t*>(XOb + frag_offset(r, 2 * (int64_t)pv[i], nso)) =
+                        (uint16_t)f32_to_bf16_rne(q[i]);
                 q[i] = 0.0f;
             }
         }
-        if (live && blockIdx.x == 0 && lane < kp - k) XO[r * kp + k + lane] = 0;
-        encode_store(q, lane, valid && live, Aq + r * (K / 2),
-                     As + sc_offset(r, (int32_t)blockIdx.x * kScBlocks, nwin), j0);
+        if (piece && blockIdx.x == 0 && lane < kp16 - k)
+            *reinterpret_cast<uint16_t*>(XOb + frag_offset(r, 2 * (int64_t)(k + lane), nso)) = 0;
+        encode_store(q, lane, piece && j0 < 64 * ns4 ? Aq + frag_offset(r, j0 / 2, ns4) : nullptr,
+                     As + sc_offset(r, (int32_t)blockIdx.x * kScBlocks, nwin));
     }
     if (amax != nullptr && valid) {
 #pragma unroll
@@ -343,38 +402,52 @@ __global__ void __launch_bounds__(256) quant_f32_kernel(const float* __restrict_
 
 }  // namespace
 
+// Workgroups of kernel `kern` that fit on one CU (registers, LDS), looked
+// up once per device and kernel.
+static int blocks_per_cu(const void* kern) {
+    struct Entry { const void* k; int dev; int n; };
+    static thread_local Entry cache[8] = {};
+    static thread_local int used = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 1;
+    for (int i = 0; i < used; ++i)
+        if (cache[i].k == kern && cache[i].dev == dev) return cache[i].n;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, 256, 0) != hipSuccess || n < 1) n = 1;
+    if (used < 8) cache[used++] = Entry{kern, dev, n};
+    return n;
+}
+
+template <typename F, typename... A>
+static void launch_rows(F* kern, int64_t M, int64_t gx, hipStream_t st, A... args) {
+    // one resident round of workgroups; each takes 32-row groups through the
+    // last 256-row scale group
+    int64_t gy = (M + kScRows - 1) / kScRows * (kScRows / 32);
+    int64_t cap = (int64_t)device_cu_count() * blocks_per_cu(reinterpret_cast<const void*>(kern)) / gx;
+    if (cap < 1) cap = 1;
+    if (gy > cap) gy = cap;
+    if (gy > 65535) gy = 65535;
+    hipLaunchKernelGGL(kern, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, st, args...);
+}
+
 hipError_t launch_quant(const void* X, int32_t dtype, int64_t M, int32_t K, int32_t k,
                         const float* s, const float* rcp, const int32_t* pos, uint8_t* Aq,
                         uint8_t* As, uint16_t* XO, hipStream_t st, bool gelu, float* amax) {
     if (M <= 0) return hipSuccess;
     const int64_t gx = ((int64_t)K / 8 + 63) / 64;
-    // about WAVES_PER_CU waves per CU, each wave at least one row
-    int64_t gy = (M + kWaves - 1) / kWaves;
-    // the statistics variant holds 7 waves per SIMD (more registers), the others 8
-    const int waves_per_cu = amax ? 28 : WAVES_PER_CU;
-    int64_t cap = (int64_t)device_cu_count() * (waves_per_cu / kWaves) / gx;
-    if (cap < 1) cap = 1;
-    if (gy > cap) gy = cap;
-    if (gy > 65535) gy = 65535;
-    dim3 grid((unsigned)gx, (unsigned)gy);
     uint32_t* am = reinterpret_cast<uint32_t*>(amax);   // non-negative f32 maxima: integer max of the bits
     const uint16_t* Xb = static_cast<const uint16_t*>(X);
     if (dtype == MG_BF16) {
         if (gelu && am)
-            hipLaunchKernelGGL((quant_bf16_kernel<true, true>), grid, dim3(256), 0, st, Xb, M, K, k, s, rcp, pos, Aq, As,
-                               XO, am);
+            launch_rows(quant_bf16_kernel<true, true>, M, gx, st, Xb, M, K, k, s, rcp, pos, Aq, As, XO, am);
         else if (gelu)
-            hipLaunchKernelGGL((quant_bf16_kernel<true, false>), grid, dim3(256), 0, st, Xb, M, K, k, s, rcp, pos, Aq,
-                               As, XO, am);
+            launch_rows(quant_bf16_kernel<true, false>, M, gx, st, Xb, M, K, k, s, rcp, pos, Aq, As, XO, am);
         else if (am)
-            hipLaunchKernelGGL((quant_bf16_kernel<false, true>), grid, dim3(256), 0, st, Xb, M, K, k, s, rcp, pos, Aq,
-                               As, XO, am);
+            launch_rows(quant_bf16_kernel<false, true>, M, gx, st, Xb, M, K, k, s, rcp, pos, Aq, As, XO, am);
         else
-            hipLaunchKernelGGL((quant_bf16_kernel<false, false>), grid, dim3(256), 0, st, Xb, M, K, k, s, rcp, pos, Aq,
-                               As, XO, am);
+            launch_rows(quant_bf16_kernel<false, false>, M, gx, st, Xb, M, K, k, s, rcp, pos, Aq, As, XO, am);
     } else {
-        hipLaunchKernelGGL(quant_f32_kernel, grid, dim3(256), 0, st, static_cast<const float*>(X), M, K, k, s, pos,
-                           Aq, As, XO, am);
+        launch_rows(quant_f32_kernel, M, gx, st, static_cast<const float*>(X), M, K, k, s, pos, Aq, As, XO, am);
     }
     return hipGetLastError();
 }

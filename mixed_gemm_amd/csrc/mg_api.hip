@@ -74,10 +74,10 @@ int check_plan(const mg_plan* p, bool need_w) {
 
 // The GEMM addresses each operand with 32-bit offsets below 3 GiB.
 int check_gemm_size(const mg_plan* p, int64_t M) {
-    const uint64_t lim = 0xC0000000ull;
-    const uint64_t K = (uint64_t)p->d.K, N = (uint64_t)p->d.N, k = (uint64_t)mg::xo_cols(p->d.k);
-    if ((uint64_t)M * K / 2 >= lim || N * K / 2 >= lim || (uint64_t)M * 2 * k >= lim || N * 2 * k >= lim ||
-        (uint64_t)mg::sc_bytes(M, p->d.K) >= lim || (uint64_t)mg::sc_bytes(p->d.N, p->d.K) >= lim)
+    const int64_t lim = 0xC0000000ll;
+    const int64_t K = p->d.K, N = p->d.N, k = p->d.k;
+    if (mg::frag_bytes(M, K / 2) >= lim || mg::frag_bytes(N, K / 2) >= lim || mg::frag_bytes(M, 2 * k) >= lim ||
+        mg::frag_bytes(N, 2 * k) >= lim || mg::sc_bytes(M, p->d.K) >= lim || mg::sc_bytes(p->d.N, p->d.K) >= lim)
         return fail(MG_ERR_UNSUPPORTED, "operands of M=%lld, N=%d, K=%d, k=%d exceed 3 GiB", (long long)M, p->d.N,
                     p->d.K, p->d.k);
     return MG_OK;
@@ -133,7 +133,7 @@ int device_cu_count() {
 
 extern "C" {
 
-int mg_version(void) { return 300; }   // 0.3.0: scales in windows, outlier rows padded to 8
+int mg_version(void) { return 400; }   // 0.4.0: operands in fragment order
 
 const char* mg_last_error(void) { return g_err; }
 
@@ -145,11 +145,11 @@ int mg_plan_bytes(const mg_plan_desc* d, size_t out[8]) {
     out[1] = 4 * K;                                        // rcp
     out[2] = 4 * k;                                        // O
     out[3] = 4 * K;                                        // pos
-    out[4] = N * K / 2;                                    // Wq
+    out[4] = (size_t)mg::frag_bytes((int64_t)N, d->K / 2);  // Wq, fragment order
     out[5] = (size_t)mg::sc_bytes((int64_t)N, d->K);       // Ws, in 256-row x 16-block windows
     out[6] = d->layout == MG_W_32X32 ? (N / 32) * (K / 32)       // Wst
            : d->layout == MG_W_128X1 ? N * ((K + 127) / 128) : 0;
-    out[7] = 2 * N * (size_t)mg::xo_cols(d->k);            // WO [N][kp], kp = k rounded up to 8
+    out[7] = (size_t)mg::frag_bytes((int64_t)N, 2 * (int64_t)d->k);   // WO, fragment order
     return MG_OK;
 }
 
@@ -157,10 +157,9 @@ int mg_act_bytes(const mg_plan_desc* d, int64_t M, size_t out[3]) {
     if (int e = check_desc(d)) return e;
     if (!out) return fail(MG_ERR_ARG, "null output array");
     if (M < 0) return fail(MG_ERR_SHAPE, "M=%lld must be >= 0", (long long)M);
-    const size_t K = (size_t)d->K, k = (size_t)d->k, m = (size_t)M;
-    out[0] = m * K / 2;
+    out[0] = (size_t)mg::frag_bytes(M, d->K / 2);          // Aq, fragment order
     out[1] = (size_t)mg::sc_bytes(M, d->K);                // As, in 256-row x 16-block windows
-    out[2] = 2 * m * (size_t)mg::xo_cols(d->k);            // XO [M][kp]
+    out[2] = (size_t)mg::frag_bytes(M, 2 * (int64_t)d->k);  // XO, fragment order
     return MG_OK;
 }
 

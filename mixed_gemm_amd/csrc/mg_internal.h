@@ -12,11 +12,15 @@ constexpr int32_t kMaxK = 65536;
 
 // Storage order of the E8M0 scale codes of Aq (As) and Wq (Ws): windows of
 // 256 rows x 16 blocks (512 channels), 16 bytes per row, so that one window
-// is 4 KB of contiguous memory -- the unit the GEMM copies into LDS.  Byte
-// (row, block) sits at ((row / 256) * nwin + block / 16) * 4096 +
-// (row % 256) * 16 + block % 16 with nwin = ceil(K / 512); the layout depends
-// on K only.  Blocks past K / 32 and rows past the last row of the final
-// 256-row group hold code 0, the code of an all-zero block.
+// is 4 KB of contiguous memory -- the unit the GEMM copies into LDS.  Inside
+// a row the even blocks come first, then the odd ones (block b of the window
+// at byte 8 (b % 2) + b / 2), so a matrix-core lane, which takes either the
+// even or the odd 32-block of each 64-wide K step, finds its codes in 8
+// consecutive bytes.  Byte (row, block) sits at ((row / 256) * nwin + block /
+// 16) * 4096 + (row % 256) * 16 + 8 (block % 2) + (block % 16) / 2 with nwin
+// = ceil(K / 512); the layout depends on K only.  Blocks past K / 32 and rows
+// past the last row of the final 256-row group hold code 0, the code of an
+// all-zero block.
 constexpr int kScRows = 256;      // rows per window
 constexpr int kScBlocks = 16;     // 32-blocks per window row
 constexpr int kScWinBytes = kScRows * kScBlocks;
@@ -24,12 +28,30 @@ __host__ __device__ constexpr int64_t sc_nwin(int32_t K) { return ((int64_t)K + 
 __host__ __device__ constexpr int64_t sc_bytes(int64_t rows, int32_t K) {
     return (rows + kScRows - 1) / kScRows * sc_nwin(K) * kScWinBytes;
 }
-// Row stride (in bf16 values) of the outlier operands XO [M][kp] and WO
-// [N][kp]: k rounded up to a multiple of 8, so every row starts 16-byte
-// aligned; the pad columns k .. kp-1 hold +0.
-__host__ __device__ constexpr int32_t xo_cols(int32_t k) { return (k + 7) & ~7; }
+// Fragment order: the storage order of the GEMM operands Aq, Wq (row_bytes =
+// K/2) and XO, WO (row_bytes = 2k).  A [rows][row_bytes] byte matrix is cut
+// into blocks of 32 rows x 32 bytes (one 32x32x64 FP4 or 32x32x16 bf16
+// matrix-core operand); block (row group g = r / 32, slice c = byte / 32)
+// is 1024 contiguous bytes at (g * ns + c) * 1024, ns = 2 ceil(row_bytes /
+// 64) (an even number of slices: the GEMM moves two per step), and inside it
+// byte b of row r's slice sits at 16 * (r % 32 + 32 * (b / 16)) + b % 16 --
+// the byte lane l = r % 32 + 32 * (b / 16) of the instruction holds at
+// position b % 16.  Rows up to the next multiple of 32 and bytes up to ns *
+// 32 are pads holding 0.
+constexpr int kFragRows = 32;
+constexpr int kFragSliceBytes = 32;
+constexpr int kFragBlock = kFragRows * kFragSliceBytes;
+__host__ __device__ constexpr int64_t frag_slices(int64_t row_bytes) { return (row_bytes + 63) / 64 * 2; }
+__host__ __device__ constexpr int64_t frag_bytes(int64_t rows, int64_t row_bytes) {
+    return (rows + 31) / 32 * frag_slices(row_bytes) * kFragBlock;
+}
+__host__ __device__ constexpr int64_t frag_offset(int64_t r, int64_t b, int64_t ns) {
+    return ((r >> 5) * ns + (b >> 5)) * kFragBlock + (((r & 31) + ((b >> 4) & 1) * 32) << 4) + (b & 15);
+}
+// position of block b (0..15) inside a window row
+__host__ __device__ constexpr int32_t sc_pos(int32_t b) { return 8 * (b & 1) + ((b & 15) >> 1); }
 __host__ __device__ constexpr int64_t sc_offset(int64_t row, int32_t blk, int64_t nwin) {
-    return ((row / kScRows) * nwin + blk / kScBlocks) * kScWinBytes + (row % kScRows) * kScBlocks + blk % kScBlocks;
+    return ((row / kScRows) * nwin + blk / kScBlocks) * kScWinBytes + (row % kScRows) * kScBlocks + sc_pos(blk);
 }
 
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t st);

@@ -26,28 +26,51 @@ def host(t: torch.Tensor) -> np.ndarray:
 def scale_rows(x, rows: int, K: int) -> np.ndarray:
     """[rows][K/32] E8M0 codes of a scale array (As, Ws) stored in scale
     windows: the code of (row r, block b) at byte ((r // 256) * nwin + b // 16)
-    * 4096 + (r % 256) * 16 + b % 16, nwin = ceil(K / 512).  Asserts that the
-    bytes the writers fill around the matrix (blocks past K/32, rows up to the
-    end of the last 256-row group) hold code 0."""
+    * 4096 + (r % 256) * 16 + 8 * (b % 2) + (b % 16) // 2, nwin = ceil(K /
+    512) (inside a window row the even blocks first, then the odd ones).
+    Asserts that the bytes the writers fill around the matrix (blocks past
+    K/32, rows up to the end of the last 256-row group) hold code 0."""
     a = np.ascontiguousarray(host(x) if isinstance(x, torch.Tensor) else np.asarray(x)).reshape(-1)
     nwin, nb = -(-K // 512), K // 32
     assert a.dtype == np.uint8 and a.size % (nwin * 4096) == 0, (a.dtype, a.size)
     groups = a.size // (nwin * 4096)
     assert groups * 256 >= rows, (groups, rows)
-    full = a.reshape(groups, nwin, 256, 16).transpose(0, 2, 1, 3).reshape(groups * 256, nwin * 16)
+    # [group][window][row][odd][block // 2] -> [group][row][window][block // 2][odd]
+    full = a.reshape(groups, nwin, 256, 2, 8).transpose(0, 2, 1, 4, 3).reshape(groups * 256, nwin * 16)
     written = full[: -(-rows // 256) * 256].copy()
     written[:rows, :nb] = 0
     assert not written.any(), "scale pad bytes must hold code 0"
     return np.ascontiguousarray(full[:rows, :nb])
 
 
-def outlier_cols(x, k: int) -> np.ndarray:
-    """The k outlier columns of XO [M][kp] or WO [N][kp] (kp = k rounded up to
-    a multiple of 8), asserting that the pad columns hold +0."""
-    a = host(x) if isinstance(x, torch.Tensor) else np.asarray(x)
-    assert a.ndim == 2 and a.shape[1] == (k + 7) // 8 * 8, (a.shape, k)
-    assert not np.asarray(a[:, k:]).view(np.uint16).any(), "outlier pad columns must hold +0"
-    return np.ascontiguousarray(a[:, :k])
+def frag_rows(x, rows: int, row_bytes: int) -> np.ndarray:
+    """[rows][row_bytes] bytes of an operand stored in fragment order (Aq, Wq:
+    row_bytes = K/2; XO, WO: row_bytes = 2k): 32-row x 32-byte blocks of 1 KB,
+    block (r // 32, b // 32) at ((r // 32) * ns + b // 32) * 1024 with ns =
+    2 * ceil(row_bytes / 64), byte b of row r at 16 * (r % 32 + 32 * ((b //
+    16) % 2)) + b % 16 inside it.  Asserts that the pads (rows up to the next
+    multiple of 32, bytes up to ns * 32) hold 0."""
+    a = np.ascontiguousarray(host(x) if isinstance(x, torch.Tensor) else np.asarray(x)).reshape(-1).view(np.uint8)
+    ns = 2 * -(-row_bytes // 64)
+    groups = -(-rows // 32)
+    assert a.size == groups * ns * 1024, (a.size, groups, ns)
+    # [group][slice][half][row % 32][16] -> [group][row % 32][slice][half][16]
+    full = a.reshape(groups, ns, 2, 32, 16).transpose(0, 3, 1, 2, 4).reshape(groups * 32, ns * 32)
+    pad = full.copy()
+    pad[:rows, :row_bytes] = 0
+    assert not pad.any(), "fragment-order pad bytes must hold 0"
+    return np.ascontiguousarray(full[:rows, :row_bytes])
+
+
+def outlier_cols(x, rows: int, k: int) -> np.ndarray:
+    """The [rows][k] bf16 bit patterns of XO or WO (fragment order, rows of
+    2k bytes), asserting that the pads hold +0."""
+    return frag_rows(x, rows, 2 * k).view(np.uint16)
+
+
+def aq_rows(x, rows: int, K: int) -> np.ndarray:
+    """The [rows][K/2] packed nibbles of Aq or Wq (fragment order)."""
+    return frag_rows(x, rows, K // 2)
 
 
 def run_pipeline(X: np.ndarray, W: np.ndarray, alpha: float, k: int, layout: str = "1x32",
@@ -76,9 +99,10 @@ def run_pipeline(X: np.ndarray, W: np.ndarray, alpha: float, k: int, layout: str
     torch.cuda.synchronize()
     out = dict(act_max=host(act_max), w_max=host(w_max), Y=host(Y), Y32=host(Y32))
     out.update({n: host(t) for n, t in p.tensors().items()})
+    out["Wq"] = aq_rows(p.Wq, N, K)
     out["Ws"] = scale_rows(p.Ws, N, K)
-    out["WO"] = outlier_cols(p.WO, k)
-    out.update(Aq=host(a.Aq), As=scale_rows(a.As, M, K), XO=outlier_cols(a.XO, k))
+    out["WO"] = outlier_cols(p.WO, N, k)
+    out.update(Aq=aq_rows(a.Aq, M, K), As=scale_rows(a.As, M, K), XO=outlier_cols(a.XO, M, k))
     return out
 
 

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import mixed_gemm_amd as mg
-from tests.gpu_util import scale_rows
+from tests.gpu_util import frag_rows, scale_rows
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "mixed_gemm.h")
 FAKE = 1 << 20          # aligned, never dereferenced: every call below fails validation first
@@ -42,11 +42,17 @@ def test_exports_every_declared_symbol():
 def test_plan_and_act_sizes():
     d = mg.make_desc(5120, 13824, 64, 0.6, "1x32")
     b = mg.mg_plan_bytes(d)
-    assert b == [4 * 5120, 4 * 5120, 4 * 64, 4 * 5120, 13824 * 2560, 13824 * 160, 0, 2 * 13824 * 64]
+    # Wq, WO in fragment order: 32-row x 32-byte blocks of 1 KB
+    assert b == [4 * 5120, 4 * 5120, 4 * 64, 4 * 5120, 432 * 80 * 1024, 13824 * 160, 0, 432 * 4 * 1024]
     d2 = mg.make_desc(512, 1024, 8, 0.5, "32x32")
     assert mg.mg_plan_bytes(d2)[6] == 32 * 16
     # scales in 256-row x 16-block windows of 4 KB: 128 row groups x 10 windows
-    assert mg.mg_act_bytes(d, 32760) == [32760 * 2560, 128 * 10 * 4096, 2 * 32760 * 64]
+    assert mg.mg_act_bytes(d, 32760) == [1024 * 80 * 1024, 128 * 10 * 4096, 1024 * 4 * 1024]
+    d4 = mg.make_desc(352, 96, 3, 0.5, "1x32")               # 176-byte rows: 6 slices; 6-byte XO rows: 2
+    assert mg.mg_act_bytes(d4, 33) == [2 * 6 * 1024, 1 * 1 * 4096, 2 * 2 * 1024]
+    assert mg.mg_plan_bytes(d4)[4] == 3 * 6 * 1024 and mg.mg_plan_bytes(d4)[7] == 3 * 2 * 1024
+    d5 = mg.make_desc(480, 96, 40, 0.5, "1x32")              # 240-byte rows: 8 slices (7 padded to 8); XO 80: 4
+    assert mg.mg_act_bytes(d5, 64) == [2 * 8 * 1024, 1 * 1 * 4096, 2 * 4 * 1024]
     assert mg.mg_act_bytes(d, 0) == [0, 0, 0]
     d3 = mg.make_desc(352, 96, 3, 0.5, "1x32")               # K % 512 != 0: one window per group
     assert mg.mg_plan_bytes(d3)[5] == 1 * 1 * 4096
@@ -63,7 +69,7 @@ def test_scale_window_layout(rows, K):
     buf = np.zeros(-(-rows // 256) * nwin * 4096, dtype=np.uint8)
     for r in range(rows):
         for b in range(nb):
-            buf[((r // 256) * nwin + b // 16) * 4096 + (r % 256) * 16 + b % 16] = codes[r, b]
+            buf[((r // 256) * nwin + b // 16) * 4096 + (r % 256) * 16 + 8 * (b % 2) + (b % 16) // 2] = codes[r, b]
     assert buf.size == mg.mg_act_bytes(mg.make_desc(K, 32, 0, 0.5, "1x32"), rows)[1]
     assert buf.size == int(np.prod(mg.scale_shape(rows, K)))
     assert np.array_equal(scale_rows(buf, rows, K), codes)
@@ -72,6 +78,25 @@ def test_scale_window_layout(rows, K):
         buf[pad] = 7
         with pytest.raises(AssertionError):
             scale_rows(buf, rows, K)
+
+
+@pytest.mark.parametrize("rows,row_bytes", [(33, 176), (32, 64), (1, 16), (70, 6), (64, 2560)])
+def test_fragment_order_layout(rows, row_bytes):
+    """The tests' reader of the fragment order against the header's byte
+    formula applied byte by byte, and the buffer size against frag_shape."""
+    rng = np.random.default_rng(rows * 7 + row_bytes)
+    data = rng.integers(1, 255, size=(rows, row_bytes), dtype=np.uint8)
+    ns = 2 * -(-row_bytes // 64)
+    buf = np.zeros(-(-rows // 32) * ns * 1024, dtype=np.uint8)
+    for r in range(rows):
+        for b in range(row_bytes):
+            buf[((r // 32) * ns + b // 32) * 1024 + 16 * (r % 32 + 32 * ((b // 16) % 2)) + b % 16] = data[r, b]
+    assert buf.size == int(np.prod(mg.frag_shape(rows, row_bytes)))
+    assert np.array_equal(frag_rows(buf, rows, row_bytes), data)
+    if buf.size > data.size:                                  # a non-zero pad byte is caught
+        buf[np.flatnonzero(buf == 0)[0]] = 9
+        with pytest.raises(AssertionError):
+            frag_rows(buf, rows, row_bytes)
 
 
 @pytest.mark.parametrize("K,N,k,alpha,layout,smooth,code", [
@@ -233,7 +258,7 @@ def test_binding_checks_shapes_before_any_launch():
         lambda: mg.mg_quantize_act(p, torch.zeros((8, 32), dtype=torch.bfloat16), a),      # K mismatch
         lambda: mg.mg_quantize_act(p, torch.zeros((9, 64), dtype=torch.bfloat16), a),      # act.M != M
         lambda: mg.mg_quantize_act(p, torch.zeros(64, dtype=torch.bfloat16), a),           # not 2-D
-        lambda: mg.mg_quantize_act(p, X, mg.Act.empty(mg.make_desc(64, 96, 12, 0.5), 8, device="cpu")),
+        lambda: mg.mg_quantize_act(p, X, mg.Act.empty(mg.make_desc(64, 96, 40, 0.5), 8, device="cpu")),
         lambda: mg.mg_quantize_act_stats(p, X, a, v32),                                     # stats of K
         lambda: mg.mg_dual_gemm(p, a, torch.zeros((8, 64), dtype=torch.bfloat16)),         # Y not [M][N]
         lambda: mg.mg_dual_gemm(p, a, torch.zeros((8, 96), dtype=torch.float64)),          # Y dtype

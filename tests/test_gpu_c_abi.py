@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 from oracle import layer
-from tests.gpu_util import check_output, outlier_cols, scale_rows
+from tests.gpu_util import aq_rows, check_output, outlier_cols, scale_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -58,8 +58,10 @@ def test_c_program_matches_oracle(tmp_path):
         got = np.frombuffer(b[name], np.uint8)
         if name in ("As", "Ws"):                                     # stored in scale windows
             got = scale_rows(got, M if name == "As" else N, K)
-        elif name in ("XO", "WO"):                                   # rows of kp = k rounded up to 8
-            got = outlier_cols(got.view(np.uint16).reshape(M if name == "XO" else N, -1), k).view(np.uint8)
+        elif name in ("Aq", "Wq"):                                   # fragment order
+            got = aq_rows(got, M if name == "Aq" else N, K)
+        elif name in ("XO", "WO"):                                   # fragment order, rows of 2k bytes
+            got = outlier_cols(got, M if name == "XO" else N, k).view(np.uint8)
         assert got.size == ref.nbytes and np.array_equal(got.ravel(), ref.view(np.uint8).ravel()), name
     assert len(b["Wst"]) == 0
     Y64 = layer.dual_gemm_f64(qa["Aq"], qa["As"], p["Wq"], p["Ws"], qa["XO"], p["WO"])

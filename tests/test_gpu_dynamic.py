@@ -14,7 +14,7 @@ import torch
 import mixed_gemm_amd as mg
 import synth
 from oracle import layer
-from tests.gpu_util import check_output, dev, host, outlier_cols, scale_rows
+from tests.gpu_util import aq_rows, check_output, dev, host, outlier_cols, scale_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -72,7 +72,7 @@ def test_dynamic_router_follows_previous_step(score):
         torch.cuda.synchronize()
         op = layer.plan(a_cal, w, W, 0.6, k, score=score, rank=prev)
         oq = layer.quantize_act(X, op["s"], op["O"])
-        got = dict(Aq=host(act.Aq), As=scale_rows(act.As, M, K), XO=outlier_cols(act.XO, k))
+        got = dict(Aq=aq_rows(act.Aq, M, K), As=scale_rows(act.As, M, K), XO=outlier_cols(act.XO, M, k))
         for n in ("Aq", "As", "XO"):
             assert np.array_equal(np.asarray(got[n]).view(np.uint8), np.asarray(oq[n]).view(np.uint8)), (t, n)
         Y32 = torch.empty((M, N), dtype=torch.float32, device="cuda")

@@ -27,7 +27,7 @@ import torch
 import mixed_gemm_amd as mg
 import synth
 from oracle import layer
-from tests.gpu_util import dev, host, scale_rows
+from tests.gpu_util import aq_rows, dev, scale_rows
 
 pytestmark = pytest.mark.gpu
 K = 512
@@ -70,7 +70,7 @@ def _run(Xd, X, s: np.ndarray):
     mg.mg_quantize_act(p, Xd, a)
     torch.cuda.synchronize()
     o = layer.quantize_act(X, s, np.zeros(0, np.int32))
-    Aq, As = host(a.Aq), scale_rows(a.As, X.shape[0], K)
+    Aq, As = aq_rows(a.Aq, X.shape[0], K), scale_rows(a.As, X.shape[0], K)
     for name, g_, o_ in (("Aq", Aq, o["Aq"]), ("As", As, o["As"])):
         if not np.array_equal(g_, o_):
             bad = np.argwhere(g_ != o_)

@@ -21,7 +21,7 @@ import torch
 import mixed_gemm_amd as mg
 import synth
 from oracle import layer
-from tests.gpu_util import check_output, dev, host, outlier_cols, scale_rows
+from tests.gpu_util import aq_rows, check_output, dev, host, outlier_cols, scale_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -87,12 +87,13 @@ def _run_full(w: synth.Workload, layout="1x32", score="max", all_rows=True):
     torch.cuda.synchronize()
     g = dict(act_max=host(act_max), w_max=host(w_max), Y=host(Y[ridx]), Y32=host(Y32[ridx]))
     if all_rows:
-        g.update(Aq=host(a.Aq), As=scale_rows(a.As, M, K), XO=outlier_cols(host(a.XO), w.k))
+        g.update(Aq=aq_rows(a.Aq, M, K), As=scale_rows(a.As, M, K), XO=outlier_cols(a.XO, M, w.k))
     else:
-        g.update(Aq=host(a.Aq[ridx]), As=scale_rows(a.As, M, K)[rows], XO=outlier_cols(host(a.XO[ridx]), w.k))
+        g.update(Aq=aq_rows(a.Aq, M, K)[rows], As=scale_rows(a.As, M, K)[rows], XO=outlier_cols(a.XO, M, w.k)[rows])
     g.update({n: host(t) for n, t in p.tensors().items()})
     g["Ws"] = scale_rows(p.Ws, N, K)
-    g["WO"] = outlier_cols(p.WO, w.k)
+    g["Wq"] = aq_rows(p.Wq, N, K)
+    g["WO"] = outlier_cols(p.WO, N, w.k)
     del Y, Y32, a, Xd, Wd
     torch.cuda.empty_cache()
 

@@ -16,7 +16,7 @@ import torch
 import mixed_gemm_amd as mg
 import synth
 from oracle import layer
-from tests.gpu_util import assert_faithful_bf16, bf16_to_f64, check_output, dev, host, outlier_cols, run_pipeline, scale_rows
+from tests.gpu_util import aq_rows, assert_faithful_bf16, bf16_to_f64, check_output, dev, host, outlier_cols, run_pipeline, scale_rows
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
@@ -122,6 +122,20 @@ def test_large_K(M, K, N, k):
     _compare(g, _oracle(X, W, 0.6, k))
 
 
+@pytest.mark.parametrize("M,K,N,k", [(4096, 128, 8192, 0), (4096, 640, 8192, 0), (4096, 32, 8192, 0),
+                                     (4096, 96, 8192, 3), (2304, 1056, 8192, 40)])
+def test_many_tiles_per_workgroup(M, K, N, k):
+    """More 256x256 tiles than compute units (512 or 288 tiles), so each
+    workgroup walks several tiles and the copy pipeline and the scale windows
+    run across tile boundaries: tiles of one half-stage (K <= 128, the copies
+    two tiles ahead), a tile ending one half-stage into its second scale
+    window (K = 640, k = 0), a half-filled last K-slice (K = 32, 96) and
+    outlier half-stages after the bulk ones."""
+    X, W = _heavy(M, K, N, 7000 + K)
+    g = run_pipeline(X, W, 0.6, k)
+    _compare(g, _oracle(X, W, 0.6, k))
+
+
 @pytest.mark.parametrize("layout", ["1x32", "32x32", "128x1"])
 def test_layouts(layout):
     X, W = _heavy(300, 512, 256, 77)
@@ -153,12 +167,15 @@ def test_smoothed_score(layout):
 @pytest.mark.parametrize("layout", ["1x32", "32x32", "128x1"])
 @pytest.mark.parametrize("M,K,N,k,bf16", [(300, 352, 96, 6, True), (600, 800, 288, 12, False)])
 def test_scale_pads_written_over_garbage(M, K, N, k, bf16, layout):
-    """Ragged M, N and K (not multiples of 256, 256 and 512) and k not a
-    multiple of 8: over scale buffers pre-filled with 0xFF (the E8M0 NaN code)
-    and outlier buffers pre-filled with bf16 NaNs, the writers fill every pad
-    row and pad block of the scale windows with code 0 and every pad column of
-    XO / WO with +0 (checked by scale_rows and outlier_cols), the codes equal
-    the oracle's, and the output is exact."""
+    """Ragged M, N and K (not multiples of 256, 256 and 512; K % 64 == 32, so
+    the last 32-byte slice of an Aq / Wq row is half pad) and k not a
+    multiple of 16: over scale buffers pre-filled with 0xFF (the E8M0 NaN
+    code), payload buffers pre-filled with 0xFF and outlier buffers with bf16
+    NaNs, the writers fill every pad row and pad block of the scale windows
+    with code 0, every fragment-order pad of Aq / Wq (rows up to a multiple of
+    32, the half slice) with zero codes and every pad of XO / WO with +0
+    (checked by scale_rows, aq_rows and outlier_cols), the codes equal the
+    oracle's, and the output is exact."""
     X, W = _heavy(M, K, N, 70 + K, bf16=bf16)
     Xd, Wd = dev(X), dev(W)
     act_max = mg.calibrate([Xd], K)
@@ -167,11 +184,13 @@ def test_scale_pads_written_over_garbage(M, K, N, k, bf16, layout):
     desc = mg.make_desc(K, N, k, 0.6, layout)
     p = mg.Plan.empty(desc)
     p.Ws.fill_(0xFF)
-    p.WO.view(torch.int16).fill_(-1)
+    p.WO.fill_(0xFF)                         # bf16 NaNs
+    p.Wq.fill_(0xFF)
     mg.mg_plan_build(p, act_max, w_max, Wd)
     a = mg.Act.empty(desc, M)
     a.As.fill_(0xFF)
-    a.XO.view(torch.int16).fill_(-1)
+    a.XO.fill_(0xFF)
+    a.Aq.fill_(0xFF)
     mg.mg_quantize_act(p, Xd, a)
     Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     Y32 = torch.empty((M, N), dtype=torch.float32, device="cuda")
@@ -181,8 +200,8 @@ def test_scale_pads_written_over_garbage(M, K, N, k, bf16, layout):
     o = _oracle(X, W, 0.6, k, layout)
     assert np.array_equal(scale_rows(p.Ws, N, K), o["Ws"])
     assert np.array_equal(scale_rows(a.As, M, K), o["As"])
-    assert np.array_equal(host(a.Aq), o["Aq"]) and np.array_equal(host(p.Wq), o["Wq"])
-    assert np.array_equal(outlier_cols(a.XO, k), o["XO"]) and np.array_equal(outlier_cols(p.WO, k), o["WO"])
+    assert np.array_equal(aq_rows(a.Aq, M, K), o["Aq"]) and np.array_equal(aq_rows(p.Wq, N, K), o["Wq"])
+    assert np.array_equal(outlier_cols(a.XO, M, k), o["XO"]) and np.array_equal(outlier_cols(p.WO, N, k), o["WO"])
     check_output(host(Y), host(Y32), o["Y64"])
 
 
@@ -295,7 +314,7 @@ def test_gelu_quantize_fused(M, K, k):
     for n in ("Aq", "As", "XO"):
         assert torch.equal(getattr(a1, n).view(torch.uint8), getattr(a2, n).view(torch.uint8)), n
     oq = layer.quantize_act(host(h), host(p.s), host(p.O))
-    got = dict(Aq=host(a2.Aq), As=scale_rows(a2.As, M, K), XO=outlier_cols(a2.XO, k))
+    got = dict(Aq=aq_rows(a2.Aq, M, K), As=scale_rows(a2.As, M, K), XO=outlier_cols(a2.XO, M, k))
     for n in ("Aq", "As", "XO"):
         assert np.array_equal(np.asarray(got[n]).view(np.uint8), np.asarray(oq[n]).view(np.uint8)), n
 

@@ -8,7 +8,7 @@ import torch
 import mixed_gemm_amd as mg
 import synth
 from oracle import layer
-from tests.gpu_util import dev, host, outlier_cols, scale_rows
+from tests.gpu_util import aq_rows, dev, host, outlier_cols, scale_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -58,7 +58,8 @@ def test_plan_ranked_by_percentile(score):
     op = layer.plan(layer.act_max(X), layer.weight_range(W), W, 0.6, k, score=score, rank=o_pct)
     g = {n: host(t) for n, t in p.tensors().items() if t is not None and t.numel()}
     g["Ws"] = scale_rows(p.Ws, N, K)
-    g["WO"] = outlier_cols(p.WO, k)
+    g["Wq"] = aq_rows(p.Wq, N, K)
+    g["WO"] = outlier_cols(p.WO, N, k)
     for name in ("s", "rcp", "O", "pos", "Wq", "Ws", "WO"):
         gv, ov = np.asarray(g[name]), np.asarray(op[name])
         same = (np.array_equal(gv.view(np.uint32), ov.view(np.uint32)) if gv.dtype.kind == "f"
