@@ -33,6 +33,15 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+# the host cores this process may run on, and the threads the oracle baseline
+# uses: all of them, unless the environment already caps the thread pools
+# (a shared host's share); BLAS is told that count before numpy is imported
+HOST_CORES = len(os.sched_getaffinity(0))
+_cap = min([int(os.environ[v]) for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS")
+            if os.environ.get(v, "").isdigit() and int(os.environ[v]) > 0] + [HOST_CORES])
+BASELINE_THREADS = _cap
+for _v in ("OPENBLAS_NUM_THREADS", "OMP_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ.setdefault(_v, str(BASELINE_THREADS))
 
 PEAK_FP4_TFLOPS = 10100.0          # MI355X dense MXFP4 MFMA (published)
 PEAK_HBM_GBS = 8000.0              # MI355X HBM3E (published)
@@ -65,10 +74,14 @@ def cpu_baseline(w, X, W, rows: int) -> dict:
     """The oracle as it stands, on a bounded sample: the weight ranges and plan
     on the full W, and the per-row work (calibration, quantize, float64 dual
     GEMM) on `rows` rows, whose cost is scaled to the workload's M."""
-    import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import layer
+    with threadpool_limits(limits=BASELINE_THREADS):
+        return _cpu_baseline(layer, threadpool_info, w, X, W, rows)
+
+
+def _cpu_baseline(layer, threadpool_info, w, X, W, rows: int) -> dict:
     t0 = time.perf_counter()
     a = layer.act_max(X[:rows])                                   # per-row work
     t1 = time.perf_counter()
@@ -83,6 +96,7 @@ def cpu_baseline(w, X, W, rows: int) -> dict:
     t_full = t_plan + t_rows * w.M / rows
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": round(w.flops() / t_full / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "host_cores": HOST_CORES,
             "kind": "oracle",
             "sample": (f"the whole oracle step, all {w.M} rows: weight ranges and plan {t_plan:.1f} s, "
                        f"per-row work {t_rows:.1f} s" if rows == w.M else

@@ -235,9 +235,13 @@ int mg_plan_build(const mg_plan* p, const float* act_max, const float* w_max, co
 
 /* ---- forward (per batch) ---- */
 
-/* Runtime activation path: q = RN_f32(X[m][j] / s_j) (exact IEEE division),
- * XO[m][pos_j] = bf16(q), bulk q with outlier columns set to +0 MXFP4-encoded
- * into Aq/As.  M == 0 is a no-op. */
+/* Runtime activation path (the integration paragraph after Eq. (5): at
+ * inference a calibrated layer's input is divided in place by s, quantized to
+ * 4 bits, and its outlier columns go to the narrow high-precision branch;
+ * Eq. (1)'s X / s and Eq. (5)'s split into J and O):
+ * q = RN_f32(X[m][j] / s_j) (exact IEEE division), XO[m][pos_j] = bf16(q),
+ * bulk q with outlier columns set to +0 MXFP4-encoded into Aq/As.  M == 0 is
+ * a no-op. */
 int mg_quantize_act(const mg_plan* p, const void* X, int32_t dtype, int64_t M,
                     const mg_act* a, hipStream_t stream);
 
@@ -286,9 +290,10 @@ int mg_forward(const mg_plan* p, const void* X, int32_t dtype, int64_t M, const 
 int mg_forward_noalloc(const mg_plan* p, const void* X, int32_t dtype, int64_t M, void* Y, int32_t y_dtype,
                        hipStream_t stream);
 
-/* Between the two projections of the FFN block: out[i] = gelu_tanh(in[i]) for
- * n bf16 values (in == out allowed), gelu_tanh(y) = 0.5 y (1 + tanh(sqrt(2/pi)
- * (y + 0.044715 y^3))).  Evaluated in f32 as the equal y / (1 + exp(-2u))
+/* Between the two projections of the FFN block (the integration paragraph:
+ * the calibrated FFN linear layers take their inputs after the SiLU/GELU
+ * gates): out[i] = gelu_tanh(in[i]) for n bf16 values (in == out allowed),
+ * gelu_tanh(y) = 0.5 y (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3))).  Evaluated in f32 as the equal y / (1 + exp(-2u))
  * (u the tanh argument) with the hardware exp2 and reciprocal, then rounded
  * to bf16: a faithful bf16 rounding (one of the two bf16 neighbours) of the
  * exact value for every finite input where that is at least 2^-24 in

@@ -56,6 +56,19 @@ def test_large_workload_small_slice():
     assert g.shape == (8, 13824)
     assert synth.pick_channels(13824, 0.01, 301).size == 138
     h = synth.bf16_bits_to_f32(g)
-    # the shape of an activation output: negatives bounded near -0.17, a heavy positive tail
-    assert h.min() >= -0.171 and (h < 0).mean() > 0.3
+    # a GELU output: negatives no lower than its minimum (about -0.1700 at
+    # z = -0.7518), decaying to -0 for very negative z; a heavy positive tail
+    assert h.min() >= -0.1702 and (h < 0).mean() > 0.3
     assert h[:, synth.pick_channels(13824, 0.01, 301)].max() > 20.0
+
+
+def test_gelu_input_recipe():
+    """The down-projection input recipe is GELU-tanh of its pre-activation:
+    GELU(0) = 0, GELU(z) -> z for large z, -> 0 for very negative z, its
+    minimum near z = -0.752, and GELU(z) - GELU(-z) = z (the odd part of z
+    Phi(z)-like gates) up to float32 rounding."""
+    z = np.array([0.0, 10.0, -10.0, -0.7518, 1.0, -1.0], np.float32)
+    h = synth.gelu_tanh_input_f32(z)
+    assert h[0] == 0.0 and abs(h[1] - 10.0) < 1e-5 and abs(h[2]) < 1e-5
+    assert -0.1701 < h[3] < -0.1699
+    assert abs((h[4] - h[5]) - 1.0) < 1e-6
