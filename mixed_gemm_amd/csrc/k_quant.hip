@@ -32,11 +32,11 @@
 // in registers with the GELU kernel's own code: one pass instead of a GELU
 // pass that writes h and a quantize pass that reads it back.
 //
-// bf16 input: the quotient comes from Markstein's correction of x * RN(1/s),
-// exact when every x of the lane's row lies in {0} or [2^-100, 2^100]; that
-// range is checked on the raw bf16 bits, two channels per 16-bit-lane
-// integer instruction.  Rows of a lane that fail it, and f32 input, use the
-// correctly rounded division.
+// bf16 input: the quotient comes from Markstein's correction of x * RN(1/s);
+// the conditions under which its codes are the exact ones are checked on the
+// quotients and block maxima the encoder forms anyway (process_row), and a
+// wave whose row fails them redoes the row with the correctly rounded
+// division.  f32 input always uses the correctly rounded division.
 #include "mg_device.h"
 #include "mg_internal.h"
 
@@ -50,30 +50,19 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 4;
 constexpr int kStgRow = 272;      // LDS staging row: 256 bytes of codes + 16 pad
 
-// |x| bit patterns of bf16 2^-100 and 2^100 (biased exponents 27 and 227)
-constexpr unsigned short kBf16Lo = 0x0D80, kBf16Hi = 0x7180;
+// f32 bit patterns of 2^126, 2^-74 and 2^-78 (the fast-division checks)
+constexpr uint32_t kF32Pow126 = 0x7E800000u, kF32PowM74 = 0x1A800000u, kF32PowM78 = 0x18800000u;
+// integer predicates of __builtin_amdgcn_uicmp (a wave mask of the lanes where
+// the unsigned comparison holds)
+constexpr int kCmpNE = 33, kCmpUGE = 35, kCmpULT = 36;
 
 // Max over the 4 lanes of a quad (one 32-block: quad_perm [1,0,3,2] then
 // [2,3,0,1]) of the bit patterns of non-negative f32 values, whose unsigned
 // integer order is their numeric order.
 __device__ __forceinline__ uint32_t quad_max_bits(uint32_t v) {
-    v = __builtin_elementwise_max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));
-    v = __builtin_elementwise_max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));
+    v = __builtin_elementwise_max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true));
+    v = __builtin_elementwise_max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true));
     return v;
-}
-
-// Every bf16 of the four words is 0 or has 2^-100 <= |x| <= 2^100.
-__device__ __forceinline__ bool bf16x8_in_fast_range(const u32x4& w) {
-    u16x2 hi = {0, 0}, lo = {0xFFFF, 0xFFFF};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const u16x2 a = __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu);
-        hi = __builtin_elementwise_max(hi, a);
-        lo = __builtin_elementwise_min(lo, a - (u16x2){1, 1});      // 0 wraps to 0xFFFF
-    }
-    const unsigned short h = hi[0] > hi[1] ? hi[0] : hi[1];
-    const unsigned short l = lo[0] < lo[1] ? lo[0] : lo[1];
-    return h <= kBf16Hi && l >= (unsigned short)(kBf16Lo - 1);
 }
 
 // E8M0 scale code c of the lane's 32-block and the packed E2M1 nibbles of its
@@ -109,8 +98,10 @@ __device__ __forceinline__ void encode_store(const float (&q)[8], int lane, uint
 __device__ __forceinline__ uint32_t frag_lane_off(uint32_t b) { return (b >> 5) * 1024u + ((b >> 4) & 1u) * 512u + (b & 15u); }
 __device__ __forceinline__ int64_t frag_row_off(int64_t r, int64_t ns) { return (r >> 5) * ns * kFragBlock + ((r & 31) << 4); }
 
+// 5 waves per SIMD (at most 96 VGPRs each); the statistics variants, which
+// also carry the lane's running channel maxima, fit 4 without spills.
 template <bool GELU, bool STATS>
-__global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restrict__ X, int64_t M, int32_t K,
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(STATS ? 4 : 5, 8))) quant_bf16_kernel(const uint16_t* __restrict__ X, int64_t M, int32_t K,
                                                          int32_t k, const float* __restrict__ s,
                                                          const float* __restrict__ rcp,
                                                          const int32_t* __restrict__ pos,
@@ -163,11 +154,17 @@ __global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restr
         omask |= (pv[i] >= 0 ? 1u : 0u) << i;
         s_ok &= div_fast_ok_s(sv[i]);
     }
-    // keep masks of the input words (outlier channels -> +0 in the bulk)
-    uint32_t keepw[4];
+    // The fast quotient multiplies by rz = RN(1/s), or by 0 on outlier channels:
+    // their bulk quotient is then +-0 (no effect on the block maximum) and
+    // their nibbles are cleared after encoding (nkeep), so that they encode
+    // the +0 of Eq. (5)'s bulk.  The exact-division path divides +0 there.
+    float rz[8];
+    uint32_t nkeep = 0;
 #pragma unroll
-    for (int w = 0; w < 4; ++w)
-        keepw[w] = ((omask >> (2 * w)) & 1u ? 0u : 0x0000FFFFu) | ((omask >> (2 * w + 1)) & 1u ? 0u : 0xFFFF0000u);
+    for (int i = 0; i < 8; ++i) {
+        rz[i] = (omask >> i) & 1u ? 0.0f : rv[i];
+        nkeep |= ((omask >> i) & 1u ? 0u : 0xFu) << (4 * i);
+    }
     // The first outlier channel of the lane (if any) is written with one store
     // per row; further outlier channels of the same lane take one more store each.
     const int oc0 = omask ? __builtin_ctz(omask) : 0;
@@ -180,20 +177,30 @@ __global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restr
         op0 = oc0 == i ? pv[i] : op0;
     }
     const uint32_t omask_rest = omask & (omask - 1);
+    const uint32_t osh = (oc0 & 1) ? 0u : 16u;     // brings the first outlier's bf16 to the top half
 
-    // Per-lane byte offsets inside a row.  Rows are addressed through a buffer
-    // resource per row (scalar registers), so lanes whose channels lie past
-    // K read zeros and drop their stores by the hardware range check, and so
-    // do the lanes that store no scale byte or no outlier value (offset
-    // kNoStore).  The workgroup's 512 channels are one scale window: a row's
-    // 16 scale bytes are contiguous, lane 4 i storing block i's code at byte
+    // Per-lane byte offsets.  Rows of X are read through a buffer resource
+    // per row (scalar registers), so lanes whose channels lie past K read
+    // zeros.  XO pieces and As codes are written through one resource per
+    // 32-row group; a row's part of the offset, 16 bytes per row of the
+    // group, is a per-wave constant plus the row's index in the wave times 16.
+    // Lanes that store no scale byte or no outlier value get the offset
+    // kNoStore, past every resource's range, and the hardware drops those
+    // stores.  The workgroup's 512 channels are one scale window: a row's 16
+    // scale bytes are contiguous, lane 4 i storing block i's code at byte
     // sc_pos(i) (past K: the code 0 of its all-zero block).
     constexpr uint32_t kNoStore = 0x40000000u;
     const uint32_t offX = 2u * (uint32_t)j0;
-    const uint32_t offAs = (lane & 3) == 0 ? (uint32_t)sc_pos(lane >> 2) : kNoStore;
-    const uint32_t offXO = omask ? frag_lane_off(2u * (uint32_t)op0) : kNoStore;
-    const bool wave_o = __builtin_amdgcn_ballot_w64(omask != 0) != 0;
-    const bool wave_rest = __builtin_amdgcn_ballot_w64(omask_rest != 0) != 0;
+    const uint32_t rowpart = 128u * (uint32_t)wave;                       // 16 (8 wave) bytes
+    const uint32_t offAs = ((lane & 3) == 0 ? (uint32_t)sc_pos(lane >> 2) : kNoStore) + rowpart;
+    const uint32_t offXO = (omask ? frag_lane_off(2u * (uint32_t)op0) : kNoStore) + rowpart;
+    // wave-uniform flags as scalars (readfirstlane), so that branches on them
+    // stay scalar
+    const int wave_o = __builtin_amdgcn_readfirstlane((int)(__builtin_amdgcn_ballot_w64(omask != 0) != 0));
+    const int wave_rest = __builtin_amdgcn_readfirstlane((int)(__builtin_amdgcn_ballot_w64(omask_rest != 0) != 0));
+    // |q0| bound of the fast path, 0 on lanes whose s is outside [2^-20, 2^20]
+    // (their rows always take the exact division)
+    const uint32_t a0_lim = s_ok ? kF32Pow126 : 0u;
     // Aq rows of K/2 bytes in ns4 slices, XO rows of 2k bytes in nso slices;
     // the workgroup of channels 0..511 writes XO's pad columns k .. 16 nso - 1
     // (+0), one per lane
@@ -201,7 +208,6 @@ __global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restr
     const int kp16 = 16 * (int)nso;
     const uint32_t rowX = 2u * (uint32_t)K;
     const bool pad_wg = blockIdx.x == 0 && kp16 > k;
-    const uint32_t offPad = lane < kp16 - k ? frag_lane_off(2u * (uint32_t)(k + lane)) : kNoStore;
 
     auto rsrc = [](const void* p, uint32_t bytes) {
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
@@ -211,16 +217,24 @@ __global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restr
                                                                                 2));   // nt
     };
 
-    // one row m: w its 8 bf16 per lane, ps its 16 bytes of the As window;
-    // live: a row below M rounded up to 32 (rows of X, and pad rows whose
-    // zero codes the fragment order holds); else a pad row of the last
-    // 256-row scale group, of which only the scale codes are written.  The
-    // row's resources start at its fragment-order row part and cover its
-    // pieces: ns * 1024 - 16 (m % 32) bytes.
-    auto process_row = [&](u32x4 w, int64_t m, uint8_t* ps, bool live) {
-        const uint32_t rsub = (uint32_t)(m & 31) << 4;
-        uint8_t* const po = reinterpret_cast<uint8_t*>(XO) + frag_row_off(m, nso);
-        const uint32_t rowXO = nso ? (uint32_t)nso * 1024u - rsub : 0u;    // k == 0: no XO
+    // Row r (0..7) of the wave's 8 rows in a group: w its 8 bf16 per lane;
+    // rxo / ras the group's XO and As resources (rxo of range 0 for a group
+    // of pad rows that only have scale codes).
+    //
+    // The quotient q = RN(x / s) comes from Markstein's correction of
+    // q0 = RN(x * RN(1/s)) (div_fast), which is the IEEE quotient whenever
+    // |x| >= 2^-100, s lies in [2^-20, 2^20] and |q0| < 2^126.  A smaller
+    // nonzero |x| gives |q| < 2^-79 on both the fast and the exact path
+    // (same sign; a fast +-0 stands for an exact +-0 or +-2^-149): such values
+    // encode to a zero code under any block scale of 2^-76 or more, i.e. when
+    // the block maximum is at least 2^-74, and then neither the maximum nor
+    // any code depends on which path computed them; an all-zero block gets
+    // the code 0 either way.  So the fast codes are the exact ones unless
+    // some lane has s out of range, |q0| >= 2^126, or a block maximum in
+    // (0, 2^-74); the outlier value (stored itself, in bf16) needs |qo| in
+    // [2^-78, 2^126) or qo = +-0.  If any of the wave's lanes fails, the
+    // wave redoes the row with the correctly rounded division.
+    auto process_row = [&](u32x4 w, int r, __amdgpu_buffer_rsrc_t rxo, __amdgpu_buffer_rsrc_t ras) {
         if constexpr (GELU) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) w[i] = gelu_bf16x2(w[i]);
@@ -230,49 +244,79 @@ __global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restr
             for (int i = 0; i < 4; ++i)
                 mx[i] = __builtin_elementwise_max(mx[i], __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
         }
-        const bool fast = s_ok & bf16x8_in_fast_range(w);
-        float x[8], q[8];
+        float q[8];
+        float a0 = 0.0f, aq = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t m = w[i] & keepw[i];
-            x[2 * i] = __uint_as_float(m << 16);
-            x[2 * i + 1] = __uint_as_float(m & 0xFFFF0000u);
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t wi = w[i >> 1];
+            const float x = __uint_as_float((i & 1) ? (wi & 0xFFFF0000u) : (wi << 16));
+            const float q0 = x * rz[i];
+            const float t = __builtin_fmaf(q0, sv[i], -x);
+            q[i] = __builtin_fmaf(-t, rz[i], q0);
+            a0 = fmaxf(a0, __builtin_fabsf(q0));
+            aq = fmaxf(aq, __builtin_fabsf(q[i]));
         }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = div_fast(x[i], sv[i], rv[i]);
-        if (!fast) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) q[i] = __fdiv_rn(x[i], sv[i]);
-        }
+        uint32_t qb = quad_max_bits(__float_as_uint(aq));
+        // lanes failing a check, as wave masks (one compare each)
+        uint64_t bad = __builtin_amdgcn_uicmp(__float_as_uint(a0), a0_lim, kCmpUGE) |
+                       __builtin_amdgcn_uicmp(qb - 1u, kF32PowM74 - 1u, kCmpULT);
+        float xo = 0.0f, qo = 0.0f;
         if (wave_o) {
             // the first outlier channel's own (unmasked) value from the raw words
             uint32_t wo = w[0];
 #pragma unroll
             for (int i = 1; i < 4; ++i) wo = (oc0 >> 1) == i ? w[i] : wo;
-            const float xo = __uint_as_float((oc0 & 1) ? (wo & 0xFFFF0000u) : (wo << 16));
-            const float qo = fast ? div_fast(xo, so, ro) : __fdiv_rn(xo, so);
-            const __amdgpu_buffer_rsrc_t rxo = rsrc(po, live ? rowXO : 0u);
-            if (omask) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_rne(qo), rxo, offXO, 0, 0);
+            xo = __uint_as_float((wo << osh) & 0xFFFF0000u);
+            qo = div_fast(xo, so, ro);
+            const uint32_t ab = __float_as_uint(qo) & 0x7FFFFFFFu;
+            // lanes without an outlier hold +-0 or a harmless value here: only those with one count
+            bad |= __builtin_amdgcn_uicmp(omask ? ab - kF32PowM78 : 0u, kF32Pow126 - kF32PowM78, kCmpUGE) &
+                   __builtin_amdgcn_uicmp(ab, 0u, kCmpNE);
+        }
+        if (bad) {
+            aq = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t wi = w[i >> 1];
+                const float x = (omask >> i) & 1u ? 0.0f : __uint_as_float((i & 1) ? (wi & 0xFFFF0000u) : (wi << 16));
+                q[i] = __fdiv_rn(x, sv[i]);
+                aq = fmaxf(aq, __builtin_fabsf(q[i]));
+            }
+            qb = quad_max_bits(__float_as_uint(aq));
+            if (wave_o) qo = __fdiv_rn(xo, so);
+        }
+        const uint32_t rb = 16u * (uint32_t)r;    // the row's 16 bytes in the wave's part of the group
+        if (wave_o) {
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_rne(qo), rxo, offXO + rb, 0, 0);
             if (wave_rest) {
-                // further outlier channels of the lane (two or more in its 8)
+                // further outlier channels of the lane (two or more in its 8): exact division
                 for (uint32_t mm = omask_rest; mm; mm &= mm - 1) {
                     const int i = __builtin_ctz(mm);
                     const int jl = lane * 8 + i;
                     const uint32_t wi = w[i >> 1];
                     const float xi = __uint_as_float((i & 1) ? (wi & 0xFFFF0000u) : (wi << 16));
-                    const float si = t_s[jl];
-                    const float qi = fast ? div_fast(xi, si, t_r[jl]) : __fdiv_rn(xi, si);
+                    const float qi = __fdiv_rn(xi, t_s[jl]);
                     __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_rne(qi), rxo,
-                                                          frag_lane_off(2u * (uint32_t)t_p[jl]), 0, 0);
+                                                          frag_lane_off(2u * (uint32_t)t_p[jl]) + rowpart + rb, 0,
+                                                          0);
                 }
             }
         }
-        uint32_t c;
-        const uint32_t word = encode8(q, c);
-        *reinterpret_cast<uint32_t*>(stgw + (m & 7) * kStgRow + 4 * lane) = word;
-        if (pad_wg) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)0, rsrc(po, live ? rowXO : 0u), offPad, 0, 0);
-        if ((lane & 3) == 0)
-            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)c, rsrc(ps, (uint32_t)kScBlocks), offAs, 0, 0);
+        // E8M0 code c = max(e - 2, 0) of the block maximum's biased exponent e,
+        // and its scale 2^(c - 127) as the converter takes it (exponent field c)
+        const int32_t sb = __builtin_elementwise_max((int32_t)(qb & 0x7F800000u) - (2 << 23), 0x00200000);
+        const float scale = __int_as_float(sb);
+        uint32_t word = 0;
+        MG_CVT_FP4X2(word, q[0], q[1], scale, 0);
+        MG_CVT_FP4X2(word, q[2], q[3], scale, 1);
+        MG_CVT_FP4X2(word, q[4], q[5], scale, 2);
+        MG_CVT_FP4X2(word, q[6], q[7], scale, 3);
+        *reinterpret_cast<uint32_t*>(stgw + r * kStgRow + 4 * lane) = word & nkeep;
+        if (pad_wg) {
+            const uint32_t offPad = lane < kp16 - k ? frag_lane_off(2u * (uint32_t)(k + lane)) : kNoStore;
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)0, rxo, offPad + rowpart + rb, 0, 0);
+        }
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(sb >> 23), ras, offAs + rb, 0, 0);
     };
 
     // 32-row groups G = blockIdx.y, blockIdx.y + gridDim.y, ...; wave w takes
@@ -291,43 +335,38 @@ __global__ void __launch_bounds__(256) quant_bf16_kernel(const uint16_t* __restr
     const int GA = (int)((M + 31) / 32);                                  // groups with Aq / XO pieces
     const int gstride = (int)gridDim.y;
     const int64_t win_stride = sc_nwin(K) * kScWinBytes;     // bytes between 256-row groups of As
-    static_assert(kScRows == 256, "row group = m >> 8");
+    static_assert(kScRows == 256, "8 row groups per scale group");
     uint8_t* const asw = As + (int64_t)blockIdx.x * kScWinBytes;
-    // the store lanes' staged pieces and their offsets inside the row group's blocks
-    uint32_t srd[2], sof[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int line = 8 * t + (lane >> 3), sl = line >> 1, hf = line & 1, rr = lane & 7;
-        srd[t] = (uint32_t)(rr * kStgRow + sl * 32 + hf * 16);
-        sof[t] = (uint32_t)((blockIdx.x * 8 + sl) * 1024 + 16 * (wave * 8 + rr + 32 * hf));
-    }
-    // the next group's 8 rows are loaded before the current group is processed
-    auto load8 = [&](int g, u32x4 (&xr)[8]) {
-        const int64_t m0 = (int64_t)g * 32 + wave * 8;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) xr[r] = load_row(X + (m0 + r) * K, g < ngr && m0 + r < M);
+    uint8_t* const XOb = reinterpret_cast<uint8_t*>(XO);
+    const uint32_t xo_group = (uint32_t)nso * 1024u;                      // XO bytes of a 32-row group
+    // rows of group g: row r of the wave's 8, as a load through its own resource
+    auto load_group_row = [&](int g, int r) -> u32x4 {
+        const int64_t m = (int64_t)g * 32 + wave * 8 + r;
+        return load_row(X + m * K, g < ngr && m < M);
     };
-    u32x4 xn[8];
-    load8((int)blockIdx.y, xn);
+    u32x4 xa[4], xb[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) xa[r] = load_group_row((int)blockIdx.y, r);
     for (int G = (int)blockIdx.y; G < ngr; G += gstride) {
-        const int64_t m0 = (int64_t)G * 32 + wave * 8;
-        u32x4 xr[8];
+        const bool live = G < GA;
+        const __amdgpu_buffer_rsrc_t rxo = rsrc(XOb + (int64_t)G * xo_group, live ? xo_group : 0u);
+        const __amdgpu_buffer_rsrc_t ras = rsrc(asw + (int64_t)(G >> 3) * win_stride + (G & 7) * 512, 512u);
 #pragma unroll
-        for (int r = 0; r < 8; ++r) xr[r] = xn[r];
-        if (G + gstride < ngr) load8(G + gstride, xn);
+        for (int r = 0; r < 4; ++r) xb[r] = load_group_row(G, 4 + r);
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int64_t m = m0 + r;
-            process_row(xr[r], m, asw + (m >> 8) * win_stride + (m & 255) * kScBlocks, G < GA);   // 256-row groups
-        }
-        if (G < GA) {
-            // the row group's blocks from a 64-bit base (Aq may exceed 4 GiB);
-            // slices past the row's (ns4) fall outside the range and are dropped
+        for (int r = 0; r < 4; ++r) process_row(xa[r], r, rxo, ras);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) xa[r] = load_group_row(G + gstride, r);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) process_row(xb[r], 4 + r, rxo, ras);
+        if (live) {
             const __amdgpu_buffer_rsrc_t rg = rsrc(Aq + (int64_t)G * ns4 * 1024, (uint32_t)ns4 * 1024u);
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const u32x4 v = *reinterpret_cast<const u32x4*>(stgw + srd[t]);
-                __builtin_amdgcn_raw_buffer_store_b128(v, rg, sof[t], 0, 0);
+                const int line = 8 * t + (lane >> 3), sl = line >> 1, hf = line & 1, rr = lane & 7;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(stgw + rr * kStgRow + sl * 32 + hf * 16);
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    v, rg, (uint32_t)((blockIdx.x * 8 + sl) * 1024 + 16 * (wave * 8 + rr + 32 * hf)), 0, 2);
             }
         }
     }
