@@ -13,6 +13,8 @@ Prints ONE JSON line.  `value` = 2*M*K*N / (time of one whole step), in
 TFLOP/s; the dual-GEMM kernel's own rate is in `roofline`.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py --power-probe S   also board power (hwmon) while the GEMM and the
+                                 quantize each run back to back for S seconds
     python bench.py --suite      one JSON line per configuration point: the
                                  480p up/down-projections (three weight-scale
                                  layouts, raw, smoothed and percentile outlier
@@ -105,6 +107,76 @@ def _cpu_baseline(layer, threadpool_info, w, X, W, rows: int) -> dict:
 
 
 COPY_BYTES = 256 << 20            # plain copy used to calibrate the HBM byte counters
+
+
+def _hwmon_power_files() -> tuple[str | None, str | None]:
+    """The GPU's board power reading and cap (microwatts) from the amdgpu hwmon
+    sysfs files, when this host exposes them."""
+    import glob
+    for d in sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*")):
+        inp = next((os.path.join(d, f) for f in ("power1_input", "power1_average")
+                    if os.path.exists(os.path.join(d, f))), None)
+        if inp:
+            cap = os.path.join(d, "power1_cap")
+            return inp, cap if os.path.exists(cap) else None
+    return None, None
+
+
+def power_probe(seconds: float, runs: dict) -> dict:
+    """Board power while each of `runs` (name -> launch function) runs back to
+    back for `seconds`, sampled every 20 ms from a host thread (the first
+    0.3 s of each run, while the clock settles, is left out), and at idle."""
+    import threading
+
+    import numpy as np
+    import torch
+
+    inp, cap = _hwmon_power_files()
+    if inp is None:
+        return {"available": False}
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                samples.append((time.perf_counter(), int(open(inp).read()) / 1e6))
+            except (OSError, ValueError):
+                pass
+            stop.wait(0.02)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    out = {"available": True, "source": inp}
+    if cap:
+        out["cap_w"] = int(open(cap).read()) / 1e6
+    torch.cuda.synchronize()
+    time.sleep(1.0)
+    windows = {"idle": (time.perf_counter() - 0.7, time.perf_counter())}
+    for name, fn in runs.items():
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        n = 0
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(20):
+                fn()
+            n += 20
+            torch.cuda.synchronize()
+        e1.record()
+        e1.synchronize()
+        windows[name] = (t0 + 0.3, time.perf_counter())
+        out[name + "_us"] = round(e0.elapsed_time(e1) * 1e3 / n, 1)
+        out[name + "_launches"] = n
+        time.sleep(1.0)
+    stop.set()
+    th.join()
+    for name, (a, b) in windows.items():
+        v = [w for t, w in samples if a <= t <= b]
+        out[name + "_w"] = round(float(np.mean(v)), 1) if v else None
+        out[name + "_samples"] = len(v)
+    return out
 
 
 def summarize_pmc(fetch_csv: str, write_csv: str, out_json: str) -> dict:
@@ -440,6 +512,9 @@ def main() -> int:
                          "10-20 s of CPU work)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run a plain device copy of 256 MiB (HBM counter calibration)")
+    ap.add_argument("--power-probe", type=float, default=0.0, metavar="SECONDS",
+                    help="after the timed steps, run the dual GEMM and then the quantize back to back for "
+                         "SECONDS each while sampling board power (hwmon); adds a `power` object")
     ap.add_argument("--suite", action="store_true",
                     help="one JSON line per configuration point (see the module docstring)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -555,6 +630,9 @@ def main() -> int:
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
+    if args.power_probe > 0:
+        out["power"] = power_probe(args.power_probe, {"gemm": lambda: mg.mg_dual_gemm(plan, act, Y),
+                                                      "quant": lambda: mg.mg_quantize_act(plan, X, act)})
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, X_h, W_h, args.cpu_rows if 0 < args.cpu_rows < M else M)
     print(json.dumps(out), flush=True)
