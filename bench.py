@@ -251,15 +251,23 @@ def _suite_tools():
 
     def timed(fn, reps=10, warmup=20, cold=False):
         """mean ms of fn() over reps launches after `warmup` untimed ones (the
-        first ~10-20 launches after a pause run up to ~10% slower), HIP events on
-        the current stream; cold: a 1 GiB write before each launch, outside the
-        timed interval."""
+        clock settles over the first launches after a pause), HIP events on the
+        current stream around the reps launches back to back; cold: a 1 GiB
+        write before each launch, outside its own pair of events."""
         for _ in range(warmup):
             fn()
+        if not cold:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                fn()
+            b.record(stream)
+            b.synchronize()
+            return a.elapsed_time(b) / reps
         ts = []
         for _ in range(reps):
-            if cold:
-                scratch.fill_(1.0)
+            scratch.fill_(1.0)
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record(stream)
