@@ -103,3 +103,20 @@ def test_every_bf16_at_plan_and_random_scales():
         s = np.exp2(g.uniform(-30.0, 0.0, K)).astype(np.float32)
         print(f"[encoder] small scale set {i}: s in [{s.min():.3g}, {s.max():.3g}]", flush=True)
         _run(Xsd, Xs, s)
+
+
+def test_large_quotients_take_the_exact_division():
+    """Quotients of 2^126 and more: every finite bf16 below 2^127 under
+    scales in [0.5, 1) (quotients up to just below 2^128, all finite).  The
+    kernel's fast division is used only while |x * RN(1/s)| < 2^126, so the
+    rows holding these values go through the correctly rounded division; Aq /
+    As must still be the oracle's bit for bit."""
+    X = every_bf16_in_setter_blocks(emax=253)
+    Xd = dev(X)
+    g = np.random.default_rng(4242)
+    for i in range(2):
+        s = g.uniform(0.5, 1.0, K).astype(np.float32)
+        q = np.abs(layer.as_f32(X).astype(np.float64)) / s.astype(np.float64)[None, :]
+        assert q.max() >= 2.0 ** 126 and np.isfinite(q.astype(np.float32)).all()
+        print(f"[encoder] large-quotient set {i}: s in [{s.min():.3g}, {s.max():.3g}]", flush=True)
+        _run(Xd, X, s)
