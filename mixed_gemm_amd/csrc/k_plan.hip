@@ -173,7 +173,8 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const float* __restr
 // ---------------------------------------------------------------------------- fold + pack
 
 constexpr int kFoldWaves = 4;
-constexpr int kFoldWavesPerCU = 32;
+constexpr int kFoldStgRow = 272;      // LDS staging row of Wq codes: 256 bytes + 16 pad (conflict-free writes)
+typedef uint32_t u32x4f __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float quad_max_f(float v) {
     // max over the 4 lanes of a quad (one 32-block): quad_perm [1,0,3,2] then [2,3,0,1]
@@ -286,36 +287,66 @@ __global__ void __launch_bounds__(256) fold_pack_kernel(const void* __restrict__
     // the last 32-byte slice, whose pad half gets the zero codes) and, from
     // one lane per quad, the block's scale code (every lane of rows < Np: past
     // K or N the code 0 of an all-zero block)
-    auto encode_store = [&](int64_t n, const float (&f)[8], uint32_t c) {
+    auto encode_word = [&](const float (&f)[8], uint32_t c) {
         const float scale = e8m0_to_f32(c);
         uint32_t word = 0;
         MG_CVT_FP4X2(word, f[0], f[1], scale, 0);
         MG_CVT_FP4X2(word, f[2], f[3], scale, 1);
         MG_CVT_FP4X2(word, f[4], f[5], scale, 2);
         MG_CVT_FP4X2(word, f[6], f[7], scale, 3);
+        return word;
+    };
+    auto encode_store = [&](int64_t n, const float (&f)[8], uint32_t c) {
+        const uint32_t word = encode_word(f, c);
         if (j0 < 64 * ns4 && n < N) *reinterpret_cast<uint32_t*>(Wq + frag_offset(n, j0 / 2, ns4)) = word;
         if ((lane & 3) == 0) Ws[sc_offset(n, j0 / 32, nwin)] = (uint8_t)(valid ? c : 0u);   // a short stripe's pads: 0
     };
 
     const int64_t wstride = (int64_t)gridDim.y * kFoldWaves;
-    if constexpr (LAY == MG_W_1X32) {
-        for (int64_t n = (int64_t)blockIdx.y * kFoldWaves + wave; n < Np; n += wstride) {
-            float f[8];
-            fold_row(n, f);
-            const float amax = quad_max_f(extract(n, f));
-            encode_store(n, f, e8m0_from_amax_bits(__float_as_uint(amax)));
-        }
-    } else if constexpr (LAY == MG_W_128X1) {
-        const int ns = (K + 127) / 128;
-        for (int64_t n = (int64_t)blockIdx.y * kFoldWaves + wave; n < Np; n += wstride) {
-            float f[8];
-            fold_row(n, f);
-            float amax = quad_max_f(extract(n, f));
-            amax = fmaxf(amax, __shfl_xor(amax, 4, 64));      // the stripe's 4 quads (16 lanes)
-            amax = fmaxf(amax, __shfl_xor(amax, 8, 64));
-            const uint32_t c = e8m0_from_amax_bits(__float_as_uint(amax));
-            encode_store(n, f, c);
-            if (valid && n < N && (lane & 15) == 0) Wst[n * ns + j0 / 128] = (uint8_t)c;
+    if constexpr (LAY == MG_W_1X32 || LAY == MG_W_128X1) {
+        // 32-row groups G = blockIdx.y, blockIdx.y + gridDim.y, ... through the
+        // last scale group; wave w takes rows 32 G + 8 w .. + 7, all 8 loaded
+        // before any is folded.  The wave's 8 rows fill whole 128-byte lines of
+        // Wq's fragment blocks (8 rows x 16 bytes of one slice half), so it
+        // stages its codes in its own LDS rows and stores them as 16 full lines
+        // (two 1 KB stores; lane L of store t takes row L % 8 of line 8 t + L / 8
+        // = (slice, half)); no wave reads another's staging, so no barrier.
+        __shared__ __attribute__((aligned(16))) uint8_t stg[kFoldWaves * 8 * kFoldStgRow];
+        uint8_t* const stgw = stg + wave * 8 * kFoldStgRow;
+        const int64_t NG = (int64_t)N / 32, NGp = Np / 32;
+        const int ns_str = (K + 127) / 128;
+        for (int64_t G = blockIdx.y; G < NGp; G += gridDim.y) {
+            const int64_t n0 = G * 32 + wave * 8;
+            float f[8][8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) fold_row(n0 + r, f[r]);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const int64_t n = n0 + r;
+                float amax = quad_max_f(extract(n, f[r]));
+                if constexpr (LAY == MG_W_128X1) {
+                    amax = fmaxf(amax, __shfl_xor(amax, 4, 64));      // the stripe's 4 quads (16 lanes)
+                    amax = fmaxf(amax, __shfl_xor(amax, 8, 64));
+                }
+                const uint32_t c = e8m0_from_amax_bits(__float_as_uint(amax));
+                const uint32_t word = encode_word(f[r], c);
+                *reinterpret_cast<uint32_t*>(stgw + r * kFoldStgRow + 4 * lane) = word;
+                if ((lane & 3) == 0) Ws[sc_offset(n, j0 / 32, nwin)] = (uint8_t)(valid ? c : 0u);
+                if constexpr (LAY == MG_W_128X1) {
+                    if (valid && n < N && (lane & 15) == 0) Wst[n * ns_str + j0 / 128] = (uint8_t)c;
+                }
+            }
+            if (G < NG) {
+                const __amdgpu_buffer_rsrc_t rg = make_rsrc(Wq + G * ns4 * kFragBlock, (uint64_t)ns4 * kFragBlock);
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int line = 8 * t + (lane >> 3), sl = line >> 1, hf = line & 1, rr = lane & 7;
+                    const uint4 v = *reinterpret_cast<const uint4*>(stgw + rr * kFoldStgRow + sl * 32 + hf * 16);
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        __builtin_bit_cast(u32x4f, v), rg,
+                        (uint32_t)((blockIdx.x * 8 + sl) * kFragBlock + 16 * (wave * 8 + rr + 32 * hf)), 0, 2);
+                }
+            }
         }
     } else {
         // 32-row groups through the last scale group (N % 32 == 0: the groups
@@ -376,15 +407,19 @@ hipError_t launch_fold_pack(const void* W, int32_t dtype, int32_t N, int32_t K, 
     const bool tile = layout == MG_W_32X32;
     const bool stripe = layout == MG_W_128X1;
     const int64_t gx = ((int64_t)K / 8 + 63) / 64;
-    const int64_t units = tile ? ((int64_t)N + 31) / 32 : (int64_t)N;   // rows, or 32-row groups
-    int64_t gy = (units + kFoldWaves - 1) / kFoldWaves;
-    int64_t cap = (int64_t)device_cu_count() * (kFoldWavesPerCU / kFoldWaves) / gx;
-    if (cap < 1) cap = 1;
-    if (gy > cap) gy = cap;
-    if (gy > 65535) gy = 65535;
-    dim3 grid((unsigned)gx, (unsigned)gy);
+    // 32x32: a wave per 32-row group; otherwise a workgroup per 32-row group
+    const int64_t groups = ((int64_t)N + kScRows - 1) / kScRows * (kScRows / 32);
+    int64_t gy = tile ? (groups + kFoldWaves - 1) / kFoldWaves : groups;
+    // one resident round of workgroups
 #define MG_FOLD_LAUNCH(BFV, LAYV)                                                                          \
-    hipLaunchKernelGGL((fold_pack_kernel<BFV, LAYV>), grid, dim3(256), 0, st, W, N, K, k, s, pos, Wq, Ws, Wst, WO)
+    do {                                                                                                   \
+        const void* kern = reinterpret_cast<const void*>(fold_pack_kernel<BFV, LAYV>);                     \
+        int64_t cap = (int64_t)device_cu_count() * blocks_per_cu(kern) / gx;                               \
+        cap = cap < 1 ? 1 : cap;                                                                           \
+        const int64_t gyl = gy > cap ? cap : (gy > 65535 ? 65535 : gy);                                    \
+        hipLaunchKernelGGL((fold_pack_kernel<BFV, LAYV>), dim3((unsigned)gx, (unsigned)gyl), dim3(256), 0, st, \
+                           W, N, K, k, s, pos, Wq, Ws, Wst, WO);                                           \
+    } while (0)
     if (bf) {
         if (tile) MG_FOLD_LAUNCH(true, MG_W_32X32);
         else if (stripe) MG_FOLD_LAUNCH(true, MG_W_128X1);

@@ -441,22 +441,6 @@ __global__ void __launch_bounds__(256) quant_f32_kernel(const float* __restrict_
 
 }  // namespace
 
-// Workgroups of kernel `kern` that fit on one CU (registers, LDS), looked
-// up once per device and kernel.
-static int blocks_per_cu(const void* kern) {
-    struct Entry { const void* k; int dev; int n; };
-    static thread_local Entry cache[8] = {};
-    static thread_local int used = 0;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 1;
-    for (int i = 0; i < used; ++i)
-        if (cache[i].k == kern && cache[i].dev == dev) return cache[i].n;
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, 256, 0) != hipSuccess || n < 1) n = 1;
-    if (used < 8) cache[used++] = Entry{kern, dev, n};
-    return n;
-}
-
 template <typename F, typename... A>
 static void launch_rows(F* kern, int64_t M, int64_t gx, hipStream_t st, A... args) {
     // one resident round of workgroups; each takes 32-row groups through the

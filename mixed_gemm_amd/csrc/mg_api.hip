@@ -114,6 +114,20 @@ int fail_msg(int code, const char* fmt, ...) {
     return code;
 }
 
+int blocks_per_cu(const void* kern) {
+    struct Entry { const void* k; int dev; int n; };
+    static thread_local Entry cache[32] = {};
+    static thread_local int used = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 1;
+    for (int i = 0; i < used; ++i)
+        if (cache[i].k == kern && cache[i].dev == dev) return cache[i].n;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, 256, 0) != hipSuccess || n < 1) n = 1;
+    if (used < 32) cache[used++] = Entry{kern, dev, n};
+    return n;
+}
+
 int device_cu_count() {
     static thread_local int cached_dev = -1;
     static thread_local int cached_cus = 0;

@@ -83,6 +83,10 @@ hipError_t launch_pct_select(int32_t K, int pass, double q, uint32_t* hist, int3
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 
+// Workgroups of 256 threads of kernel `kern` that fit on one CU (registers,
+// LDS), looked up once per device and kernel.
+int blocks_per_cu(const void* kern);
+
 // Every argument check of mg_forward except the activation workspace (plan,
 // dtypes, M, X, Y, operand sizes); MG_OK or the error (message set).
 int check_forward(const mg_plan* p, const void* X, int32_t dtype, int64_t M, const void* Y, int32_t y_dtype);
