@@ -428,12 +428,19 @@ def suite(args) -> int:
             mg.mg_gelu_quantize_act(blk.plan2, Y0, a2)
             mg.mg_dual_gemm(blk.plan2, a2, Y2)
 
+        def run_block_epilogue():     # GELU and ffn.2's quantize in ffn.0's GEMM epilogue
+            mg.mg_quantize_act(blk.plan0, X5, a0)
+            mg.mg_dual_gemm_gelu_quant(blk.plan0, a0, blk.plan2, a2)
+            mg.mg_dual_gemm(blk.plan2, a2, Y2)
+
         def run_block_unfused():
             mg.mg_forward(blk.plan0, X5, a0, Y0)
             mg.mg_gelu_tanh_bf16(Y0, h)
             mg.mg_forward(blk.plan2, h, a2, Y2)
         t_block = timed(run_block, reps=5)
         t_block_unfused = timed(run_block_unfused, reps=5)
+        t_block_epi = timed(run_block_epilogue, reps=5)
+        t_g0q = timed(lambda: mg.mg_dual_gemm_gelu_quant(blk.plan0, a0, blk.plan2, a2))
         t_gq = timed(lambda: mg.mg_gelu_quantize_act(blk.plan2, Y0, a2))
         t_g0 = timed(lambda: mg.mg_dual_gemm(blk.plan0, a0, Y0))
         t_gelu = timed(lambda: mg.mg_gelu_tanh_bf16(Y0, h))
@@ -445,6 +452,9 @@ def suite(args) -> int:
                           "alpha": [w0.alpha, w2.alpha], "weight_blocks": lay, "output": "bf16"},
                "block_ms": round(t_block, 4), "block_tflops": round((fl0 + fl2) / t_block / 1e9, 1),
                "block_ms_unfused_gelu": round(t_block_unfused, 4),
+               "block_ms_gemm_epilogue": round(t_block_epi, 4),
+               "ffn0_gemm_ms": round(t_g0, 4),
+               "ffn0_gemm_gelu_quant_ms": round(t_g0q, 4),
                "gelu_quant_ms": round(t_gq, 4),
                "gelu_quant_gbs": round((M * w2.K * 2.53125 + 2 * M * w2.k) / t_gq / 1e6, 1),
                "ffn0_gemm_tflops": round(fl0 / t_g0 / 1e9, 1), "ffn2_gemm_tflops": round(fl2 / t_g2 / 1e9, 1),

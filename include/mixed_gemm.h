@@ -308,6 +308,20 @@ int mg_gelu_tanh_bf16(const uint16_t* in, uint16_t* out, int64_t n, hipStream_t 
  * Same arguments and errors as mg_quantize_act with dtype MG_BF16. */
 int mg_gelu_quantize_act(const mg_plan* p, const uint16_t* Y, int64_t M, const mg_act* a, hipStream_t stream);
 
+/* The FFN block's two projections joined in the first one's GEMM epilogue
+ * ("W4A4 Quantization for Inference on Wan2.2-I2V-A14B": the integration
+ * paragraph -- FFN inputs after the GELU gate are quantized like every
+ * linear input -- and Eq. (5) for the first projection): mg_dual_gemm of
+ * plan p0 on the workspace a0 (M rows), whose bf16 output is never written;
+ * instead each output tile goes through GELU-tanh and the second
+ * projection's quantizer (plan p2, p2->d.K == p0->d.N) into a2.  a2 holds bit
+ * for bit what mg_dual_gemm(p0, a0, M, Y, MG_BF16) followed by
+ * mg_gelu_quantize_act(p2, Y, M, a2) writes, including every pad byte.
+ * Device pointers as in those calls; errors: theirs, and MG_ERR_SHAPE when
+ * p2->d.K != p0->d.N.  a2 must not overlap a0 or the plans. */
+int mg_dual_gemm_gelu_quant(const mg_plan* p0, const mg_act* a0, int64_t M, const mg_plan* p2, const mg_act* a2,
+                            hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

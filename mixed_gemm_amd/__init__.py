@@ -64,7 +64,7 @@ EXPORTS = ("mg_version", "mg_last_error", "mg_plan_bytes", "mg_act_bytes", "mg_c
            "mg_calib_act", "mg_weight_range", "mg_smooth_scales", "mg_outlier_set", "mg_fold_pack",
            "mg_plan_build", "mg_quantize_act", "mg_dual_gemm", "mg_forward", "mg_gelu_tanh_bf16",
            "mg_gelu_quantize_act", "mg_pct_reset", "mg_pct_count", "mg_pct_select", "mg_quantize_act_stats",
-           "mg_forward_noalloc")
+           "mg_forward_noalloc", "mg_dual_gemm_gelu_quant")
 
 _lib = None
 
@@ -96,6 +96,7 @@ def lib() -> ctypes.CDLL:
             "mg_forward_noalloc": ([P(mg_plan), vp, i32, i64, vp, i32, vp], ctypes.c_int),
             "mg_gelu_tanh_bf16": ([vp, vp, i64, vp], ctypes.c_int),
             "mg_gelu_quantize_act": ([P(mg_plan), vp, i64, P(mg_act), vp], ctypes.c_int),
+            "mg_dual_gemm_gelu_quant": ([P(mg_plan), P(mg_act), i64, P(mg_plan), P(mg_act), vp], ctypes.c_int),
             "mg_quantize_act_stats": ([P(mg_plan), vp, i32, i64, P(mg_act), vp, vp], ctypes.c_int),
             "mg_pct_reset": ([P(mg_pct), vp], ctypes.c_int),
             "mg_pct_count": ([P(mg_pct), i32, vp, i64, vp], ctypes.c_int),
@@ -425,6 +426,17 @@ def mg_gelu_quantize_act(plan: Plan, Y: torch.Tensor, act: Act, stream=None) -> 
     _check(lib().mg_gelu_quantize_act(ctypes.byref(p), _ptr(Y), Y.shape[0], ctypes.byref(a), _stream(stream)))
 
 
+def mg_dual_gemm_gelu_quant(plan0: Plan, act0: Act, plan2: Plan, act2: Act, stream=None) -> None:
+    """plan0's dual GEMM whose epilogue applies GELU to the bf16 output and
+    quantizes it for plan2 into act2 (the output itself is never written)."""
+    _need(plan2.desc.K == plan0.desc.N, f"plan2's K={plan2.desc.K} must equal plan0's N={plan0.desc.N}")
+    _check_act(plan0.desc, act0)
+    _check_act(plan2.desc, act2, act0.M)
+    p0, a0, p2, a2 = plan0.c(), act0.c(), plan2.c(), act2.c()
+    _check(lib().mg_dual_gemm_gelu_quant(ctypes.byref(p0), ctypes.byref(a0), act0.M, ctypes.byref(p2),
+                                         ctypes.byref(a2), _stream(stream)))
+
+
 class PctState:
     """Device state of one percentile calibration run: hist [K][256] u32
     counts (stored as int32) and sel [K][2] (selected high byte, rank)."""
@@ -627,14 +639,22 @@ def ffn_block_plans(act0: torch.Tensor, act2: torch.Tensor, W0: torch.Tensor, W2
 
 
 @_on_stream
-def ffn_block_forward(blk: FFNBlock, X: torch.Tensor, stream=None) -> torch.Tensor:
+def ffn_block_forward(blk: FFNBlock, X: torch.Tensor, stream=None, epilogue: bool = False) -> torch.Tensor:
     """Y2 = ffn.2(gelu(ffn.0(X))): ffn.0's forward, then GELU and ffn.2's
     activation quantization in one pass (mg_gelu_quantize_act), then ffn.2's
-    dual GEMM."""
-    y0 = forward(blk.plan0, X, stream=stream)
+    dual GEMM; with epilogue=True the GELU and ffn.2's quantization run inside
+    ffn.0's GEMM epilogue (mg_dual_gemm_gelu_quant) and ffn.0's output is
+    never written.  Both give the same bits."""
     a2 = Act.empty(blk.plan2.desc, X.shape[0], X.device)
-    mg_gelu_quantize_act(blk.plan2, y0, a2, stream)
-    del y0
+    if epilogue:
+        a0 = Act.empty(blk.plan0.desc, X.shape[0], X.device)
+        mg_quantize_act(blk.plan0, X, a0, stream)
+        mg_dual_gemm_gelu_quant(blk.plan0, a0, blk.plan2, a2, stream)
+        del a0
+    else:
+        y0 = forward(blk.plan0, X, stream=stream)
+        mg_gelu_quantize_act(blk.plan2, y0, a2, stream)
+        del y0
     y2 = torch.empty((X.shape[0], blk.plan2.desc.N), dtype=torch.bfloat16, device=X.device)
     mg_dual_gemm(blk.plan2, a2, y2, stream)
     return y2

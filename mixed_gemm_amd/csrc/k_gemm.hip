@@ -77,6 +77,11 @@ namespace {
 // After a tile's last half-stage its 256x256 bf16 result is staged through
 // the two ring slots that hold no pending copy and written as whole 512-byte
 // rows while the next tile's first half-stage already sits in LDS.
+// A third epilogue (QuantOut) joins the FFN block's two projections: the
+// staged bf16 tile goes through GELU-tanh and the next projection's
+// activation quantizer (its channels are this tile's columns) instead of
+// being written, producing the bytes that the bf16 output followed by the
+// fused GELU + quantize pass would.
 // Operand rows past M (or N) and slices past K / k read as zeros through
 // buffer range checks.  Tiles are dealt so that each XCD (workgroups go
 // round-robin to the 8 XCDs) walks a contiguous run of the tile order,
@@ -144,7 +149,38 @@ struct GemmArgs {
     int64_t M;
     int32_t N, K, k;
     int32_t MT, NT;     // tile counts
+    // GELU + quantize epilogue (QuantOut): the next layer's plan (input width
+    // N) and activation workspace
+    const float* s2;
+    const float* rcp2;
+    const int32_t* pos2;
+    uint8_t* Aq2;
+    uint8_t* As2;
+    uint8_t* XO2;
+    int32_t k2;
 };
+
+// Output tag of the epilogue that applies GELU to the bf16-rounded tile and
+// quantizes it as the next layer's activation, instead of writing Y.
+struct QuantOut {};
+
+// Per-tile lane constants of the GELU + quantize epilogue: the lane's 8
+// channels' s, fast-path reciprocals (0 on outlier channels) and outlier
+// routing, and its byte offsets inside the tile's part of Aq, XO, As.
+struct QuantLane {
+    float sv[8], rz[8];
+    float so, ro;
+    uint32_t omask, nkeep, a0_lim;
+    uint32_t offAq, offXO, offAs, ns4, nso;
+    int oc0, cj0, wave_o, wave_rest;
+    bool valid;
+};
+
+// bytes of a buffer of `total` bytes from offset `from` on (0 past its end)
+__device__ __forceinline__ uint64_t rest_bytes(int64_t total, int64_t from) {
+    return total > from ? (uint64_t)(total - from) : 0u;
+}
+__device__ __forceinline__ uint64_t min_u64(uint64_t a, uint64_t b) { return a < b ? a : b; }
 
 // Origin of an output tile (wave-uniform).
 struct TileOrg {
@@ -399,13 +435,168 @@ dual_gemm_tiled(GemmArgs g) {
         stage_sync();
     };
 
+    // ---- GELU + quantize epilogue (QuantOut).  The staged bf16 tile is the
+    // next layer's input h = GELU(bf16(Y)) before the GELU: its columns are
+    // that layer's input channels.  A lane takes 8 consecutive channels of a
+    // row (one staged 16-byte piece), 4 lanes one 32-block, as in the
+    // activation quantizer, and produces the same bits as GELU-then-quantize
+    // of the bf16 output: the same GELU function, the quotient RN(h / s)
+    // (Markstein's correction under the quantizer's checks, else the
+    // correctly rounded division), E8M0 of the block maximum, the hardware
+    // E2M1 converter; outlier channels go to XO as bf16 and +0 into the bulk.
+    // Rows past M and channels past N are zeros (their accumulators are not
+    // the layer's); the codes of pad rows and pad slices land inside the
+    // buffers' pads, the rest outside the resources' ranges.
+    auto quant_lane = [&](const TileOrg& o, int cj0, bool cvalid, uint32_t ln) {
+        QuantLane L;
+        float rv[8];
+        int pv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { L.sv[i] = 1.0f; rv[i] = 1.0f; pv[i] = -1; }
+        if (cvalid) {
+#pragma unroll
+            for (int h4 = 0; h4 < 2; ++h4) {
+                const float4 a = *reinterpret_cast<const float4*>(g.s2 + cj0 + 4 * h4);
+                const float4 b = *reinterpret_cast<const float4*>(g.rcp2 + cj0 + 4 * h4);
+                const int4 c = *reinterpret_cast<const int4*>(g.pos2 + cj0 + 4 * h4);
+                L.sv[4 * h4] = a.x; L.sv[4 * h4 + 1] = a.y; L.sv[4 * h4 + 2] = a.z; L.sv[4 * h4 + 3] = a.w;
+                rv[4 * h4] = b.x; rv[4 * h4 + 1] = b.y; rv[4 * h4 + 2] = b.z; rv[4 * h4 + 3] = b.w;
+                pv[4 * h4] = c.x; pv[4 * h4 + 1] = c.y; pv[4 * h4 + 2] = c.z; pv[4 * h4 + 3] = c.w;
+            }
+        }
+        uint32_t om = 0;
+        bool s_ok = true;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            om |= (pv[i] >= 0 ? 1u : 0u) << i;
+            s_ok &= div_fast_ok_s(L.sv[i]);
+        }
+        L.omask = om;
+        L.nkeep = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            L.rz[i] = (om >> i) & 1u ? 0.0f : rv[i];
+            L.nkeep |= ((om >> i) & 1u ? 0u : 0xFu) << (4 * i);
+        }
+        const int oc0 = om ? __builtin_ctz(om) : 0;
+        L.oc0 = oc0;
+        L.so = L.sv[0]; L.ro = rv[0];
+        int op0 = pv[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) {
+            L.so = oc0 == i ? L.sv[i] : L.so;
+            L.ro = oc0 == i ? rv[i] : L.ro;
+            op0 = oc0 == i ? pv[i] : op0;
+        }
+        L.a0_lim = s_ok ? kF32Pow126 : 0u;
+        L.valid = cvalid;
+        L.cj0 = cj0;
+        L.wave_o = __builtin_amdgcn_readfirstlane((int)(__builtin_amdgcn_ballot_w64(om != 0) != 0));
+        L.wave_rest = __builtin_amdgcn_readfirstlane((int)(__builtin_amdgcn_ballot_w64((om & (om - 1)) != 0) != 0));
+        // byte offsets inside the tile's part of each buffer, the row's part
+        // (16 per row of the 32-row group, 1 KB blocks per group) added per row
+        const uint32_t ns4b = (uint32_t)frag_slices(N / 2), nsob = (uint32_t)frag_slices(2 * (int64_t)g.k2);
+        const uint32_t b = (uint32_t)cj0 / 2u;
+        L.offAq = (b >> 5) * 1024u + ((b >> 4) & 1u) * 512u + (b & 15u);
+        const uint32_t bo = 2u * (uint32_t)op0;
+        L.offXO = om ? (bo >> 5) * 1024u + ((bo >> 4) & 1u) * 512u + (bo & 15u) : OOB;
+        const int blk = cj0 / 32;
+        L.offAs = (ln & 3u) == 0u ? (uint32_t)(blk / kScBlocks) * kScWinBytes + (uint32_t)sc_pos(blk) : OOB;
+        L.ns4 = ns4b; L.nso = nsob;
+        return L;
+    };
+    // row piece of tile row mt (0..255): w the staged bf16 words (before GELU)
+    auto quant_octet = [&](const QuantLane& L, const TileOrg& o, u32x4 w, uint32_t mt) {
+        const int64_t m = o.m0 + mt;
+        const bool live = m < M && L.valid;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = live ? gelu_bf16x2(w[i]) : 0u;
+        const int wave_o = L.wave_o;
+        float q[8];
+        float a0 = 0.0f, aq = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t wi = w[i >> 1];
+            const float x = __uint_as_float((i & 1) ? (wi & 0xFFFF0000u) : (wi << 16));
+            const float q0 = x * L.rz[i];
+            const float t = __builtin_fmaf(q0, L.sv[i], -x);
+            q[i] = __builtin_fmaf(-t, L.rz[i], q0);
+            a0 = fmaxf(a0, __builtin_fabsf(q0));
+            aq = fmaxf(aq, __builtin_fabsf(q[i]));
+        }
+        uint32_t qb = quad_max_bits(__float_as_uint(aq));
+        uint64_t bad = __builtin_amdgcn_uicmp(__float_as_uint(a0), L.a0_lim, kCmpUGE) |
+                       __builtin_amdgcn_uicmp(qb - 1u, kF32PowM74 - 1u, kCmpULT);
+        float xo = 0.0f, qo = 0.0f;
+        if (wave_o) {
+            uint32_t wo = w[0];
+#pragma unroll
+            for (int i = 1; i < 4; ++i) wo = (L.oc0 >> 1) == i ? w[i] : wo;
+            xo = __uint_as_float((L.oc0 & 1) ? (wo & 0xFFFF0000u) : (wo << 16));
+            qo = div_fast(xo, L.so, L.ro);
+            const uint32_t ab = __float_as_uint(qo) & 0x7FFFFFFFu;
+            bad |= __builtin_amdgcn_uicmp(L.omask ? ab - kF32PowM78 : 0u, kF32Pow126 - kF32PowM78, kCmpUGE) &
+                   __builtin_amdgcn_uicmp(ab, 0u, kCmpNE);
+        }
+        if (bad) {
+            aq = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t wi = w[i >> 1];
+                const float x = (L.omask >> i) & 1u ? 0.0f : __uint_as_float((i & 1) ? (wi & 0xFFFF0000u) : (wi << 16));
+                q[i] = __fdiv_rn(x, L.sv[i]);
+                aq = fmaxf(aq, __builtin_fabsf(q[i]));
+            }
+            qb = quad_max_bits(__float_as_uint(aq));
+            if (wave_o) qo = __fdiv_rn(xo, L.so);
+        }
+        // the tile's row group and the row inside it
+        const uint32_t rg = mt >> 5, rin = (mt & 31u) << 4;
+        if (wave_o) {
+            // the row's 32-row group of XO (its nso blocks; none past the last group)
+            const int64_t xo0 = (o.m0 / 32 + rg) * (int64_t)L.nso * kFragBlock;
+            const __amdgpu_buffer_rsrc_t rxo = make_rsrc(
+                g.XO2 + xo0, min_u64(rest_bytes(frag_bytes(M, 2 * (int64_t)g.k2), xo0), (uint64_t)L.nso * kFragBlock));
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_rne(qo), rxo, L.offXO + rin, 0, 0);
+            // further outlier channels of the lane (two or more in its 8): exact division
+            if (L.wave_rest) {
+                for (uint32_t mm = L.omask & (L.omask - 1); mm; mm &= mm - 1) {
+                    const int i = __builtin_ctz(mm);
+                    const uint32_t wi = w[i >> 1];
+                    const float xi = __uint_as_float((i & 1) ? (wi & 0xFFFF0000u) : (wi << 16));
+                    const float qi = __fdiv_rn(xi, g.s2[L.cj0 + i]);
+                    const uint32_t bi = 2u * (uint32_t)g.pos2[L.cj0 + i];
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_rne(qi), rxo,
+                                                          (bi >> 5) * 1024u + ((bi >> 4) & 1u) * 512u + (bi & 15u) + rin,
+                                                          0, 0);
+                }
+            }
+        }
+        const int32_t sb = __builtin_elementwise_max((int32_t)(qb & 0x7F800000u) - (2 << 23), 0x00200000);
+        const float scale = __int_as_float(sb);
+        uint32_t word = 0;
+        MG_CVT_FP4X2(word, q[0], q[1], scale, 0);
+        MG_CVT_FP4X2(word, q[2], q[3], scale, 1);
+        MG_CVT_FP4X2(word, q[4], q[5], scale, 2);
+        MG_CVT_FP4X2(word, q[6], q[7], scale, 3);
+        const int64_t gb = o.m0 / 32 + rg;           // the row's 32-row group
+        // the row's 32-row group of Aq (its ns4 blocks: slices past them, of
+        // channels past the padded row, fall outside the range)
+        const int64_t aq0 = gb * (int64_t)L.ns4 * kFragBlock;
+        const __amdgpu_buffer_rsrc_t raq = make_rsrc(
+            g.Aq2 + aq0, min_u64(rest_bytes(frag_bytes(M, N / 2), aq0), (uint64_t)L.ns4 * kFragBlock));
+        __builtin_amdgcn_raw_buffer_store_b32(word & L.nkeep, raq, L.offAq + rin, 0, 0);
+        const __amdgpu_buffer_rsrc_t ras = make_rsrc(g.As2 + (o.m0 / kScRows) * sc_nwin(N) * kScWinBytes, (uint64_t)sc_nwin(N) * kScWinBytes);
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(sb >> 23), ras, L.offAs + mt * (uint32_t)kScBlocks, 0, 0);
+    };
+
     // ---- epilogue of one tile.  The MFMAs take the weight fragment as their
     // first operand, so acc[i][j] holds Y^T for A row-tile i and W row-tile j:
     // lane (l32, h), register 4 q + e holds output row 32 i + l32 and output
     // column 32 j + 8 q + 4 h + e of this wave's quarter -- four consecutive
     // columns per register group.
     auto epilogue = [&](const TileOrg& o, uint8_t* wbuf) {
-        if constexpr (sizeof(OutT) == 2) {
+        if constexpr (std::is_same_v<OutT, uint16_t> || std::is_same_v<OutT, QuantOut>) {
             // bf16: round pairs with the hardware converter (nearest even).
             // Each wave stages its own 128x128 quarter through its own 16 KB
             // of a free ring slot (wbuf), 64 rows x 256 B per pass, and writes the
@@ -432,6 +623,8 @@ dual_gemm_tiled(GemmArgs g) {
             const int gcol = o.n0 + wn * 128 + (int)cl * 8;
             const bool col_ok = gcol < N;
             const uint32_t cofs = (uint32_t)gcol * 2u;
+            [[maybe_unused]] QuantLane ql;
+            if constexpr (std::is_same_v<OutT, QuantOut>) ql = quant_lane(o, gcol, col_ok, (uint32_t)(et & 63u));
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
 #pragma unroll
@@ -453,19 +646,29 @@ dual_gemm_tiled(GemmArgs g) {
                             *reinterpret_cast<u32x2*>(wbuf + rb + ((((uint32_t)(4 * j + q)) ^ rs) << 4)) = w;
                         }
                 }
-                u32x4 v[16];
+                if constexpr (std::is_same_v<OutT, QuantOut>) {
+                    // row pieces of the staged bf16 rows (lane: 8 columns of a row), each
+                    // through GELU and the next layer's quantizer
+                    for (int sI = 0; sI < 16; ++sI) {
+                        const uint32_t rr = (uint32_t)(4 * sI) + rl;
+                        const u32x4 w = *reinterpret_cast<const u32x4*>(wbuf + rr * 256 + ((cl ^ (rr & 15u)) << 4));
+                        quant_octet(ql, o, w, (uint32_t)(wm * 128 + 64 * p) + rr);
+                    }
+                } else {
+                    u32x4 v[16];
 #pragma unroll
-                for (int sI = 0; sI < 16; ++sI) {
-                    const uint32_t rr = (uint32_t)(4 * sI) + rl;
-                    v[sI] = *reinterpret_cast<const u32x4*>(wbuf + rr * 256 + ((cl ^ (rr & 15u)) << 4));
-                }
+                    for (int sI = 0; sI < 16; ++sI) {
+                        const uint32_t rr = (uint32_t)(4 * sI) + rl;
+                        v[sI] = *reinterpret_cast<const u32x4*>(wbuf + rr * 256 + ((cl ^ (rr & 15u)) << 4));
+                    }
 #pragma unroll
-                for (int sI = 0; sI < 16; ++sI) {
-                    const uint32_t rr = (uint32_t)(4 * sI) + rl;
-                    const uint32_t off = col_ok ? ((uint32_t)(wm * 128 + 64 * p) + rr) * rowY + cofs : OOB;
-                    // streaming store (nt): Y is written once and must not
-                    // push the operand panels out of L2
-                    __builtin_amdgcn_raw_buffer_store_b128(v[sI], rY, off, 0, 2);
+                    for (int sI = 0; sI < 16; ++sI) {
+                        const uint32_t rr = (uint32_t)(4 * sI) + rl;
+                        const uint32_t off = col_ok ? ((uint32_t)(wm * 128 + 64 * p) + rr) * rowY + cofs : OOB;
+                        // streaming store (nt): Y is written once and must not
+                        // push the operand panels out of L2
+                        __builtin_amdgcn_raw_buffer_store_b128(v[sI], rY, off, 0, 2);
+                    }
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -581,8 +784,28 @@ hipError_t launch_dual_gemm(const uint8_t* Aq, const uint8_t* As, const uint16_t
                             int32_t N, int32_t K, int32_t k, void* Y, int32_t y_dtype,
                             hipStream_t st) {
     if (M <= 0) return hipSuccess;
-    GemmArgs a{Aq, As, XO, Wq, Ws, WO, Y, M, N, K, k, (int32_t)((M + TBM - 1) / TBM), (N + TBN - 1) / TBN};
+    GemmArgs a{Aq, As, XO, Wq, Ws, WO, Y, M, N, K, k, (int32_t)((M + TBM - 1) / TBM), (N + TBN - 1) / TBN,
+               nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0};
     return y_dtype == MG_BF16 ? launch_tiled<uint16_t>(a, st) : launch_tiled<float>(a, st);
+}
+
+hipError_t launch_dual_gemm_gelu_quant(const uint8_t* Aq, const uint8_t* As, const uint16_t* XO,
+                                       const uint8_t* Wq, const uint8_t* Ws, const uint16_t* WO, int64_t M,
+                                       int32_t N, int32_t K, int32_t k, const float* s2, const float* rcp2,
+                                       const int32_t* pos2, int32_t k2, uint8_t* Aq2, uint8_t* As2,
+                                       uint16_t* XO2, hipStream_t st) {
+    if (M <= 0) return hipSuccess;
+    // XO2 (its pad columns, and every outlier value of pad rows) and As2 (a
+    // last window half past N, when N % 512 != 0, belongs to no tile) start at 0
+    if (k2 > 0) {
+        hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(XO2), 0u, frag_bytes(M, 2 * (int64_t)k2) / 4, st);
+        if (e != hipSuccess) return e;
+    }
+    hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(As2), 0u, sc_bytes(M, N) / 4, st);
+    if (e != hipSuccess) return e;
+    GemmArgs a{Aq, As, XO, Wq, Ws, WO, nullptr, M, N, K, k, (int32_t)((M + TBM - 1) / TBM), (N + TBN - 1) / TBN,
+               s2, rcp2, pos2, Aq2, As2, reinterpret_cast<uint8_t*>(XO2), k2};
+    return launch_tiled<QuantOut>(a, st);
 }
 
 }  // namespace mg

@@ -50,21 +50,6 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 4;
 constexpr int kStgRow = 272;      // LDS staging row: 256 bytes of codes + 16 pad
 
-// f32 bit patterns of 2^126, 2^-74 and 2^-78 (the fast-division checks)
-constexpr uint32_t kF32Pow126 = 0x7E800000u, kF32PowM74 = 0x1A800000u, kF32PowM78 = 0x18800000u;
-// integer predicates of __builtin_amdgcn_uicmp (a wave mask of the lanes where
-// the unsigned comparison holds)
-constexpr int kCmpNE = 33, kCmpUGE = 35, kCmpULT = 36;
-
-// Max over the 4 lanes of a quad (one 32-block: quad_perm [1,0,3,2] then
-// [2,3,0,1]) of the bit patterns of non-negative f32 values, whose unsigned
-// integer order is their numeric order.
-__device__ __forceinline__ uint32_t quad_max_bits(uint32_t v) {
-    v = __builtin_elementwise_max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true));
-    v = __builtin_elementwise_max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true));
-    return v;
-}
-
 // E8M0 scale code c of the lane's 32-block and the packed E2M1 nibbles of its
 // 8 (masked) quotients (first value in the low nibble).
 __device__ __forceinline__ uint32_t encode8(const float (&q)[8], uint32_t& c) {

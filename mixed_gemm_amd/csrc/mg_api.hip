@@ -324,6 +324,24 @@ int mg_gelu_quantize_act(const mg_plan* p, const uint16_t* Y, int64_t M, const m
     return h == hipSuccess ? MG_OK : hip_fail(h, "mg_gelu_quantize_act");
 }
 
+int mg_dual_gemm_gelu_quant(const mg_plan* p0, const mg_act* a0, int64_t M, const mg_plan* p2, const mg_act* a2,
+                            hipStream_t stream) {
+    if (int e = check_plan(p0, true)) return e;
+    if (int e = check_plan(p2, false)) return e;
+    if (p2->d.K != p0->d.N)
+        return fail(MG_ERR_SHAPE, "the next layer's K=%d must equal this layer's N=%d", p2->d.K, p0->d.N);
+    if (M < 0) return fail(MG_ERR_SHAPE, "M=%lld must be >= 0", (long long)M);
+    if (M == 0) return MG_OK;
+    if (int e = check_act(p0, a0)) return e;
+    if (int e = check_act(p2, a2)) return e;
+    if (int e = check_gemm_size(p0, M)) return e;
+    if (int e = check_gemm_size(p2, M)) return e;
+    hipError_t h = mg::launch_dual_gemm_gelu_quant(a0->Aq, a0->As, a0->XO, p0->Wq, p0->Ws, p0->WO, M, p0->d.N,
+                                                   p0->d.K, p0->d.k, p2->s, p2->rcp, p2->pos, p2->d.k, a2->Aq,
+                                                   a2->As, a2->XO, stream);
+    return h == hipSuccess ? MG_OK : hip_fail(h, "mg_dual_gemm_gelu_quant");
+}
+
 int mg_dual_gemm(const mg_plan* p, const mg_act* a, int64_t M, void* Y, int32_t y_dtype, hipStream_t stream) {
     if (int e = check_plan(p, true)) return e;
     if (int e = check_dtype(y_dtype)) return e;

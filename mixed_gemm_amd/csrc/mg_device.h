@@ -32,19 +32,20 @@ __device__ __forceinline__ uint32_t e8m0_from_amax_bits(uint32_t amax_bits) {
 // correction (P. Markstein, IBM J. Res. Dev. 1990; Muller et al., Handbook of
 // Floating-Point Arithmetic, division with a fused multiply-add): q0 = x*rcp,
 // t = q0*s - x (exact), q = q0 - t*rcp.  The result is the correctly rounded
-// quotient when the remainder cannot underflow and the quotient is normal;
-// callers check the operand ranges (div_fast_ok_s, and x on its bits) and otherwise divide with
-// __fdiv_rn.  The remainder is formed as q0*s - x and subtracted, so a zero x
-// keeps its sign (-0 / s = -0) without a separate sign fix-up.
+// quotient when nothing overflows and the remainder cannot underflow; the
+// callers check their conditions (div_fast_ok_s, and bounds on the quotients)
+// and otherwise divide with __fdiv_rn.  The remainder is formed as q0*s - x
+// and subtracted, so a zero x keeps its sign (-0 / s = -0) without a separate
+// sign fix-up.
 __device__ __forceinline__ float div_fast(float x, float s, float rcp) {
     const float q0 = x * rcp;
     const float t = __builtin_fmaf(q0, s, -x);
     return __builtin_fmaf(-t, rcp, q0);
 }
 
-// Divisor range in which div_fast is exact for x == 0 or 2^-100 <= |x| <= 2^100
-// (the quotient stays far from underflow and overflow and the exact
-// remainder is representable); the callers check x on its raw bits.
+// Divisor range of the fast division: with 2^-20 <= s <= 2^20, div_fast is
+// the IEEE quotient for every bf16 x with |x| >= 2^-100 and |x * rcp| < 2^126
+// (the remainder is then representable and nothing overflows).
 __device__ __forceinline__ bool div_fast_ok_s(float s) { return s >= 0x1p-20f && s <= 0x1p20f; }
 
 // GELU (tanh form) in f32 of one value: 0.5 y (1 + tanh u) with
@@ -73,7 +74,27 @@ __device__ __forceinline__ uint32_t gelu_bf16x2(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, mg_bf16x2_t));
 }
 
-// E8M0 code c -> the f32 scale 2^(c - 127) (c = 0 gives the subnormal 2^-127).
+// f32 bit patterns of 2^126, 2^-74 and 2^-78: the bounds of the activation
+// quantizer's checks on its fast division (see the quantizer)
+constexpr uint32_t kF32Pow126 = 0x7E800000u, kF32PowM74 = 0x1A800000u, kF32PowM78 = 0x18800000u;
+// integer predicates of __builtin_amdgcn_uicmp (a wave mask of the lanes where
+// the unsigned comparison holds)
+constexpr int kCmpNE = 33, kCmpUGE = 35, kCmpULT = 36;
+
+// Max over the 4 lanes of a quad (one 32-block: quad_perm [1,0,3,2] then
+// [2,3,0,1]) of the bit patterns of non-negative f32 values, whose unsigned
+// integer order is their numeric order.
+__device__ __forceinline__ uint32_t quad_max_bits(uint32_t v) {
+    v = __builtin_elementwise_max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true));
+    v = __builtin_elementwise_max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true));
+    return v;
+}
+
+// E8M0 code c -> the scale operand of the hardware converter, which takes
+// the E8M0 code from the exponent field of its f32 scale: 2^(c - 127) for
+// c >= 1, and for c = 0 a value whose exponent field is 0 (the converter then
+// scales by 2^-127; checked bit for bit against the oracle on blocks with
+// that code).
 __device__ __forceinline__ float e8m0_to_f32(uint32_t c) {
     return __uint_as_float(c ? (c << 23) : 0x00200000u);
 }

@@ -73,6 +73,14 @@ hipError_t launch_dual_gemm(const uint8_t* Aq, const uint8_t* As, const uint16_t
                             const uint8_t* Wq, const uint8_t* Ws, const uint16_t* WO, int64_t M,
                             int32_t N, int32_t K, int32_t k, void* Y, int32_t y_dtype,
                             hipStream_t st);
+// launch_dual_gemm whose epilogue applies GELU to the bf16-rounded output and
+// quantizes it as the input of the next layer (plan s2, rcp2, pos2, k2; its
+// input width is N) into Aq2, As2, XO2, instead of writing Y.
+hipError_t launch_dual_gemm_gelu_quant(const uint8_t* Aq, const uint8_t* As, const uint16_t* XO,
+                                       const uint8_t* Wq, const uint8_t* Ws, const uint16_t* WO, int64_t M,
+                                       int32_t N, int32_t K, int32_t k, const float* s2, const float* rcp2,
+                                       const int32_t* pos2, int32_t k2, uint8_t* Aq2, uint8_t* As2,
+                                       uint16_t* XO2, hipStream_t st);
 hipError_t launch_gelu(const uint16_t* in, uint16_t* out, int64_t n, hipStream_t st);
 hipError_t launch_pct_reset(uint32_t* hist, int32_t K, hipStream_t st);
 hipError_t launch_pct_count(const uint16_t* X, int64_t M, int32_t K, int pass, const int32_t* sel, uint32_t* hist,

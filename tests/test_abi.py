@@ -314,3 +314,28 @@ def test_forward_validates_both_steps_before_launching():
     assert L.mg_forward_noalloc(ctypes.byref(p), FAKE, 1, 24000, FAKE, 1, None) == -5
     assert b"limit" in L.mg_last_error()
     assert L.mg_forward_noalloc(ctypes.byref(p), FAKE, 1, big, FAKE, 1, None) == -5
+
+
+def test_gemm_gelu_quant_validates_before_launching():
+    """mg_dual_gemm_gelu_quant checks both plans, both workspaces, the chained
+    widths (the next layer's K = this layer's N) and both layers' operand
+    limits before any launch (an accepted call would fail with a HIP error on
+    this GPU-less host)."""
+    L = mg.lib()
+    p0 = _plan(K=5120, N=256, k=64)
+    p2 = _plan(K=256, N=128, k=8)
+    bad = _plan(K=512, N=128, k=8)
+    a = mg.mg_act(FAKE, FAKE, FAKE)
+    call = lambda q0, a0, M, q2, a2: L.mg_dual_gemm_gelu_quant(q0, a0, M, q2, a2, None)
+    r = ctypes.byref
+    assert call(None, r(a), 8, r(p2), r(a), ) == -1
+    assert call(r(p0), r(a), 8, None, r(a)) == -1
+    assert call(r(p0), r(a), 8, r(bad), r(a)) == -2
+    assert b"equal" in L.mg_last_error()
+    assert call(r(p0), r(a), -1, r(p2), r(a)) == -2
+    assert call(r(p0), r(a), 0, r(p2), r(a)) == 0                    # M == 0: no-op
+    assert call(r(p0), None, 8, r(p2), r(a)) == -1
+    assert call(r(p0), r(a), 8, r(p2), None) == -1
+    assert call(r(p0), r(a), 8, r(p2), r(mg.mg_act(FAKE, None, FAKE))) == -1
+    big = (3 << 30) // 2560 + 1
+    assert call(r(p0), r(a), big, r(p2), r(a)) == -5

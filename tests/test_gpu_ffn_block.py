@@ -14,8 +14,9 @@ Stage-wise parity:
   bit and its output within 2e-3 (fp32) / one RNE (bf16); the GELU within one
   bf16 rounding of the float64 GELU of the GPU's ffn.0 output; ffn.2's codes
   (from the GPU's h) bit for bit and its output within 2e-3 / one RNE;
-- the fused GELU + quantize pass from ffn.0's output gives ffn.2's codes bit
-  for bit, on every row.
+- the fused GELU + quantize pass from ffn.0's output, and the same work in
+  ffn.0's GEMM epilogue (mg_dual_gemm_gelu_quant), give ffn.2's codes bit for
+  bit, on every row.
 The block's fidelity against the unquantized float64 block is printed, not
 asserted.
 """
@@ -114,7 +115,7 @@ def test_block_stagewise(block, layout):
     g0 = dict(Aq=aq_rows(a0.Aq, M, w0.K)[rows], As=scale_rows(a0.As, M, w0.K)[rows],
               XO=outlier_cols(a0.XO, M, w0.k)[rows], Y=host(Y0[ridx]),
               Y32=host(Y0_32[ridx]))
-    del a0, Y0_32
+    del Y0_32
     h = torch.empty_like(Y0)
     mg.mg_gelu_tanh_bf16(Y0, h)
     a2 = mg.Act.empty(blk.plan2.desc, M)
@@ -123,7 +124,13 @@ def test_block_stagewise(block, layout):
     mg.mg_gelu_quantize_act(blk.plan2, Y0, af)
     for n in ("Aq", "As", "XO"):
         assert torch.equal(getattr(af, n).view(torch.uint8), getattr(a2, n).view(torch.uint8)), f"fused {n}"
-    del af, Y0
+    # GELU + quantize in ffn.0's GEMM epilogue (ffn.0's output never written)
+    for t in (af.Aq, af.As, af.XO):
+        t.view(torch.uint8).fill_(0x5A)
+    mg.mg_dual_gemm_gelu_quant(blk.plan0, a0, blk.plan2, af)
+    for n in ("Aq", "As", "XO"):
+        assert torch.equal(getattr(af, n).view(torch.uint8), getattr(a2, n).view(torch.uint8)), f"epilogue {n}"
+    del af, Y0, a0
     Y2 = torch.empty((M, w2.N), dtype=torch.bfloat16, device="cuda")
     mg.mg_dual_gemm(blk.plan2, a2, Y2)
     Y2_32 = torch.empty((M, w2.N), dtype=torch.float32, device="cuda")
