@@ -35,10 +35,10 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 namespace {
 
 // ---------------------------------------------------------------------------
-// Persistent tiled kernel.  One workgroup per CU (4 waves); each walks a list
-// of 256x256 output tiles.  Each wave owns a 128x128 quarter = 4x4 MFMA tiles
-// of 32x32 (256 fp32 accumulators per lane, held in the accumulation
-// registers).
+// Persistent tiled kernel.  One workgroup per CU (NW waves); each walks a
+// list of 256x256 output tiles.  Each wave owns 128 rows x 512/NW columns =
+// 4 x JB MFMA tiles of 32x32 (16 JB fp32 accumulators per lane, held in the
+// accumulation registers).
 //
 // K is walked in half-stages of two 32-byte K-slices per tile row: a bulk
 // half-stage carries 128 FP4 values of Aq / Wq, an outlier half-stage 32 bf16
@@ -51,14 +51,14 @@ namespace {
 // over a ring of four 32 KB LDS slots.  While half-stage g is multiplied out
 // of slot g % 4, the copies of half-stage g + 2 (which may belong to the next
 // tile) run straight from global memory into slot (g + 2) % 4; at the end of
-// g each wave waits for the copies of g + 1 only (the 8 younger ones stay in
-// flight) and the workgroup meets at one barrier.  Two half-stages of lead
+// g each wave waits for the copies of g + 1 only (its NCOPY younger ones
+// stay in flight) and the workgroup meets at one barrier.  Two half-stages of lead
 // keep the copy path streaming (with one 64 KB stage in flight and waited at
 // every stage end it was latency-bound).  Inside a half-stage the issue order
 // is fixed slot by slot, one MFMA per slot: the previous half-stage's second
-// sub-step (its fragments read before the barrier) fills the first 16 slots,
+// sub-step (its fragments read before the barrier) fills the first MPS slots,
 // so the matrix cores stay busy while this half-stage's first fragments are
-// read; the 8 copies go one per two slots.
+// read; the wave's NCOPY copies go one per two slots.
 //
 // E8M0 scales.  A bulk half-stage needs 4 scale bytes per tile row.  The 16
 // bytes of four consecutive bulk half-stages ("a window") of all 512 tile
@@ -96,7 +96,18 @@ constexpr int OP_BYTES = NRG * HS_SL * kFragBlock;    // one operand of a half-s
 constexpr int HS_BYTES = 2 * OP_BYTES;                // A + B (32 KB)
 constexpr int RING = 4;                               // LDS slots
 constexpr int LEAD = 2;                               // half-stages copied ahead
-constexpr int NCOPY = 2 * NRG * HS_SL / 4;            // copies per wave and half-stage (8)
+// Waves per workgroup, 2 along M x NW/2 along N.  With 8 (two per SIMD, 128
+// accumulators each) the matrix cores are busier than with 4 (one per SIMD,
+// 256 accumulators) but every fragment is read by more waves; the kernel is
+// written for both and runs 8, which measured 0.4-0.7 % faster.
+#ifndef MG_GEMM_WAVES
+#define MG_GEMM_WAVES 8
+#endif
+constexpr int NW = MG_GEMM_WAVES;
+constexpr int JB = 16 / NW;                           // 32-column B blocks per wave (4 or 2)
+constexpr int RPW = 8 / NW;                           // row groups per operand a wave copies
+constexpr int NCOPY = 2 * NRG * HS_SL / NW;           // copies per wave and half-stage (8 or 4)
+constexpr int MPS = 4 * JB;                           // MFMAs per wave and K-slice
 constexpr int SCW_ROWB = 16;                          // scale bytes per row per window (4 half-stages)
 constexpr int SCW_BYTES = (TBM + TBN) * SCW_ROWB;     // one window slot: A rows then B rows (8 KB)
 constexpr int SCW_SLOTS = 3;
@@ -107,7 +118,7 @@ constexpr int NXCD = 8;
 constexpr int GROUP_M = 8;
 static_assert(TBM == kScRows && TBN == kScRows && SCW_ROWB == kScBlocks, "a tile's scale window is one stored window");
 static_assert(kScBlocks == 4 * HS_SL * 2, "a window holds the scale bytes of four half-stages");
-static_assert(LEAD == 2 && NCOPY == 8, "the end-of-half-stage wait keeps exactly one half-stage of copies in flight");
+static_assert(LEAD == 2 && NCOPY * NW == 32, "the end-of-half-stage wait keeps exactly one half-stage of copies in flight");
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -189,13 +200,13 @@ struct TileOrg {
 };
 
 template <typename OutT>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 dual_gemm_tiled(GemmArgs g) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / (NW / 2), wn = wave % (NW / 2);
     const int h = lane >> 5;
     const int l32 = lane & 31;
 
@@ -230,23 +241,23 @@ dual_gemm_tiled(GemmArgs g) {
 
     // ---- tile-independent lane constants.  A copy moves one 1 KB fragment
     // block (lane L: bytes 16 L .. 16 L + 15, landing at byte 16 L of the
-    // block's LDS place).  Wave w copies row groups 2 w and 2 w + 1 of the A
-    // and of the B tile, slices 0 and 1 of the half-stage: block (operand,
-    // row group rg, slice sl) of a slot sits at operand * 16 KB + (2 rg + sl)
-    // * 1 KB.  The block's global offset goes into the scalar offset, slice 1
+    // block's LDS place).  Wave w copies row groups RPW w .. RPW w + RPW - 1
+    // of the A and of the B tile, slices 0 and 1 of the half-stage: block
+    // (operand, row group rg, slice sl) of a slot sits at operand * 16 KB +
+    // (2 rg + sl) * 1 KB.  The block's global offset goes into the scalar offset, slice 1
     // into the instruction offset (which moves the global and the LDS
     // address alike), the lane's 16 L into the vector offset.
     const uint32_t l16 = (uint32_t)lane * 16u;
     // scale windows: lane L of wave w copies window row 64 w + L of A and of
-    // B; a lane reads the 2 codes of a half-stage (slices 0, 1 of its half of
+    // B (NW = 4), or of A (w < 4) or B (NW = 8); a lane reads the 2 codes of a half-stage (slices 0, 1 of its half of
     // the K steps) of each of its fragment rows at these offsets (+ 512 i,
     // + 2 (half-stage % 4)): row * 16 + 8 h
-    const uint32_t lwr = (uint32_t)(wave * 64 + lane) * SCW_ROWB;
+    const uint32_t lwr = (uint32_t)((NW == 4 ? wave : wave & 3) * 64 + lane) * SCW_ROWB;
     const uint32_t scw_a = (uint32_t)((wm * 128 + l32) * SCW_ROWB + 8 * h);
-    const uint32_t scw_b = (uint32_t)(TBM * SCW_ROWB + (wn * 128 + l32) * SCW_ROWB + 8 * h);
+    const uint32_t scw_b = (uint32_t)(TBM * SCW_ROWB + (wn * 32 * JB + l32) * SCW_ROWB + 8 * h);
     // fragment reads: A row group 4 wm + i, B row group 4 wn + j
     const uint32_t fa0 = (uint32_t)(wm * 4 * HS_SL * kFragBlock) + l16;
-    const uint32_t fb0 = (uint32_t)(OP_BYTES + wn * 4 * HS_SL * kFragBlock) + l16;
+    const uint32_t fb0 = (uint32_t)(OP_BYTES + wn * JB * HS_SL * kFragBlock) + l16;
 
     auto tile_org = [&](int tt) {
         TileOrg o;
@@ -258,8 +269,8 @@ dual_gemm_tiled(GemmArgs g) {
         return o;
     };
 
-    v16f acc[4][4];
-    uint32_t scA[4], scB[4], pA[4], pB[4];
+    v16f acc[4][JB];
+    uint32_t scA[4], scB[JB], pA[4], pB[JB];
     int wiss = 0;      // slot of the next scale window to issue (0, 1, 2, 0, ...)
     int wnext = 0;     // slot of the next scale window to take into use
     int wcur = 0;      // slot of the window of the current bulk half-stage
@@ -267,7 +278,7 @@ dual_gemm_tiled(GemmArgs g) {
     // ---- copy cursor: the next half-stage to copy -- tile ct, half-stage
     // cst, origin corg -- and its source: the resources of the A and B
     // operands (bulk or outlier) and the global offsets of its slice-0
-    // blocks in this wave's two A and two B row groups.  `issued`
+    // blocks in this wave's RPW A and RPW B row groups.  `issued`
     // half-stages have been copied, into ring slots issued % 4.  Wave-uniform
     // (scalar registers); inside a tile's bulk or outlier run an advance is
     // four scalar adds.
@@ -279,7 +290,7 @@ dual_gemm_tiled(GemmArgs g) {
         const bool bulk = cst < H4;
         const uint32_t ns = bulk ? ns4 : nso;
         const uint32_t s0 = (uint32_t)(2 * (bulk ? cst : cst - H4)) * (uint32_t)kFragBlock;
-        const int ga = (int)(corg.m0 / kFragRows) + 2 * wave, gb = corg.n0 / kFragRows + 2 * wave;
+        const int ga = (int)(corg.m0 / kFragRows) + RPW * wave, gb = corg.n0 / kFragRows + RPW * wave;
         csA = bulk ? rA : rXO;
         csB = bulk ? rB : rWO;
         cA0 = (uint32_t)min(ga, GA - 1) * ns * (uint32_t)kFragBlock + s0;
@@ -297,8 +308,14 @@ dual_gemm_tiled(GemmArgs g) {
         uint8_t* dst = lds + SCW_OFF + slot * SCW_BYTES + wave * 64 * SCW_ROWB;
         const uint32_t wa = __builtin_amdgcn_readfirstlane(((uint32_t)(o.m0 / TBM) * nwin + (uint32_t)w) * kScWinBytes);
         const uint32_t wb = __builtin_amdgcn_readfirstlane(((uint32_t)(o.n0 / TBN) * nwin + (uint32_t)w) * kScWinBytes);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rAs, (lds_ptr_t)dst, 16, lwr, wa, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rBs, (lds_ptr_t)(dst + TBM * SCW_ROWB), 16, lwr, wb, 0, 0);
+        if constexpr (NW == 4) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rAs, (lds_ptr_t)dst, 16, lwr, wa, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rBs, (lds_ptr_t)(dst + TBM * SCW_ROWB), 16, lwr, wb, 0, 0);
+        } else {
+            // waves 0-3: A rows 64 w .., waves 4-7: B rows 64 (w - 4) .. (dst already at the B half)
+            if (wave < 4) __builtin_amdgcn_raw_ptr_buffer_load_lds(rAs, (lds_ptr_t)dst, 16, lwr, wa, 0, 0);
+            else          __builtin_amdgcn_raw_ptr_buffer_load_lds(rBs, (lds_ptr_t)dst, 16, lwr, wb, 0, 0);
+        }
     };
     // does the cursor's half-stage open a scale window?
     auto cursor_opens_window = [&]() { return ct < t_end && cst < H4 && (cst & 3) == 0; };
@@ -307,8 +324,8 @@ dual_gemm_tiled(GemmArgs g) {
     // (fast: the cursor is known to be in the bulk part, whose resources are
     // rA and rB)
     auto copy_part = [&](int c, bool fast) {
-        const int op = c >> 2, r = (c >> 1) & 1, sl = c & 1;
-        uint8_t* dst = lds + (issued & (RING - 1)) * HS_BYTES + op * OP_BYTES + (2 * (2 * wave + r)) * kFragBlock;
+        const int op = c / (2 * RPW), r = (c >> 1) % RPW, sl = c & 1;
+        uint8_t* dst = lds + (issued & (RING - 1)) * HS_BYTES + op * OP_BYTES + (2 * (RPW * wave + r)) * kFragBlock;
         const uint32_t so = op ? (r ? cB1 : cB0) : (r ? cA1 : cA0);
         const __amdgpu_buffer_rsrc_t rs = fast ? (op ? rB : rA) : (op ? csB : csA);
         if (sl)
@@ -316,7 +333,7 @@ dual_gemm_tiled(GemmArgs g) {
         else
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst, 16, l16, so, 0, 0);
     };
-    // after the 8 copies: the cursor moves to the next half-stage (past the
+    // after the wave's copies: the cursor moves to the next half-stage (past the
     // last tile it stays put: its copies then re-read valid memory into a
     // free slot)
     auto advance_fast = [&]() {      // the cursor stays in the same tile's bulk part
@@ -348,7 +365,10 @@ dual_gemm_tiled(GemmArgs g) {
     // above the wait, so they run while copies fly.
     auto stage_sync = [&]() {
         __builtin_amdgcn_sched_barrier(0);
-        asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+        if constexpr (NCOPY == 8)
+            asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -360,21 +380,24 @@ dual_gemm_tiled(GemmArgs g) {
         else       scB[q - 4] = *reinterpret_cast<const uint16_t*>(wsc + scw_b + (q - 4) * 32 * SCW_ROWB);
     };
 
-    // ---- one half-stage in a fixed issue order of one slot per MFMA:
-    //   0-15   the previous half-stage's slice 1 (kind DK: 0 none, 1 FP4, 2
-    //          BF16); slots 0-7 also read slice 0's fragments (A0 B0 B1 B2 B3
-    //          A1 A2 A3, the order its MFMAs need them) and the half-stage's
-    //          scale codes;
-    //   16-31  slice 0; slots 16-23 read slice 1's fragments;
-    //   32-47  slice 1 when it is not deferred (the last bulk half-stage of a
-    //          tile, and every outlier half-stage).
+    // ---- one half-stage in a fixed issue order of one slot per MFMA (MPS =
+    // 4 JB MFMAs per slice):
+    //   0 .. MPS-1        the previous half-stage's slice 1 (kind DK: 0 none,
+    //                     1 FP4, 2 BF16); its first 4 + JB slots also read
+    //                     slice 0's fragments (A0, B0 .. B(JB-1), A1 A2 A3,
+    //                     the order its MFMAs need them) and the half-stage's
+    //                     scale codes;
+    //   MPS .. 2 MPS-1    slice 0; its first 4 + JB slots read slice 1's
+    //                     fragments;
+    //   2 MPS .. 3 MPS-1  slice 1 when it is not deferred (the last bulk
+    //                     half-stage of a tile, and every outlier half-stage).
     // Slot 1 opens the cursor's scale window (if it starts one), slots 2,
-    // 4, .., 16 issue its 8 copies: never two memory instructions back to
-    // back, so the address unit is shared evenly between the four waves.
+    // 4, .., 2 NCOPY issue its copies: never two memory instructions back to
+    // back, so the address unit is shared evenly between the waves.
     u32x4 pf[2][2][4];                 // fragment sets [set = slice][A/B][i]
     auto frag_read = [&](const uint8_t* base, int sl, int q) {
-        const bool isA = q == 0 || q >= 5;
-        const int r = q == 0 ? 0 : (q < 5 ? q - 1 : q - 4);
+        const bool isA = q == 0 || q > JB;
+        const int r = q == 0 ? 0 : (q <= JB ? q - 1 : q - JB);
         const uint32_t off = (uint32_t)(r * HS_SL * kFragBlock + sl * kFragBlock);
         if (isA) pf[sl][0][r] = *reinterpret_cast<const u32x4*>(base + fa0 + off);
         else     pf[sl][1][r] = *reinterpret_cast<const u32x4*>(base + fb0 + off);
@@ -396,31 +419,31 @@ dual_gemm_tiled(GemmArgs g) {
             wsc = lds + SCW_OFF + wcur * SCW_BYTES + 2 * (hs & 3);
         }
         const bool opens_window = fast ? (cst & 3) == 0 : cursor_opens_window();
-        static_for<48>([&](auto QC) {
+        static_for<3 * MPS>([&](auto QC) {
             constexpr int q = decltype(QC)::value;
-            if constexpr (q < 32 || !dout) {
-                if constexpr (q < 16) {
-                    constexpr int i = q >> 2, j = q & 3;
+            if constexpr (q < 2 * MPS || !dout) {
+                if constexpr (q < MPS) {
+                    constexpr int i = q / JB, j = q % JB;
                     if constexpr (dk == 1)
                         acc[i][j] = mfma_fp4_op<1>(pf[1][1][j], pf[1][0][i], pB[j], pA[i], acc[i][j]);
                     else if constexpr (dk == 2)
                         acc[i][j] = mfma_bf16_v(pf[1][1][j], pf[1][0][i], acc[i][j]);
                 } else {
-                    constexpr int sl = (q - 16) >> 4, r = (q - 16) & 15, i = r >> 2, j = r & 3;
+                    constexpr int sl = (q - MPS) / MPS, r = (q - MPS) % MPS, i = r / JB, j = r % JB;
                     if constexpr (cb)
                         acc[i][j] = mfma_fp4_op<sl>(pf[sl][1][j], pf[sl][0][i], scB[j], scA[i], acc[i][j]);
                     else
                         acc[i][j] = mfma_bf16_v(pf[sl][1][j], pf[sl][0][i], acc[i][j]);
                 }
-                if constexpr (q < 8) {
+                if constexpr (q < 4 + JB) {
                     if constexpr (cb) read_scale(wsc, q);
                     frag_read(base, 0, q);
                 }
-                if constexpr (q >= 16 && q < 24) frag_read(base, 1, q - 16);
+                if constexpr (q >= MPS && q < MPS + 4 + JB) frag_read(base, 1, q - MPS);
                 if constexpr (q == 1) {
                     if (opens_window) load_window(corg, cst >> 2);
                 }
-                if constexpr (q >= 2 && q <= 16 && q % 2 == 0) copy_part((q - 2) >> 1, fast);
+                if constexpr (q >= 2 && q <= 2 * NCOPY && q % 2 == 0) copy_part((q - 2) >> 1, fast);
                 __builtin_amdgcn_sched_barrier(0);
             }
         });
@@ -430,7 +453,9 @@ dual_gemm_tiled(GemmArgs g) {
             advance();
         if constexpr (cb && dout) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) { pA[i] = scA[i]; pB[i] = scB[i]; }
+            for (int i = 0; i < 4; ++i) pA[i] = scA[i];
+#pragma unroll
+            for (int j = 0; j < JB; ++j) pB[j] = scB[j];
         }
         stage_sync();
     };
@@ -593,18 +618,19 @@ dual_gemm_tiled(GemmArgs g) {
     // ---- epilogue of one tile.  The MFMAs take the weight fragment as their
     // first operand, so acc[i][j] holds Y^T for A row-tile i and W row-tile j:
     // lane (l32, h), register 4 q + e holds output row 32 i + l32 and output
-    // column 32 j + 8 q + 4 h + e of this wave's quarter -- four consecutive
+    // column 32 j + 8 q + 4 h + e of this wave's part -- four consecutive
     // columns per register group.
     auto epilogue = [&](const TileOrg& o, uint8_t* wbuf) {
         if constexpr (std::is_same_v<OutT, uint16_t> || std::is_same_v<OutT, QuantOut>) {
             // bf16: round pairs with the hardware converter (nearest even).
-            // Each wave stages its own 128x128 quarter through its own 16 KB
-            // of a free ring slot (wbuf), 64 rows x 256 B per pass, and writes the
-            // rows back out with 16-byte streaming stores (four 256-byte row
-            // pieces per instruction).  No wave reads another wave's staging,
-            // so a pass needs no barrier: one wave's LDS accesses are
-            // processed in order.  In a staged row r the 16-byte chunk c
-            // (columns 8c .. 8c+7 of the quarter) sits at chunk c ^ (r & 15).
+            // Each wave stages its own 128 x 32 JB part through its own
+            // 64 KB / NW of a free ring slot pair (wbuf), 64 rows x 64 JB
+            // bytes per pass, and writes the rows back out with 16-byte
+            // streaming stores (whole 64 JB-byte row pieces).  No wave reads
+            // another wave's staging, so a pass needs no barrier: one wave's
+            // LDS accesses are processed in order.  In a staged row r the
+            // 16-byte chunk c (columns 8c .. 8c+7 of the part) sits at chunk
+            // c ^ (r % (4 JB)).
             // the tile's rows of Y: rows past M are out of the descriptor's
             // range and columns past N get an out-of-range offset, so the
             // stores need no branches
@@ -619,8 +645,9 @@ dual_gemm_tiled(GemmArgs g) {
             uint32_t et = (uint32_t)tid;
             asm volatile("" : "+v"(et));
             const uint32_t el32 = et & 31u, eh = (et >> 5) & 1u;
-            const uint32_t rl = (et & 63u) >> 4, cl = et & 15u;       // read side: row (of 4), chunk
-            const int gcol = o.n0 + wn * 128 + (int)cl * 8;
+            constexpr uint32_t CH = 4 * JB, RBY = 64 * JB;      // chunks and bytes per staged row
+            const uint32_t rl = (et & 63u) / CH, cl = et & (CH - 1);  // read side: row (of 64 / CH), chunk
+            const int gcol = o.n0 + wn * 32 * JB + (int)cl * 8;
             const bool col_ok = gcol < N;
             const uint32_t cofs = (uint32_t)gcol * 2u;
             [[maybe_unused]] QuantLane ql;
@@ -632,11 +659,11 @@ dual_gemm_tiled(GemmArgs g) {
                     const int i = 2 * p + ii;
                     // read row-block i's accumulators here, not earlier
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
+                    for (int j = 0; j < JB; ++j) asm volatile("" : "+a"(acc[i][j]));
                     const uint32_t r = (uint32_t)(32 * ii) + el32;
-                    const uint32_t rb = r * 256 + eh * 8, rs = r & 15u;
+                    const uint32_t rb = r * RBY + eh * 8, rs = r & (CH - 1);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
+                    for (int j = 0; j < JB; ++j)
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
                             const f32x2 lo = {acc[i][j][4 * q], acc[i][j][4 * q + 1]};
@@ -649,21 +676,21 @@ dual_gemm_tiled(GemmArgs g) {
                 if constexpr (std::is_same_v<OutT, QuantOut>) {
                     // row pieces of the staged bf16 rows (lane: 8 columns of a row), each
                     // through GELU and the next layer's quantizer
-                    for (int sI = 0; sI < 16; ++sI) {
-                        const uint32_t rr = (uint32_t)(4 * sI) + rl;
-                        const u32x4 w = *reinterpret_cast<const u32x4*>(wbuf + rr * 256 + ((cl ^ (rr & 15u)) << 4));
+                    for (int sI = 0; sI < (int)CH; ++sI) {
+                        const uint32_t rr = (uint32_t)(64 / CH * sI) + rl;
+                        const u32x4 w = *reinterpret_cast<const u32x4*>(wbuf + rr * RBY + ((cl ^ (rr & (CH - 1))) << 4));
                         quant_octet(ql, o, w, (uint32_t)(wm * 128 + 64 * p) + rr);
                     }
                 } else {
-                    u32x4 v[16];
+                    u32x4 v[CH];
 #pragma unroll
-                    for (int sI = 0; sI < 16; ++sI) {
-                        const uint32_t rr = (uint32_t)(4 * sI) + rl;
-                        v[sI] = *reinterpret_cast<const u32x4*>(wbuf + rr * 256 + ((cl ^ (rr & 15u)) << 4));
+                    for (int sI = 0; sI < (int)CH; ++sI) {
+                        const uint32_t rr = (uint32_t)(64 / CH * sI) + rl;
+                        v[sI] = *reinterpret_cast<const u32x4*>(wbuf + rr * RBY + ((cl ^ (rr & (CH - 1))) << 4));
                     }
 #pragma unroll
-                    for (int sI = 0; sI < 16; ++sI) {
-                        const uint32_t rr = (uint32_t)(4 * sI) + rl;
+                    for (int sI = 0; sI < (int)CH; ++sI) {
+                        const uint32_t rr = (uint32_t)(64 / CH * sI) + rl;
                         const uint32_t off = col_ok ? ((uint32_t)(wm * 128 + 64 * p) + rr) * rowY + cofs : OOB;
                         // streaming store (nt): Y is written once and must not
                         // push the operand panels out of L2
@@ -682,10 +709,10 @@ dual_gemm_tiled(GemmArgs g) {
             for (int i = 0; i < 4; ++i) {
                 const int64_t row = o.m0 + wm * 128 + 32 * i + l32;
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < JB; ++j)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const int col = o.n0 + wn * 128 + 32 * j + 8 * q + 4 * h;
+                        const int col = o.n0 + wn * 32 * JB + 32 * j + 8 * q + 4 * h;
                         if (row < M && col < N) {
                             const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                                              acc[i][j][4 * q + 3]};
@@ -705,7 +732,10 @@ dual_gemm_tiled(GemmArgs g) {
         advance();
     }
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+    if constexpr (NCOPY == 8)
+        asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
     __syncthreads();
     TileOrg cur = tile_org(t);
     int gs = 0;        // half-stages computed so far (the current one's slot: gs % 4)
@@ -718,7 +748,7 @@ dual_gemm_tiled(GemmArgs g) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+            for (int j = 0; j < JB; ++j) acc[i][j] = v16f{};
         // bulk half-stages, each leaving its slice 1 to the next.  While hs
         // + 3 < H4 the copies (two half-stages ahead) stay in this tile's
         // bulk part: the fast cursor step.
@@ -737,7 +767,7 @@ dual_gemm_tiled(GemmArgs g) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < JB; ++j)
                 acc[i][j] = mfma_fp4_op<1>(pf[1][1][j], pf[1][0][i], pB[j], pA[i], acc[i][j]);
         // outlier half-stages, each complete in itself
         for (; hs < H; ++hs) {
@@ -745,11 +775,11 @@ dual_gemm_tiled(GemmArgs g) {
             ++gs;
         }
         // the slots of the last two half-stages, (gs - 1) % 4 and (gs - 2) % 4,
-        // hold no pending copy: waves 0, 1 stage their output through the
-        // first, waves 2, 3 through the second
+        // hold no pending copy: the first half of the waves stage their
+        // output through the first, the second half through the second
         {
-            const int fs = (wave < 2 ? gs - 1 : gs - 2) & (RING - 1);
-            epilogue(cur, lds + fs * HS_BYTES + (wave & 1) * (HS_BYTES / 2));
+            const int fs = (wave < NW / 2 ? gs - 1 : gs - 2) & (RING - 1);
+            epilogue(cur, lds + fs * HS_BYTES + (wave % (NW / 2)) * (HS_BYTES / (NW / 2)));
         }
         t += nl;
         if (t >= t_end) break;
@@ -772,7 +802,7 @@ static hipError_t launch_tiled(const GemmArgs& a, hipStream_t st) {
     const int per = (T + NXCD - 1) / NXCD;
     const int cus_per_xcd = device_cu_count() / NXCD;
     const int wg_per_xcd = per < cus_per_xcd ? per : (cus_per_xcd > 0 ? cus_per_xcd : 1);
-    hipLaunchKernelGGL((dual_gemm_tiled<OutT>), dim3((unsigned)(wg_per_xcd * NXCD)), dim3(256),
+    hipLaunchKernelGGL((dual_gemm_tiled<OutT>), dim3((unsigned)(wg_per_xcd * NXCD)), dim3(64 * NW),
                        GEMM_LDS_BYTES, st, a);
     return hipGetLastError();
 }
