@@ -187,6 +187,28 @@ struct QuantLane {
     bool valid;
 };
 
+// The GELU + quantize epilogue's arguments, read from the kernel-argument
+// segment once per tile through a pointer the compiler cannot see through
+// (kernargs_per_tile), so that neither they nor the sizes derived from them
+// are held in scalar registers across the tile loop's K steps (which would
+// spill them there).
+struct QuantArgs {
+    const float* s2;
+    const float* rcp2;
+    const int32_t* pos2;
+    uint8_t* Aq2;
+    uint8_t* As2;
+    uint8_t* XO2;
+    int64_t M;
+    int32_t N, k2;
+};
+typedef const __attribute__((address_space(4))) GemmArgs* KernargPtr;
+__device__ __forceinline__ QuantArgs kernargs_per_tile() {
+    KernargPtr p = (KernargPtr)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(p));
+    return QuantArgs{p->s2, p->rcp2, p->pos2, p->Aq2, p->As2, p->XO2, p->M, p->N, p->k2};
+}
+
 // bytes of a buffer of `total` bytes from offset `from` on (0 past its end)
 __device__ __forceinline__ uint64_t rest_bytes(int64_t total, int64_t from) {
     return total > from ? (uint64_t)(total - from) : 0u;
@@ -472,7 +494,7 @@ dual_gemm_tiled(GemmArgs g) {
     // Rows past M and channels past N are zeros (their accumulators are not
     // the layer's); the codes of pad rows and pad slices land inside the
     // buffers' pads, the rest outside the resources' ranges.
-    auto quant_lane = [&](const TileOrg& o, int cj0, bool cvalid, uint32_t ln) {
+    auto quant_lane = [&](const QuantArgs& qa, int cj0, bool cvalid, uint32_t ln) {
         QuantLane L;
         float rv[8];
         int pv[8];
@@ -481,9 +503,9 @@ dual_gemm_tiled(GemmArgs g) {
         if (cvalid) {
 #pragma unroll
             for (int h4 = 0; h4 < 2; ++h4) {
-                const float4 a = *reinterpret_cast<const float4*>(g.s2 + cj0 + 4 * h4);
-                const float4 b = *reinterpret_cast<const float4*>(g.rcp2 + cj0 + 4 * h4);
-                const int4 c = *reinterpret_cast<const int4*>(g.pos2 + cj0 + 4 * h4);
+                const float4 a = *reinterpret_cast<const float4*>(qa.s2 + cj0 + 4 * h4);
+                const float4 b = *reinterpret_cast<const float4*>(qa.rcp2 + cj0 + 4 * h4);
+                const int4 c = *reinterpret_cast<const int4*>(qa.pos2 + cj0 + 4 * h4);
                 L.sv[4 * h4] = a.x; L.sv[4 * h4 + 1] = a.y; L.sv[4 * h4 + 2] = a.z; L.sv[4 * h4 + 3] = a.w;
                 rv[4 * h4] = b.x; rv[4 * h4 + 1] = b.y; rv[4 * h4 + 2] = b.z; rv[4 * h4 + 3] = b.w;
                 pv[4 * h4] = c.x; pv[4 * h4 + 1] = c.y; pv[4 * h4 + 2] = c.z; pv[4 * h4 + 3] = c.w;
@@ -520,7 +542,7 @@ dual_gemm_tiled(GemmArgs g) {
         L.wave_rest = __builtin_amdgcn_readfirstlane((int)(__builtin_amdgcn_ballot_w64((om & (om - 1)) != 0) != 0));
         // byte offsets inside the tile's part of each buffer, the row's part
         // (16 per row of the 32-row group, 1 KB blocks per group) added per row
-        const uint32_t ns4b = (uint32_t)frag_slices(N / 2), nsob = (uint32_t)frag_slices(2 * (int64_t)g.k2);
+        const uint32_t ns4b = (uint32_t)frag_slices(qa.N / 2), nsob = (uint32_t)frag_slices(2 * (int64_t)qa.k2);
         const uint32_t b = (uint32_t)cj0 / 2u;
         L.offAq = (b >> 5) * 1024u + ((b >> 4) & 1u) * 512u + (b & 15u);
         const uint32_t bo = 2u * (uint32_t)op0;
@@ -530,12 +552,18 @@ dual_gemm_tiled(GemmArgs g) {
         L.ns4 = ns4b; L.nso = nsob;
         return L;
     };
-    // row piece of tile row mt (0..255): w the staged bf16 words (before GELU)
-    auto quant_octet = [&](const QuantLane& L, const TileOrg& o, u32x4 w, uint32_t mt) {
+    // row piece of tile row mt = mu + rl (0..255): w the staged bf16 words
+    // (before GELU).  mu is wave-uniform and a multiple of 64 / CH, and
+    // rl < 64 / CH, so the row's 32-row group (mu / 32) is wave-uniform and
+    // the buffer resources below are formed in scalar registers.
+    auto quant_octet = [&](const QuantArgs& qa, const QuantLane& L, const TileOrg& o, u32x4 w, uint32_t mu,
+                           uint32_t rl) {
+        const uint32_t mt = mu + rl;
         const int64_t m = o.m0 + mt;
-        const bool live = m < M && L.valid;
+        const bool live = m < qa.M && L.valid;
+        // zeros for rows past M and channels past N (GELU(0) = 0), with no branch
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = live ? gelu_bf16x2(w[i]) : 0u;
+        for (int i = 0; i < 4; ++i) w[i] = gelu_bf16x2(live ? w[i] : 0u);
         const int wave_o = L.wave_o;
         float q[8];
         float a0 = 0.0f, aq = 0.0f;
@@ -576,12 +604,12 @@ dual_gemm_tiled(GemmArgs g) {
             if (wave_o) qo = __fdiv_rn(xo, L.so);
         }
         // the tile's row group and the row inside it
-        const uint32_t rg = mt >> 5, rin = (mt & 31u) << 4;
+        const uint32_t rg = mu >> 5, rin = (mt & 31u) << 4;
         if (wave_o) {
             // the row's 32-row group of XO (its nso blocks; none past the last group)
             const int64_t xo0 = (o.m0 / 32 + rg) * (int64_t)L.nso * kFragBlock;
             const __amdgpu_buffer_rsrc_t rxo = make_rsrc(
-                g.XO2 + xo0, min_u64(rest_bytes(frag_bytes(M, 2 * (int64_t)g.k2), xo0), (uint64_t)L.nso * kFragBlock));
+                qa.XO2 + xo0, min_u64(rest_bytes(frag_bytes(qa.M, 2 * (int64_t)qa.k2), xo0), (uint64_t)L.nso * kFragBlock));
             __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_rne(qo), rxo, L.offXO + rin, 0, 0);
             // further outlier channels of the lane (two or more in its 8): exact division
             if (L.wave_rest) {
@@ -589,8 +617,8 @@ dual_gemm_tiled(GemmArgs g) {
                     const int i = __builtin_ctz(mm);
                     const uint32_t wi = w[i >> 1];
                     const float xi = __uint_as_float((i & 1) ? (wi & 0xFFFF0000u) : (wi << 16));
-                    const float qi = __fdiv_rn(xi, g.s2[L.cj0 + i]);
-                    const uint32_t bi = 2u * (uint32_t)g.pos2[L.cj0 + i];
+                    const float qi = __fdiv_rn(xi, qa.s2[L.cj0 + i]);
+                    const uint32_t bi = 2u * (uint32_t)qa.pos2[L.cj0 + i];
                     __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_rne(qi), rxo,
                                                           (bi >> 5) * 1024u + ((bi >> 4) & 1u) * 512u + (bi & 15u) + rin,
                                                           0, 0);
@@ -609,9 +637,10 @@ dual_gemm_tiled(GemmArgs g) {
         // channels past the padded row, fall outside the range)
         const int64_t aq0 = gb * (int64_t)L.ns4 * kFragBlock;
         const __amdgpu_buffer_rsrc_t raq = make_rsrc(
-            g.Aq2 + aq0, min_u64(rest_bytes(frag_bytes(M, N / 2), aq0), (uint64_t)L.ns4 * kFragBlock));
+            qa.Aq2 + aq0, min_u64(rest_bytes(frag_bytes(qa.M, qa.N / 2), aq0), (uint64_t)L.ns4 * kFragBlock));
         __builtin_amdgcn_raw_buffer_store_b32(word & L.nkeep, raq, L.offAq + rin, 0, 0);
-        const __amdgpu_buffer_rsrc_t ras = make_rsrc(g.As2 + (o.m0 / kScRows) * sc_nwin(N) * kScWinBytes, (uint64_t)sc_nwin(N) * kScWinBytes);
+        const __amdgpu_buffer_rsrc_t ras =
+            make_rsrc(qa.As2 + (o.m0 / kScRows) * sc_nwin(qa.N) * kScWinBytes, (uint64_t)sc_nwin(qa.N) * kScWinBytes);
         __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(sb >> 23), ras, L.offAs + mt * (uint32_t)kScBlocks, 0, 0);
     };
 
@@ -650,8 +679,12 @@ dual_gemm_tiled(GemmArgs g) {
             const int gcol = o.n0 + wn * 32 * JB + (int)cl * 8;
             const bool col_ok = gcol < N;
             const uint32_t cofs = (uint32_t)gcol * 2u;
+            [[maybe_unused]] QuantArgs qa;
             [[maybe_unused]] QuantLane ql;
-            if constexpr (std::is_same_v<OutT, QuantOut>) ql = quant_lane(o, gcol, col_ok, (uint32_t)(et & 63u));
+            if constexpr (std::is_same_v<OutT, QuantOut>) {
+                qa = kernargs_per_tile();
+                ql = quant_lane(qa, gcol, col_ok, (uint32_t)(et & 63u));
+            }
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
 #pragma unroll
@@ -679,7 +712,7 @@ dual_gemm_tiled(GemmArgs g) {
                     for (int sI = 0; sI < (int)CH; ++sI) {
                         const uint32_t rr = (uint32_t)(64 / CH * sI) + rl;
                         const u32x4 w = *reinterpret_cast<const u32x4*>(wbuf + rr * RBY + ((cl ^ (rr & (CH - 1))) << 4));
-                        quant_octet(ql, o, w, (uint32_t)(wm * 128 + 64 * p) + rr);
+                        quant_octet(qa, ql, o, w, (uint32_t)(wm * 128 + 64 * p + 64 / CH * sI), rl);
                     }
                 } else {
                     u32x4 v[CH];
