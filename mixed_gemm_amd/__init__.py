@@ -21,7 +21,9 @@ from dataclasses import dataclass
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmixed_gemm.so")
+# MIXED_GEMM_LIB may name another build of the library (for example the
+# 4-wave GEMM variant, `python -m mixed_gemm_amd.build --gemm-waves 4`)
+LIB_PATH = os.environ.get("MIXED_GEMM_LIB") or os.path.join(HERE, "libmixed_gemm.so")
 
 MG_F32, MG_BF16 = 0, 1
 MG_W_1X32, MG_W_32X32, MG_W_128X1 = 0, 1, 2

@@ -1,14 +1,20 @@
 """Build libmixed_gemm.so (HIP, gfx950) in-tree.
 
-    python -m mixed_gemm_amd.build
+    python -m mixed_gemm_amd.build [--gemm-waves 4]
 
 Compiles every ``csrc/*.hip`` with hipcc for gfx950 (one object per file, in
 parallel) and links them into ``mixed_gemm_amd/libmixed_gemm.so``; then builds
 ``tests/c/abi_demo`` (plain C against ``include/mixed_gemm.h``, the library and
 the HIP runtime), which a GPU test runs to exercise the C ABI without Python.
+
+``--gemm-waves 4`` builds the dual GEMM with 4 waves per workgroup (one per
+SIMD) instead of 8, into ``mixed_gemm_amd/libmixed_gemm_w4.so`` (objects under
+``_build/w4``), for comparing the two schedules; the binding loads it when
+``MIXED_GEMM_LIB`` names it.
 """
 from __future__ import annotations
 
+import argparse
 import concurrent.futures as cf
 import glob
 import os
@@ -39,13 +45,22 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build mixed_gemm_amd)")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", src, "-o", obj]
+def _compile(src: str, obj_dir: str = OBJ, defines: tuple = ()) -> str:
+    obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
+    cmd = [hipcc(), *FLAGS, *defines, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj
+
+
+def _link(objs: list, lib: str) -> None:
+    tmp = lib + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, lib)
 
 
 def build(verbose: bool = False) -> str:
@@ -53,12 +68,7 @@ def build(verbose: bool = False) -> str:
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    _link(objs, LIB)
     if verbose:
         print(f"built {LIB}")
     demo = build_c_demo()
@@ -89,6 +99,31 @@ def build_c_demo() -> str:
     return exe
 
 
+def build_gemm_waves(waves: int, verbose: bool = False) -> str:
+    """The library with the dual GEMM built for `waves` waves per workgroup
+    (4 or 8; 8 is the default build), as libmixed_gemm_w<waves>.so."""
+    if waves not in (4, 8):
+        raise ValueError("the dual GEMM is written for 4 or 8 waves per workgroup")
+    obj_dir = os.path.join(OBJ, f"w{waves}")
+    os.makedirs(obj_dir, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    defines = (f"-DMG_GEMM_WAVES={waves}",)
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, obj_dir, defines), srcs))
+    lib = os.path.join(HERE, f"libmixed_gemm_w{waves}.so")
+    _link(objs, lib)
+    if verbose:
+        print(f"built {lib}")
+    return lib
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    ap = argparse.ArgumentParser(description="build libmixed_gemm (gfx950) in-tree")
+    ap.add_argument("--gemm-waves", type=int, default=0,
+                    help="build only a variant library with this many waves per GEMM workgroup (4 or 8)")
+    a = ap.parse_args()
+    if a.gemm_waves:
+        build_gemm_waves(a.gemm_waves, verbose=True)
+    else:
+        build(verbose=True)
     sys.exit(0)

@@ -341,8 +341,8 @@ dual_gemm_tiled(GemmArgs g) {
     };
     // does the cursor's half-stage open a scale window?
     auto cursor_opens_window = [&]() { return ct < t_end && cst < H4 && (cst & 3) == 0; };
-    // copies c = 2 r + sl of the cursor's half-stage into its ring slot: row
-    // group 2 w + r of operand A (c < 4) or B, slice sl
+    // copy c = 2 RPW op + 2 r + sl of the cursor's half-stage into its ring
+    // slot: row group RPW w + r of operand A (op 0) or B (op 1), slice sl
     // (fast: the cursor is known to be in the bulk part, whose resources are
     // rA and rB)
     auto copy_part = [&](int c, bool fast) {
@@ -381,7 +381,7 @@ dual_gemm_tiled(GemmArgs g) {
     };
 
     // End of a half-stage: this wave's copies of the next half-stage have
-    // landed (the 8 younger ones, of the half-stage after it, stay in
+    // landed (the NCOPY younger ones, of the half-stage after it, stay in
     // flight; loads complete in order) and its reads of the current slot are
     // done, then every wave arrives.  The scheduling barriers keep the MFMAs
     // above the wait, so they run while copies fly.
