@@ -577,19 +577,23 @@ def main() -> int:
     stages = ("calib", "wrange", "plan", "quant", "gemm")
     ev = {s: [] for s in stages}
 
-    def step(record: bool):
+    def step(record: str):
+        """One pass of the path.  record = "gemm": HIP events around the dual
+        GEMM only (the timed steps); "stages": events between all stages (each
+        event pair costs a few microseconds of the step, so these steps run
+        after the timed ones); "": none (warm-up)."""
         marks = [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] if record else None
-        if record:
+        if record == "stages":
             marks[0].record(stream)
         mg.mg_calib_reset(act_max)
         mg.mg_calib_act(X, act_max)
-        if record:
+        if record == "stages":
             marks[1].record(stream)
         mg.mg_weight_range(W, w_max)
-        if record:
+        if record == "stages":
             marks[2].record(stream)
         mg.mg_plan_build(plan, act_max, w_max, W)
-        if record:
+        if record == "stages":
             marks[3].record(stream)
         mg.mg_quantize_act(plan, X, act)
         if record:
@@ -598,18 +602,25 @@ def main() -> int:
         if record:
             marks[5].record(stream)
             for i, s in enumerate(stages):
-                ev[s].append((marks[i], marks[i + 1]))
+                if record == "stages" or s == "gemm":
+                    ev[s if record == "stages" else "gemm_timed"].append((marks[i], marks[i + 1]))
 
+    ev["gemm_timed"] = []
     for _ in range(args.warmup):
-        step(False)
+        step("")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(True)
+        step("gemm")
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
+    # per-stage intervals: the same number of further steps, events between stages
+    for _ in range(args.steps):
+        step("stages")
+    torch.cuda.synchronize()
     ms = {s: float(np.mean([a.elapsed_time(b) for a, b in ev[s]])) for s in stages}
+    ms["gemm"] = float(np.mean([a.elapsed_time(b) for a, b in ev["gemm_timed"]]))
 
     flops = w.flops()
     value = flops / (ms_step * 1e-3) / 1e12
