@@ -53,10 +53,37 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dual_gemm_ffn0_480p_traffic.json"
 GEMM_SRCS = [os.path.join(ROOT, "mixed_gemm_amd", "csrc", f) for f in ("k_gemm.hip", "mg_device.h", "mg_internal.h")]
 
 
+def _code_only(src: str) -> str:
+    """C/C++ source with comments removed and whitespace runs collapsed (string
+    and character literals kept), so that only changes to the code itself
+    change the hash below."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def gemm_source_hash() -> str:
+    """Hash of the dual GEMM's code (comments and layout excluded)."""
     h = hashlib.sha256()
     for f in GEMM_SRCS:
-        h.update(open(f, "rb").read())
+        h.update(_code_only(open(f, encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 

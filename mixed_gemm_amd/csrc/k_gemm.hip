@@ -191,7 +191,8 @@ struct QuantLane {
 // segment once per tile through a pointer the compiler cannot see through
 // (kernargs_per_tile), so that neither they nor the sizes derived from them
 // are held in scalar registers across the tile loop's K steps (which would
-// spill them there).
+// spill them there).  The kernel's one parameter, a GemmArgs passed by value,
+// is the start of that segment.
 struct QuantArgs {
     const float* s2;
     const float* rcp2;
