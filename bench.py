@@ -13,8 +13,9 @@ Prints ONE JSON line.  `value` = 2*M*K*N / (time of one whole step), in
 TFLOP/s; the dual-GEMM kernel's own rate is in `roofline`.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-    python bench.py --power-probe S   also board power (hwmon) while the GEMM and the
-                                 quantize each run back to back for S seconds
+    python bench.py --power-probe S   board power (hwmon) while the GEMM and the quantize
+                                 each run back to back for S seconds after the timed
+                                 steps (default 2; 0 leaves the `power` object out)
     python bench.py --suite      one JSON line per configuration point: the
                                  480p up/down-projections (three weight-scale
                                  layouts, raw, smoothed and percentile outlier
@@ -557,7 +558,7 @@ def main() -> int:
                          "10-20 s of CPU work)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run a plain device copy of 256 MiB (HBM counter calibration)")
-    ap.add_argument("--power-probe", type=float, default=0.0, metavar="SECONDS",
+    ap.add_argument("--power-probe", type=float, default=2.0, metavar="SECONDS",
                     help="after the timed steps, run the dual GEMM and then the quantize back to back for "
                          "SECONDS each while sampling board power (hwmon); adds a `power` object")
     ap.add_argument("--suite", action="store_true",
