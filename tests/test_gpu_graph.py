@@ -104,9 +104,13 @@ def test_step_graph_replays_match_eager():
         _same(b.snapshot(), want[r], f"replay {rep} (input {r})")
 
 
-def test_ffn_block_forward_graph_replays_match_eager():
+@pytest.mark.parametrize("epilogue", [False, True])
+def test_ffn_block_forward_graph_replays_match_eager(epilogue):
     """quantize -> GEMM (ffn.0) -> fused GELU + quantize -> GEMM (ffn.2) with
-    plans built beforehand, captured as one graph."""
+    plans built beforehand, captured as one graph; with epilogue=True the GELU
+    and ffn.2's quantize run in ffn.0's GEMM epilogue (which reads its
+    arguments from the kernel-argument segment once per tile: a graph's kernel
+    node carries its own copy of that segment)."""
     M, K0, N0, N2, k0, k2 = 600, 512, 1024, 384, 16, 32
     Xs = [synth.heavy_tail_act(M, K0, sigma=0.25, frac=0.02, mult=25.0, ch_seed=170 + r, x_seed=180 + r, bf16=True)
           for r in range(3)]
@@ -134,16 +138,22 @@ def test_ffn_block_forward_graph_replays_match_eager():
             self.y2 = torch.empty((M, N2), dtype=torch.bfloat16, device="cuda")
 
         def tensors(self):
-            return dict(Aq0=self.a0.Aq, As0=self.a0.As, XO0=self.a0.XO, Y0=self.y0,
-                        Aq2=self.a2.Aq, As2=self.a2.As, XO2=self.a2.XO, Y2=self.y2)
+            t = dict(Aq0=self.a0.Aq, As0=self.a0.As, XO0=self.a0.XO, Y0=self.y0,
+                     Aq2=self.a2.Aq, As2=self.a2.As, XO2=self.a2.XO, Y2=self.y2)
+            if epilogue:
+                del t["Y0"]                   # not written in the epilogue form
+            return t
 
     def fwd(X, bb):
         mg.mg_quantize_act(p0, X, bb.a0)
-        mg.mg_dual_gemm(p0, bb.a0, bb.y0)
-        mg.mg_gelu_quantize_act(p2, bb.y0, bb.a2)
+        if epilogue:
+            mg.mg_dual_gemm_gelu_quant(p0, bb.a0, p2, bb.a2)
+        else:
+            mg.mg_dual_gemm(p0, bb.a0, bb.y0)
+            mg.mg_gelu_quantize_act(p2, bb.y0, bb.a2)
         mg.mg_dual_gemm(p2, bb.a2, bb.y2)
 
-    print(f"\n[graph] FFN block M={M} {K0}->{N0}->{N2}: eager references", flush=True)
+    print(f"\n[graph] FFN block M={M} {K0}->{N0}->{N2} epilogue={epilogue}: eager references", flush=True)
     want = []
     for X in Xs:
         bb = Bufs()
